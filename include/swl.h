@@ -1,0 +1,141 @@
+/*
+ * swl.h — sink + window + landmark ("sealed O(1)") attention on AMD MI355X
+ * (gfx950).  C ABI of libswl.so.
+ *
+ * The layer: for every KV group g and query head h, a row attends under one
+ * softmax to three sources — ns sink keys, a ring-buffer window of the last
+ * w_g keys (self included), and a far field that summarises every key the
+ * window has evicted.  The far field keeps, per query head and landmark b, a
+ * running max M_b, a mass Z_b and a value accumulator Theta_b (an online
+ * softmax of landmark query q~_b over the evicted keys), and is read through
+ * the Nystrom estimate u_b = sum_a exp(f_a - f_max) mu[a][b] with
+ * f_a = scale <q, k~_a>.  Source: cortiq-engine 0.8.51
+ * src/gpu_wgpu/o1_batch.rs (module doc; kernels o1b_far_e, o1b_attend,
+ * o1b_far_commit, o1b_ring_commit, o1b_meta) and cortiq-engine 0.8.82
+ * src/gpu_metal/o1c.rs (encode, encode_tok, state_commit).
+ *
+ * Geometry (swl_geom): G KV groups, H query heads per group (nh = G*H,
+ * query head gh = g*H + h), m landmarks, W ring stride (the widest group
+ * window), ns sinks, d key width, dv value width, scale (usually 1/sqrt(d)),
+ * rect (1: clamp u_b at 0).  Supported: d == dv in {16, 32, 64, 128},
+ * 1 <= m <= 64, 1 <= H <= 16, 1 <= G <= 64, 0 <= ns <= 256, 1 <= W <= 65536.
+ *
+ * Device arrays (swl_state; all row-major, fp32 unless noted):
+ *   meta    u32 [G][4]   len, head, nfar, window override (0 = W)
+ *   ring_k  [G][W][d]    ring_v [G][W][dv]   logical key x of group g sits
+ *                        in slot (head + x) mod w_g
+ *   sink_k  [G][ns][d]   sink_v [G][ns][dv]
+ *   k_tilde [G][m][d]    landmark keys
+ *   q_tilde [nh][m][d]   landmark queries
+ *   mu      [nh][m][m]   mu[gh][a][b]
+ *   mz      [nh][2][m]   M (row 0) then Z (row 1); an empty far field is
+ *                        M = -inf, Z = 0
+ *   theta   [nh][m][dv]
+ * Call arrays: q [rows][nh][d] (rotated), k [rows][G][d] (rotated),
+ * v [rows][G][dv], out [rows][nh][dv].
+ *
+ * Ownership: the caller allocates every array, including the scratch
+ * buffer, in device memory; the library allocates nothing, keeps no global
+ * state and never frees.  Every call only enqueues kernels on `stream`
+ * (a hipStream_t; NULL is the default stream) and returns; results are
+ * ready when the stream is.  Calls on one state must be ordered on one
+ * stream.
+ *
+ * Errors: every entry point validates its arguments on the host before it
+ * enqueues anything; on SWL_EINVAL nothing was enqueued.  SWL_EHIP means a
+ * launch failed (hipGetLastError); earlier launches of that call may have
+ * run.
+ */
+#ifndef SWL_H
+#define SWL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SWL_OK 0
+#define SWL_EINVAL 1
+#define SWL_EHIP 2
+
+/* Rows of one sub-chunk (the pages' OB_K): a chunk longer than this is
+ * processed as consecutive sub-chunks of this many rows. */
+#define SWL_SUB 64
+
+typedef struct swl_geom {
+    int32_t G, H, m, W, ns, d, dv;
+    float scale;
+    int32_t rect;
+} swl_geom;
+
+typedef struct swl_state {
+    uint32_t* meta;
+    float* ring_k;
+    float* ring_v;
+    const float* sink_k;
+    const float* sink_v;
+    const float* k_tilde;
+    const float* q_tilde;
+    const float* mu;
+    float* mz;
+    float* theta;
+} swl_state;
+
+/* Bytes of scratch a call over `rows` rows needs (attend_chunk + commit on
+ * the same rows, prefill, or attend_token with rows = 1).  Prefill over
+ * more rows than one pass holds reuses the scratch pass after pass, so the
+ * size stops growing at 16384 rows.  Returns 0 for an invalid geometry. */
+size_t swl_scratch_bytes(const swl_geom* geom, int64_t rows);
+
+/* The empty state (o1b_meta's fields at zero pushes; o1b_far_e's empty far
+ * field): meta[g] = {0, 0, 0, windows[g]}, M = -inf, Z = 0, Theta = 0.
+ * `windows` is a host array of G window overrides (0 = W, else
+ * 1 <= w_g <= W) or NULL for all W.  Sinks, landmarks and mu are the
+ * caller's.  Ring contents are left as they are (len = 0). */
+int swl_init_state(const swl_geom* geom, const swl_state* st,
+                   const uint32_t* windows, void* stream);
+
+/* Attention of one sub-chunk of 1 <= rows <= 64 rows from the state, into
+ * out (o1b_far_e then o1b_attend): every evicted key is scored against
+ * every landmark query, the far max jumps to its post-chunk value, and each
+ * row reads the far field rescaled to it plus a causal in-chunk sum over the
+ * rows evicted so far.  Does not change the state; leaves the far-field
+ * quantities of the sub-chunk in `scratch` for swl_commit. */
+int swl_attend_chunk(const swl_geom* geom, const swl_state* st,
+                     const float* q, const float* k, const float* v, int32_t rows,
+                     float* out, void* scratch, size_t scratch_bytes, void* stream);
+
+/* The state after the rows of the preceding swl_attend_chunk (same k, v,
+ * rows and scratch, nothing else on the state in between): far commit
+ * (Theta <- R Theta + sum_j E_j v_evicted(j), M, Z; o1b_far_commit), ring
+ * commit (row j to slot (head0 + len0 + j) mod w_g; o1b_ring_commit) and
+ * meta (len, head, nfar after `rows` pushes; o1b_meta). */
+int swl_commit(const swl_geom* geom, const swl_state* st,
+               const float* k, const float* v, int32_t rows,
+               void* scratch, size_t scratch_bytes, void* stream);
+
+/* attend + commit over any number of rows (rows >= 0; 0 is a no-op), as
+ * consecutive 64-row sub-chunks with each sub-chunk's semantics (its own
+ * post-sub-chunk far max): the same result as looping swl_attend_chunk +
+ * swl_commit, up to rounding.  Sub-chunks are batched into few launches. */
+int swl_prefill(const swl_geom* geom, const swl_state* st,
+                const float* q, const float* k, const float* v, int64_t rows,
+                float* out, void* scratch, size_t scratch_bytes, void* stream);
+
+/* One row, attended and committed (a sub-chunk of one row; o1c.rs
+ * encode_tok): the window is split over blocks whose partials are merged
+ * with the far part, then the state advances by one push. */
+int swl_attend_token(const swl_geom* geom, const swl_state* st,
+                     const float* q, const float* k, const float* v,
+                     float* out, void* scratch, size_t scratch_bytes, void* stream);
+
+/* A static description of a status code. */
+const char* swl_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWL_H */

@@ -1,0 +1,232 @@
+// C entry points of libswl: host-side validation, scratch carving and the
+// launch sequence of each call.  Launch order per sub-chunk follows the
+// pages' encoder (cortiq-engine 0.8.51 src/gpu_wgpu/o1_batch.rs, encode:
+// far_e, attend, far_commit, ring_commit, meta): the far commit must follow
+// every read of the old accumulator, and the ring commit every read of the
+// evicted rows.  A prefill pass runs the same steps over up to 256
+// sub-chunks per launch.
+#include <math.h>
+#include <string.h>
+
+#include "swl_internal.h"
+
+namespace swl {
+
+size_t readout_lds_bytes(int d, int dv, int m);
+
+static bool geom_ok(const swl_geom* g)
+{
+    if (!g) return false;
+    if (g->G < 1 || g->G > 64) return false;
+    if (g->H < 1 || g->H > 16) return false;
+    if (g->m < 1 || g->m > 64) return false;
+    if (g->W < 1 || g->W > 65536) return false;
+    if (g->ns < 0 || g->ns > 256) return false;
+    if (g->d != g->dv) return false;
+    if (!(g->d == 8 || g->d == 16 || g->d == 32 || g->d == 64 || g->d == 128)) return false;
+    if (!isfinite(g->scale)) return false;
+    if (g->rect != 0 && g->rect != 1) return false;
+    return true;
+}
+
+static bool state_ok(const swl_geom* g, const swl_state* st)
+{
+    if (!st) return false;
+    if (!st->meta || !st->ring_k || !st->ring_v || !st->k_tilde || !st->q_tilde || !st->mu ||
+        !st->mz || !st->theta)
+        return false;
+    if (g->ns > 0 && (!st->sink_k || !st->sink_v)) return false;
+    return true;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Carve {
+    size_t e, p, ms, rs, th, ns, total;
+};
+
+static Carve carve(const swl_geom* g, int S)
+{
+    const size_t nhm = (size_t)g->G * g->H * g->m;
+    Carve c;
+    size_t off = 0;
+    c.e = off;  off += align256(sizeof(float) * (size_t)S * nhm * SUB);
+    c.p = off;  off += align256(sizeof(float) * (size_t)S * nhm * SUB);
+    c.ms = off; off += align256(sizeof(float) * (size_t)S * nhm);
+    c.rs = off; off += align256(sizeof(float) * (size_t)S * nhm);
+    c.th = off; off += align256(sizeof(float) * (size_t)S * nhm * g->dv);
+    c.ns = off; off += align256(sizeof(float) * (size_t)S * SUB * g->G * g->H * 2);
+    c.total = off;
+    return c;
+}
+
+static int subs_for_rows(int64_t rows)
+{
+    int64_t r = rows < 1 ? 1 : rows;
+    int64_t cap = (int64_t)PASS_SUBS * SUB;
+    if (r > cap) r = cap;
+    return (int)((r + SUB - 1) / SUB);
+}
+
+static KParams make_params(const swl_geom* g, const swl_state* st)
+{
+    KParams p;
+    memset(&p, 0, sizeof(p));
+    p.G = g->G; p.H = g->H; p.m = g->m; p.W = g->W; p.ns = g->ns;
+    p.d = g->d; p.dv = g->dv; p.nh = g->G * g->H; p.rect = g->rect;
+    p.scale = g->scale;
+    p.meta = st->meta; p.ring_k = st->ring_k; p.ring_v = st->ring_v;
+    p.sink_k = st->sink_k; p.sink_v = st->sink_v; p.k_tilde = st->k_tilde;
+    p.q_tilde = st->q_tilde; p.mu = st->mu; p.mz = st->mz; p.theta = st->theta;
+    return p;
+}
+
+static void set_scratch(KParams& p, const swl_geom* g, void* scratch, int S)
+{
+    Carve c = carve(g, S);
+    char* b = static_cast<char*>(scratch);
+    p.E = reinterpret_cast<float*>(b + c.e);
+    p.P = reinterpret_cast<float*>(b + c.p);
+    p.Ms = reinterpret_cast<float*>(b + c.ms);
+    p.Rs = reinterpret_cast<float*>(b + c.rs);
+    p.TH = reinterpret_cast<float*>(b + c.th);
+    p.NS = reinterpret_cast<float*>(b + c.ns);
+}
+
+#define SWL_TRY(x)                          \
+    do {                                    \
+        if ((x) != hipSuccess) return SWL_EHIP; \
+    } while (0)
+
+// far_e + near + far readout of one call or pass (state unchanged).
+static int run_attend(const KParams& p, hipStream_t st)
+{
+    SWL_TRY(launch_far_score(p, st));
+    SWL_TRY(launch_far_scan(p, st));
+    SWL_TRY(launch_near(p, st));
+    SWL_TRY(launch_readout(p, st));
+    return SWL_OK;
+}
+
+// far commit + ring commit + meta of one call or pass.
+static int run_commit(const KParams& p, hipStream_t st)
+{
+    SWL_TRY(launch_dtheta(p, st));
+    SWL_TRY(launch_theta_scan(p, true, st));
+    SWL_TRY(launch_ring_commit(p, st));
+    SWL_TRY(launch_meta(p, st));
+    return SWL_OK;
+}
+
+}  // namespace swl
+
+using namespace swl;
+
+extern "C" {
+
+size_t swl_scratch_bytes(const swl_geom* geom, int64_t rows)
+{
+    if (!geom_ok(geom) || rows < 0) return 0;
+    return carve(geom, subs_for_rows(rows)).total;
+}
+
+int swl_init_state(const swl_geom* geom, const swl_state* st, const uint32_t* windows,
+                   void* stream)
+{
+    if (!geom_ok(geom) || !state_ok(geom, st)) return SWL_EINVAL;
+    if (windows) {
+        for (int g = 0; g < geom->G; ++g)
+            if (windows[g] > (uint32_t)geom->W) return SWL_EINVAL;
+    }
+    KParams p = make_params(geom, st);
+    SWL_TRY(launch_init(p, windows, static_cast<hipStream_t>(stream)));
+    return SWL_OK;
+}
+
+int swl_attend_chunk(const swl_geom* geom, const swl_state* st, const float* q, const float* k,
+                     const float* v, int32_t rows, float* out, void* scratch,
+                     size_t scratch_bytes, void* stream)
+{
+    if (!geom_ok(geom) || !state_ok(geom, st)) return SWL_EINVAL;
+    if (rows < 1 || rows > SUB || !q || !k || !v || !out || !scratch) return SWL_EINVAL;
+    if (scratch_bytes < carve(geom, 1).total) return SWL_EINVAL;
+    KParams p = make_params(geom, st);
+    p.q = q; p.k = k; p.v = v; p.out = out;
+    p.T = rows; p.S = 1;
+    set_scratch(p, geom, scratch, 1);
+    p.theta_prev = st->theta;
+    p.theta_prev_stride = 0;
+    return run_attend(p, static_cast<hipStream_t>(stream));
+}
+
+int swl_commit(const swl_geom* geom, const swl_state* st, const float* k, const float* v,
+               int32_t rows, void* scratch, size_t scratch_bytes, void* stream)
+{
+    if (!geom_ok(geom) || !state_ok(geom, st)) return SWL_EINVAL;
+    if (rows < 1 || rows > SUB || !k || !v || !scratch) return SWL_EINVAL;
+    if (scratch_bytes < carve(geom, 1).total) return SWL_EINVAL;
+    KParams p = make_params(geom, st);
+    p.k = k; p.v = v;
+    p.T = rows; p.S = 1;
+    set_scratch(p, geom, scratch, 1);
+    return run_commit(p, static_cast<hipStream_t>(stream));
+}
+
+int swl_prefill(const swl_geom* geom, const swl_state* st, const float* q, const float* k,
+                const float* v, int64_t rows, float* out, void* scratch, size_t scratch_bytes,
+                void* stream)
+{
+    if (!geom_ok(geom) || !state_ok(geom, st)) return SWL_EINVAL;
+    if (rows < 0) return SWL_EINVAL;
+    if (rows == 0) return SWL_OK;
+    if (!q || !k || !v || !out || !scratch) return SWL_EINVAL;
+    const int S_max = subs_for_rows(rows);
+    if (scratch_bytes < carve(geom, S_max).total) return SWL_EINVAL;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const int64_t cap = (int64_t)PASS_SUBS * SUB;
+    const int nh = geom->G * geom->H;
+    for (int64_t done = 0; done < rows;) {
+        const int64_t T = rows - done < cap ? rows - done : cap;
+        KParams p = make_params(geom, st);
+        p.q = q + done * nh * geom->d;
+        p.k = k + done * geom->G * geom->d;
+        p.v = v + done * geom->G * geom->dv;
+        p.out = out + done * nh * geom->dv;
+        p.T = (int)T;
+        p.S = (int)((T + SUB - 1) / SUB);
+        set_scratch(p, geom, scratch, S_max);
+        p.theta_prev = p.TH;
+        p.theta_prev_stride = (int64_t)nh * geom->m * geom->dv;
+        SWL_TRY(launch_far_score(p, hs));
+        SWL_TRY(launch_far_scan(p, hs));
+        SWL_TRY(launch_dtheta(p, hs));
+        SWL_TRY(launch_theta_scan(p, true, hs));
+        SWL_TRY(launch_near(p, hs));
+        SWL_TRY(launch_readout(p, hs));
+        SWL_TRY(launch_ring_commit(p, hs));
+        SWL_TRY(launch_meta(p, hs));
+        done += T;
+    }
+    return SWL_OK;
+}
+
+int swl_attend_token(const swl_geom* geom, const swl_state* st, const float* q, const float* k,
+                     const float* v, float* out, void* scratch, size_t scratch_bytes,
+                     void* stream)
+{
+    int rc = swl_attend_chunk(geom, st, q, k, v, 1, out, scratch, scratch_bytes, stream);
+    if (rc != SWL_OK) return rc;
+    return swl_commit(geom, st, k, v, 1, scratch, scratch_bytes, stream);
+}
+
+const char* swl_status_str(int status)
+{
+    switch (status) {
+    case SWL_OK: return "ok";
+    case SWL_EINVAL: return "invalid argument";
+    case SWL_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

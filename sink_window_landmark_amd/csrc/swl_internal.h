@@ -1,0 +1,111 @@
+// Internal declarations of libswl: the parameter block every kernel takes,
+// the closed-form ring bookkeeping, and the launchers the C entry points call.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/swl.h"
+
+namespace swl {
+
+constexpr int SUB = SWL_SUB;           // rows of a sub-chunk
+constexpr int PASS_SUBS = 256;         // sub-chunks per prefill pass (16384 rows)
+
+// Everything a kernel of one call (or one prefill pass) needs, passed by value.
+struct KParams {
+    // geometry
+    int G, H, m, W, ns, d, dv, nh, rect;
+    float scale;
+    // state
+    uint32_t* meta;
+    float* ring_k;
+    float* ring_v;
+    const float* sink_k;
+    const float* sink_v;
+    const float* k_tilde;
+    const float* q_tilde;
+    const float* mu;
+    float* mz;
+    float* theta;
+    // rows of this call / pass
+    const float* q;
+    const float* k;
+    const float* v;
+    float* out;
+    int T;   // rows (<= PASS_SUBS * SUB)
+    int S;   // sub-chunks, ceil(T / SUB)
+    // scratch planes (see scratch_layout)
+    float* E;    // [S][nh*m][SUB]  scores, then exp mass against the post-sub-chunk max
+    float* P;    // [S][nh*m][SUB]  far mass prefix R*Z + sum_{j'<=j} E
+    float* Ms;   // [S][nh*m]       post-sub-chunk max
+    float* Rs;   // [S][nh*m]       rescale of the old mass
+    float* TH;   // [S][nh*m][dv]   Theta increments, then Theta before each sub-chunk
+    float* NS;   // [S*SUB][nh][2]  near max and near mass of each row and head
+    const float* theta_prev;  // Theta before sub-chunk s at theta_prev + s*theta_prev_stride
+    int64_t theta_prev_stride;
+};
+
+// Ring bookkeeping of group g at the start of a call.
+struct GMeta {
+    int len0, head0, nfar0, wg;
+};
+
+__device__ __forceinline__ GMeta load_gmeta(const uint32_t* meta, int g, int W)
+{
+    GMeta c;
+    c.len0 = (int)meta[4 * g + 0];
+    c.head0 = (int)meta[4 * g + 1];
+    c.nfar0 = (int)meta[4 * g + 2];
+    uint32_t w = meta[4 * g + 3];
+    c.wg = w ? (int)w : W;
+    return c;
+}
+
+// Ring bookkeeping at the start of the sub-chunk that begins `r0` rows into
+// the call: the closed form of r0 single pushes (o1b_meta applied r0 times).
+struct SubMeta {
+    int len0, head0, nfar0, j0;
+};
+
+__device__ __forceinline__ SubMeta sub_meta(const GMeta& c, int r0)
+{
+    SubMeta s;
+    int tot = c.len0 + r0;
+    int ev = tot > c.wg ? tot - c.wg : 0;
+    s.len0 = tot < c.wg ? tot : c.wg;
+    s.head0 = (c.head0 + ev) % c.wg;
+    s.nfar0 = c.nfar0 + ev;
+    s.j0 = c.wg - s.len0;
+    return s;
+}
+
+// Key positions of a call count keys in push order: the call-start ring in
+// logical order (positions 0 .. len0-1), then the call's rows.  Position p
+// of group g lives in ring slot (head0 + p) mod w_g when p < len0, else in
+// row p - len0 of the call's k/v.  Chunk row j of the sub-chunk at r0 is
+// position len0 + r0 + j, and it evicts position len0 + r0 + j - w_g.
+__device__ __forceinline__ const float* key_row(const KParams& p, const GMeta& c, int g, int pos)
+{
+    if (pos < c.len0) return p.ring_k + ((int64_t)g * p.W + (c.head0 + pos) % c.wg) * p.d;
+    return p.k + ((int64_t)(pos - c.len0) * p.G + g) * p.d;
+}
+
+__device__ __forceinline__ const float* val_row(const KParams& p, const GMeta& c, int g, int pos)
+{
+    if (pos < c.len0) return p.ring_v + ((int64_t)g * p.W + (c.head0 + pos) % c.wg) * p.dv;
+    return p.v + ((int64_t)(pos - c.len0) * p.G + g) * p.dv;
+}
+
+// Launchers (each returns the launch's hipGetLastError).
+hipError_t launch_init(const KParams& p, const uint32_t* windows, hipStream_t st);
+hipError_t launch_far_score(const KParams& p, hipStream_t st);
+hipError_t launch_far_scan(const KParams& p, hipStream_t st);
+hipError_t launch_dtheta(const KParams& p, hipStream_t st);
+hipError_t launch_theta_scan(const KParams& p, bool commit, hipStream_t st);
+hipError_t launch_near(const KParams& p, hipStream_t st);
+hipError_t launch_readout(const KParams& p, hipStream_t st);
+hipError_t launch_ring_commit(const KParams& p, hipStream_t st);
+hipError_t launch_meta(const KParams& p, hipStream_t st);
+
+}  // namespace swl

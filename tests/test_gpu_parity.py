@@ -1,0 +1,259 @@
+"""GPU path (through the C ABI) against the CPU oracle.
+
+Inputs are the seeded synthetic workloads of ``synth`` (and the pages' own
+deterministic ``jit`` rows for their test shapes); expected values are the
+float64 serial oracle's.  Small cases compare every output; the full-size
+workloads compare sampled rows (the oracle still steps every row) and the
+whole final state.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import sink_window_landmark_amd as swl
+
+from swl_gpu import (banner, check_out, check_state, dev, geom_of, oracle_threads, read_state,
+                     torch)
+
+pytestmark = pytest.mark.gpu
+
+
+def _state(cfg, host):
+    return swl.LayerState.from_host(geom_of(cfg), host)
+
+
+def _prefill(cfg, st, q, k, v, poison=False):
+    t = torch()
+    out = t.empty((q.shape[0], cfg.nh, cfg.dv), dtype=t.float32, device="cuda")
+    scratch = swl.alloc_scratch(st.geom, q.shape[0])
+    if poison:
+        scratch.view(t.float32)[: scratch.numel() // 4].fill_(float("nan"))
+        out.fill_(float("nan"))
+    swl.swl_prefill(st, dev(q), dev(k), dev(v), out, scratch)
+    t.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _chunks(cfg, st, q, k, v, sizes, poison=False):
+    """attend_chunk + commit over consecutive chunks of the given sizes."""
+    t = torch()
+    outs = []
+    scratch = swl.alloc_scratch(st.geom, 64)
+    r0 = 0
+    for n in sizes:
+        out = t.empty((n, cfg.nh, cfg.dv), dtype=t.float32, device="cuda")
+        if poison:
+            scratch.view(t.float32)[: scratch.numel() // 4].fill_(float("nan"))
+        qd, kd, vd = dev(q[r0:r0 + n]), dev(k[r0:r0 + n]), dev(v[r0:r0 + n])
+        swl.swl_attend_chunk(st, qd, kd, vd, out, scratch)
+        swl.swl_commit(st, kd, vd, scratch)
+        outs.append(out)
+        r0 += n
+    t.cuda.synchronize()
+    return np.concatenate([o.cpu().numpy() for o in outs])
+
+
+# -- tiny layer (w = 16 < 64 rows, ring 10/16, empty far field) ----------------
+
+def test_tiny_attend_commit():
+    banner("tiny attend_chunk + commit")
+    cfg = synth.TINY
+    host = synth.make_state(cfg)
+    q, k, v = synth.rows(cfg, 0, cfg.rows)
+    st = _state(cfg, host)
+    got = _chunks(cfg, st, q, k, v, [64], poison=True)
+    orc = oracle.from_config(cfg, host)
+    check_out(got, orc.step(q, k, v))
+    check_state(read_state(st), orc)
+
+
+def test_tiny_prefill():
+    banner("tiny prefill")
+    cfg = synth.TINY
+    host = synth.make_state(cfg)
+    q, k, v = synth.rows(cfg, 0, cfg.rows)
+    st = _state(cfg, host)
+    got = _prefill(cfg, st, q, k, v, poison=True)
+    orc = oracle.from_config(cfg, host)
+    check_out(got, orc.step(q, k, v))
+    check_state(read_state(st), orc)
+
+
+@pytest.mark.parametrize("head0,sizes", [(13, [64, 64, 64]), (5, [7, 64, 1, 33]), (0, [1] * 40)])
+def test_tiny_chunk_sizes_and_wrapped_head(head0, sizes):
+    banner(f"tiny chunks head0={head0} sizes={sizes[:4]}...")
+    cfg = synth.TINY.replace(head0=head0)
+    host = synth.make_state(cfg)
+    T = sum(sizes)
+    q, k, v = synth.rows(cfg, 0, T)
+    st = _state(cfg, host)
+    got = _chunks(cfg, st, q, k, v, sizes, poison=True)
+    orc = oracle.from_config(cfg, host)
+    check_out(got, orc.step(q, k, v))
+    check_state(read_state(st), orc)
+    # the same rows in one prefill call
+    st2 = _state(cfg, host)
+    got2 = _prefill(cfg, st2, q, k, v)
+    check_out(got2, oracle.from_config(cfg, host).step(q, k, v), "prefill")
+    check_state(read_state(st2), orc)
+
+
+# -- the pages' chunk-vs-serial shapes, with their jit inputs ---------------------
+
+@pytest.mark.parametrize("w,w2,chunks", [(64, 64, [70, 9]), (64, 128, [70, 40])])
+def test_reference_shapes(w, w2, chunks):
+    banner(f"reference shapes w={w}/{w2} chunks={chunks}")
+    d, m, ns, H, t0 = 8, 4, 2, 2, 100
+    cfg = synth.Config("ref", G=2, H=H, d=d, dv=d, ns=ns, W=max(w, w2), m=m, rows=t0,
+                       windows=(w, w2))
+    host = synth.make_state(cfg)
+    q, k, v = synth.jit_rows(2, H, d, 0, t0 + sum(chunks))
+    orc = oracle.from_config(cfg, host)
+    st = _state(cfg, host)
+    got0 = _prefill(cfg, st, q[:t0], k[:t0], v[:t0])
+    check_out(got0, orc.step(q[:t0], k[:t0], v[:t0]), "prompt")
+    r0 = t0
+    for n in chunks:
+        sl = slice(r0, r0 + n)
+        got = _prefill(cfg, st, q[sl], k[sl], v[sl])
+        check_out(got, orc.step(q[sl], k[sl], v[sl]), f"chunk {n}")
+        r0 += n
+    check_state(read_state(st), orc)
+
+
+# -- the small layer, every row ------------------------------------------------------
+
+def test_small_full():
+    cfg = synth.SMALL
+    banner(f"small layer prefill T={cfg.rows}")
+    host = synth.make_state(cfg)
+    q, k, v = synth.rows(cfg, 0, cfg.rows)
+    st = _state(cfg, host)
+    # reset through the library: the synthetic state is the empty one
+    swl.swl_init_state(st, cfg.meta_windows())
+    got = _prefill(cfg, st, q, k, v, poison=True)
+    orc = oracle.from_config(cfg, host, threads=oracle_threads())
+    check_out(got, orc.step(q, k, v))
+    check_state(read_state(st), orc)
+
+
+def _sample_rows(T, w, seed=0):
+    r = np.random.default_rng(seed)
+    s = set(range(0, 3)) | set(range(T - 64, T)) | set(r.integers(0, T, 96).tolist())
+    for x in (w - 1, w, w + 1, w + 63, w + 64):
+        if 0 <= x < T:
+            s.add(x)
+    return np.array(sorted(s))
+
+
+@pytest.mark.parametrize("name", ["maxwin", "mixed"])
+def test_full_size_sampled(name):
+    cfg = synth.CONFIGS[name]
+    banner(f"{name} prefill T={cfg.rows}")
+    host = synth.make_state(cfg)
+    q, k, v = synth.rows(cfg, 0, cfg.rows)
+    st = _state(cfg, host)
+    got = _prefill(cfg, st, q, k, v)
+    rows = _sample_rows(cfg.rows, min(cfg.window(g) for g in range(cfg.G)))
+    want_mask = np.zeros(cfg.rows, bool)
+    want_mask[rows] = True
+    banner(f"{name} oracle over {cfg.rows} rows, {rows.size} sampled outputs")
+    orc = oracle.from_config(cfg, host, threads=oracle_threads())
+    want = orc.step(q, k, v, want=want_mask)
+    check_out(got[rows], want)
+    check_state(read_state(st), orc)
+
+
+# -- decode: one row at a time after a long prompt ----------------------------------------
+
+def test_decode_after_prompt():
+    cfg = synth.DECODE
+    steps = 512
+    banner(f"decode: prefill {cfg.rows} then {steps} tokens")
+    host = synth.make_state(cfg)
+    q, k, v = synth.rows(cfg, 0, cfg.rows + steps)
+    st = _state(cfg, host)
+    _prefill(cfg, st, q[:cfg.rows], k[:cfg.rows], v[:cfg.rows])
+    t = torch()
+    scratch = swl.alloc_scratch(st.geom, 1)
+    outs = t.empty((steps, cfg.nh, cfg.dv), dtype=t.float32, device="cuda")
+    qd, kd, vd = dev(q[cfg.rows:]), dev(k[cfg.rows:]), dev(v[cfg.rows:])
+    for i in range(steps):
+        swl.swl_attend_token(st, qd[i:i + 1], kd[i:i + 1], vd[i:i + 1], outs[i:i + 1], scratch)
+    t.cuda.synchronize()
+    orc = oracle.from_config(cfg, host, threads=oracle_threads())
+    orc.step(q[:cfg.rows], k[:cfg.rows], v[:cfg.rows], want=np.zeros(cfg.rows, bool))
+    want = orc.step(q[cfg.rows:], k[cfg.rows:], v[cfg.rows:])
+    check_out(outs.cpu().numpy(), want)
+    check_state(read_state(st), orc)
+
+
+# -- edge cases ------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rect", [False, True])
+def test_negative_mu_guard_and_rect(rect):
+    banner(f"negative mu, rect={rect}")
+    cfg = synth.Config("neg", G=2, H=3, d=32, dv=32, ns=3, W=48, m=16, rows=200,
+                       windows=(40, 48), rect=rect)
+    host = synth.make_state(cfg)
+    r = np.random.default_rng(3)
+    host.mu = (r.standard_normal(host.mu.shape) / cfg.m).astype(np.float32)  # mixed signs
+    host.mu[0] = -np.abs(host.mu[0])                                          # head 0: D_far < 0
+    q, k, v = synth.rows(cfg, 0, cfg.rows)
+    st = _state(cfg, host)
+    got = _prefill(cfg, st, q, k, v)
+    orc = oracle.from_config(cfg, host)
+    check_out(got, orc.step(q, k, v))
+    check_state(read_state(st), orc)
+
+
+def test_resume_from_copied_state():
+    banner("resume from a copied state")
+    cfg = synth.SMALL.replace(rows=1500, W=256, m=16)
+    host = synth.make_state(cfg)
+    q, k, v = synth.rows(cfg, 0, cfg.rows)
+    a = _state(cfg, host)
+    full = _prefill(cfg, a, q, k, v)
+    b = _state(cfg, host)
+    cut = 704  # a sub-chunk boundary: both runs then see the same sub-chunks
+    first = _prefill(cfg, b, q[:cut], k[:cut], v[:cut])
+    saved = {f: getattr(b, f).cpu() for f in swl.LayerState.FIELDS}
+    c = swl.LayerState(b.geom, **{f: x.to("cuda") for f, x in saved.items()})
+    rest = _prefill(cfg, c, q[cut:], k[cut:], v[cut:])
+    np.testing.assert_array_equal(np.concatenate([first, rest]), full)
+    sa, sc = read_state(a), read_state(c)
+    for f in sa:
+        np.testing.assert_array_equal(sa[f], sc[f])
+
+
+def test_prefill_passes_match_one_long_call():
+    """More rows than one prefill pass holds (16384) against the oracle."""
+    cfg = synth.Config("long", G=1, H=2, d=32, dv=32, ns=4, W=512, m=8, rows=20000, rope=True,
+                       landmark_scale=0.2)
+    banner(f"long prefill T={cfg.rows}")
+    host = synth.make_state(cfg)
+    q, k, v = synth.rows(cfg, 0, cfg.rows)
+    st = _state(cfg, host)
+    got = _prefill(cfg, st, q, k, v)
+    rows = _sample_rows(cfg.rows, cfg.W)
+    rows = np.union1d(rows, np.arange(16384 - 70, 16384 + 70))
+    mask = np.zeros(cfg.rows, bool)
+    mask[rows] = True
+    orc = oracle.from_config(cfg, host)
+    check_out(got[rows], orc.step(q, k, v, want=mask))
+    check_state(read_state(st), orc)
+
+
+def test_zero_rows_is_a_noop():
+    cfg = synth.TINY
+    host = synth.make_state(cfg)
+    st = _state(cfg, host)
+    before = read_state(st)
+    t = torch()
+    z = lambda *s: t.empty(s, dtype=t.float32, device="cuda")
+    swl.swl_prefill(st, z(0, cfg.nh, cfg.d), z(0, cfg.G, cfg.d), z(0, cfg.G, cfg.dv),
+                    z(0, cfg.nh, cfg.dv), swl.alloc_scratch(st.geom, 0))
+    after = read_state(st)
+    for f in before:
+        np.testing.assert_array_equal(before[f], after[f])
