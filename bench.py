@@ -1,0 +1,334 @@
+"""Benchmark of the sink + window + landmark layer on one MI355X.
+
+A step is one pass of the whole hot path over the max-window workload
+(4 KV groups x 4 query heads, d = dv = 128, 4 sinks, w = 2048, m = 64
+landmarks): the empty state (swl_init_state), then a 32768-row prompt
+through swl_prefill as 512 consecutive 64-row sub-chunks (far scores,
+far scan, far accumulator, near attention, far readout, ring and meta
+commit).  Inputs are synthetic (seeded N(0,1) with RoPE), already resident
+in HBM when the timed region starts.
+
+Prints one JSON line: prefill rows/s (whole job, one GPU), the near
+kernel's achieved TFLOP/s against the fp32 MFMA peak (timed live with HIP
+events around its launches), the decode path's us/token after the
+32768-row prompt, the per-sub-chunk API's rate, an exact-attention timing
+for context, and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_FP32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+
+
+def near_flops(cfg, T, len0=0):
+    """Algorithmic near flops of T rows: each row and head scores and sums
+    ns + min(w_g, len0 + i + 1) keys, 2d + 2dv flops each."""
+    tot = 0
+    r = np.arange(T, dtype=np.int64)
+    for g in range(cfg.G):
+        w = cfg.window(g)
+        keys = cfg.ns + np.minimum(w, len0 + r + 1)
+        tot += int(keys.sum()) * cfg.H * (2 * cfg.d + 2 * cfg.dv)
+    return tot
+
+
+def far_flops(cfg, T, len0=0, nfar0=0):
+    """Algorithmic far flops of T rows: evicted-key scores and accumulator
+    updates (2 d m H and 2 dv m H per evicted key and group), and per row and
+    head with a non-empty far field: f (2 m d), u (2 m m), N (2 m dv) and the
+    in-chunk terms (2 n (m + dv), n = rows of the sub-chunk evicted so far)."""
+    m, d, dv, H = cfg.m, cfg.d, cfg.dv, cfg.H
+    fe = fc = ro = 0
+    for g in range(cfg.G):
+        w = cfg.window(g)
+        ln, nf = len0, nfar0
+        for r0 in range(0, T, 64):
+            k = min(64, T - r0)
+            j0 = w - ln
+            ev = max(0, k - max(j0, 0))
+            fe += ev * 2 * d * m * H
+            fc += ev * 2 * dv * m * H
+            for i in range(k):
+                n_in = max(0, i - max(j0, 0) + 1) if i >= j0 else 0
+                if nf + n_in > 0:
+                    ro += H * (2 * m * d + 2 * m * m + 2 * m * dv + 2 * n_in * (m + dv))
+            tot = ln + k
+            if tot > w:
+                nf += tot - w
+            ln = min(w, tot)
+    return fe, fc, ro
+
+
+def decode_bytes(cfg):
+    """Algorithmic HBM bytes of one decode token at a full window: the
+    group's sinks and window K/V, the far skeleton (k~, q~, mu, M/Z, Theta
+    read and Theta/M/Z written), q/k/v in, out and the pushed row written."""
+    G, H, d, dv, m, ns = cfg.G, cfg.H, cfg.d, cfg.dv, cfg.m, cfg.ns
+    nh = G * H
+    f = 0
+    for g in range(G):
+        f += (ns + cfg.window(g)) * (d + dv)
+    f += G * m * d + nh * m * d + nh * m * m + nh * 2 * m * 2 + nh * m * dv * 2
+    f += nh * d + G * (d + dv) + nh * dv + G * (d + dv)
+    return 4 * f
+
+
+def run_gpu(args, cfg):
+    import torch
+    import synth
+    import sink_window_landmark_amd as swl
+
+    dev = "cuda"
+    T = cfg.rows
+    geom = swl.Geom(cfg.G, cfg.H, cfg.m, cfg.W, cfg.ns, cfg.d, cfg.dv)
+    host = synth.make_state(cfg)
+    st = swl.LayerState.from_host(geom, host, device=dev)
+    nd = args.decode_steps
+    qh, kh, vh = synth.rows(cfg, 0, T + nd)
+    q = torch.from_numpy(qh[:T]).to(dev)
+    k = torch.from_numpy(kh[:T]).to(dev)
+    v = torch.from_numpy(vh[:T]).to(dev)
+    out = torch.empty((T, cfg.nh, cfg.dv), dtype=torch.float32, device=dev)
+    scratch = swl.alloc_scratch(geom, T, device=dev)
+    windows = cfg.meta_windows()
+
+    stage_ev = []   # (stage, start_event, end_event) of the timed steps
+    recording = [False]
+
+    def on_stage(name, begin):
+        if not recording[0]:
+            return
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record()
+        if begin:
+            stage_ev.append([name, ev, None])
+        else:
+            stage_ev[-1][2] = ev
+
+    def step():
+        swl.swl_init_state(st, windows)
+        swl.swl_prefill_traced(st, q, k, v, out, scratch, on_stage)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    recording[0] = True
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    recording[0] = False
+    ms_total = e0.elapsed_time(e1)
+    ms_per_step = ms_total / args.steps
+    stages = {}
+    for name, a, b in stage_ev:
+        stages.setdefault(name, []).append(a.elapsed_time(b))
+    near_ms = stages["near"]
+    near_launch_ms = float(np.mean(near_ms))
+    near_step_flops = near_flops(cfg, T)
+    launches_per_step = len(near_ms) / args.steps
+    near_flops_per_launch = near_step_flops / launches_per_step
+    achieved = near_flops_per_launch / (near_launch_ms * 1e-3) / 1e12
+    fe, fc, ro = far_flops(cfg, T)
+    step_flops = near_step_flops + fe + fc + ro
+
+    res = dict(
+        value=T * args.steps / (ms_total * 1e-3),
+        ms_per_step=ms_per_step,
+        wall_s=wall,
+        stages_ms_per_step={n: float(np.sum(x)) / args.steps for n, x in stages.items()},
+        near=dict(avg_launch_ms=near_launch_ms, launches_per_step=launches_per_step,
+                  flops_per_launch=near_flops_per_launch, achieved_tflops=achieved),
+        step_flops=step_flops,
+        step_tflops=step_flops / (ms_per_step * 1e-3) / 1e12,
+    )
+
+    # decode: one row at a time after the 32768-row prompt (the state left by
+    # the last timed step), through swl_attend_token
+    if nd > 0:
+        qd = torch.from_numpy(qh[T:]).to(dev)
+        kd = torch.from_numpy(kh[T:]).to(dev)
+        vd = torch.from_numpy(vh[T:]).to(dev)
+        od = torch.empty((nd, cfg.nh, cfg.dv), dtype=torch.float32, device=dev)
+        tscr = swl.alloc_scratch(geom, 1, device=dev)
+        nw = min(16, nd)
+        for i in range(nw):
+            swl.swl_attend_token(st, qd[i:i + 1], kd[i:i + 1], vd[i:i + 1], od[i:i + 1], tscr)
+        torch.cuda.synchronize()
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record()
+        for i in range(nw, nd):
+            swl.swl_attend_token(st, qd[i:i + 1], kd[i:i + 1], vd[i:i + 1], od[i:i + 1], tscr)
+        d1.record()
+        torch.cuda.synchronize()
+        us = d0.elapsed_time(d1) * 1e3 / (nd - nw)
+        db = decode_bytes(cfg)
+        res["decode"] = dict(tokens=nd - nw, us_per_token=us, bytes_per_token=db,
+                             achieved_gbs=db / (us * 1e-6) / 1e9,
+                             frac_hbm=db / (us * 1e-6) / 1e9 / HBM_PEAK_GBS)
+
+    # the per-sub-chunk API (attend_chunk + commit per 64 rows), for comparison
+    if args.chunk_api:
+        cscr = swl.alloc_scratch(geom, 64, device=dev)
+        swl.swl_init_state(st, windows)
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for r0 in range(0, T, 64):
+            sl = slice(r0, min(T, r0 + 64))
+            swl.swl_attend_chunk(st, q[sl], k[sl], v[sl], out[sl], cscr)
+            swl.swl_commit(st, k[sl], v[sl], cscr)
+        c1.record()
+        torch.cuda.synchronize()
+        res["chunk_api_rows_per_s"] = T / (c0.elapsed_time(c1) * 1e-3)
+
+    if args.exact:
+        res["exact_attention"] = exact_attention(cfg, host, q, k, v)
+    return res
+
+
+def exact_attention(cfg, host, q, k, v):
+    """Exact fp32 causal softmax attention over sinks + every key, same heads,
+    blockwise torch.matmul (for the "faster than exact" comparison only)."""
+    import torch
+    T, G, H, d = q.shape[0], cfg.G, cfg.H, cfg.d
+    sk = torch.from_numpy(host.sink_k).to(q.device)      # [G][ns][d]
+    sv = torch.from_numpy(host.sink_v).to(q.device)
+    Q = q.permute(1, 0, 2).contiguous()                    # [nh][T][d]
+    K = torch.cat([sk, k.permute(1, 0, 2)], dim=1)         # [G][ns+T][d]
+    V = torch.cat([sv, v.permute(1, 0, 2)], dim=1)
+    K = K.repeat_interleave(H, dim=0).contiguous()         # [nh][ns+T][d]
+    V = V.repeat_interleave(H, dim=0).contiguous()
+    Kt = K.transpose(1, 2).contiguous()                    # [nh][d][ns+T]
+    out = torch.empty_like(Q)
+    B = 2048
+    ns = cfg.ns
+
+    def run():
+        for b0 in range(0, T, B):
+            b1 = min(T, b0 + B)
+            nk = ns + b1
+            s = torch.matmul(Q[:, b0:b1], Kt[:, :, :nk]) * cfg.scale
+            rows = torch.arange(b0, b1, device=q.device)[:, None]
+            cols = torch.arange(nk, device=q.device)[None, :] - ns
+            s.masked_fill_(cols > rows, float("-inf"))
+            p = torch.softmax(s, dim=-1)
+            out[:, b0:b1] = torch.matmul(p, V[:, :nk])
+
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    run()
+    e1.record()
+    torch.cuda.synchronize()
+    return dict(ms=e0.elapsed_time(e1), backend="torch.matmul fp32 blockwise + softmax",
+                rows=T)
+
+
+def cpu_baseline(cfg, budget_s):
+    """The oracle (float64 serial steps, threads = min(G*H, cores)) on the
+    max-window layer: the ring is filled (2048 rows, no outputs), then rows
+    with outputs are stepped in 256-row batches until ~budget_s has passed."""
+    import oracle
+    import synth
+    cores = min(cfg.nh, os.cpu_count() or 1, 16)
+    host = synth.make_state(cfg)
+    orc = oracle.from_config(cfg, host, threads=cores)
+    fill = max(cfg.window(g) for g in range(cfg.G))
+    q, k, v = synth.rows(cfg, 0, fill)
+    orc.step(q, k, v, want=np.zeros(fill, bool))
+    done, r0 = 0, fill
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        q, k, v = synth.rows(cfg, r0, r0 + 256)
+        ts = time.perf_counter()
+        orc.step(q, k, v)
+        done += 256
+        r0 += 256
+        if time.perf_counter() - t0 > 3 * budget_s:
+            break
+        _ = ts
+    el = time.perf_counter() - t0
+    return dict(value=done / el, unit="rows/s", cores=cores, kind="oracle",
+                sample=f"max-window layer rows {fill}..{fill + done} (full window, every row "
+                       f"evicting), after a {fill}-row fill; {el:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--decode-steps", type=int, default=4096)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-exact", dest="exact", action="store_false")
+    ap.add_argument("--no-chunk-api", dest="chunk_api", action="store_false")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this layer runs on a single MI355X here "
+              "(no multi-GPU path is built); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import synth
+    cfg = synth.MAXWIN
+    res = run_gpu(args, cfg)
+    near = res["near"]
+    line = {
+        "metric": "prefill rows/sec per layer (64-row chunks) at w=2048; µs/token decode; % roofline",
+        "value": res["value"],
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "max-window layer: 4 KV groups x 4 query heads, d=dv=128, 4 sinks, "
+                               "w=2048, m=64 landmarks, 32768-row prompt from the empty state as "
+                               "64-row sub-chunks (swl_init_state + swl_prefill)",
+                   "rows_per_step": cfg.rows},
+        "roofline": {"bound": "mfma", "kernel": "k_near<128> (near attention)",
+                     "achieved": near["achieved_tflops"], "peak": MFMA_FP32_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": near["achieved_tflops"] / MFMA_FP32_PEAK_TFLOPS,
+                     "traffic": None,
+                     "avg_launch_ms": near["avg_launch_ms"],
+                     "flops_per_launch": near["flops_per_launch"]},
+        "step": {"algorithmic_flops": res["step_flops"], "tflops": res["step_tflops"],
+                 "frac_mfma_peak": res["step_tflops"] / MFMA_FP32_PEAK_TFLOPS,
+                 "stages_ms": res["stages_ms_per_step"]},
+    }
+    if "decode" in res:
+        line["decode"] = res["decode"]
+    if "chunk_api_rows_per_s" in res:
+        line["chunk_api_rows_per_s"] = res["chunk_api_rows_per_s"]
+    if "exact_attention" in res:
+        line["exact_attention"] = res["exact_attention"]
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -17,7 +17,7 @@
  * Geometry (swl_geom): G KV groups, H query heads per group (nh = G*H,
  * query head gh = g*H + h), m landmarks, W ring stride (the widest group
  * window), ns sinks, d key width, dv value width, scale (usually 1/sqrt(d)),
- * rect (1: clamp u_b at 0).  Supported: d == dv in {16, 32, 64, 128},
+ * rect (1: clamp u_b at 0).  Supported: d == dv in {8, 16, 32, 64, 128},
  * 1 <= m <= 64, 1 <= H <= 16, 1 <= G <= 64, 0 <= ns <= 256, 1 <= W <= 65536.
  *
  * Device arrays (swl_state; all row-major, fp32 unless noted):
@@ -123,6 +123,33 @@ int swl_commit(const swl_geom* geom, const swl_state* st,
 int swl_prefill(const swl_geom* geom, const swl_state* st,
                 const float* q, const float* k, const float* v, int64_t rows,
                 float* out, void* scratch, size_t scratch_bytes, void* stream);
+
+/* Stages of a call, in launch order, as reported to a swl_stage_fn. */
+enum swl_stage {
+    SWL_STAGE_FAR_SCORE = 0,  /* evicted key x landmark scores */
+    SWL_STAGE_FAR_SCAN = 1,   /* post-sub-chunk max, rescale, exp mass and its prefix */
+    SWL_STAGE_DTHETA = 2,     /* value each sub-chunk adds to the far accumulator */
+    SWL_STAGE_THETA_SCAN = 3, /* the accumulator before each sub-chunk; commit of M, Z, Theta */
+    SWL_STAGE_NEAR = 4,       /* sinks + window attention */
+    SWL_STAGE_READOUT = 5,    /* far readout merged with the near part */
+    SWL_STAGE_RING = 6,       /* ring commit */
+    SWL_STAGE_META = 7,       /* len, head, nfar */
+    SWL_STAGE_COUNT = 8
+};
+
+/* Host callback invoked around each launch while the launches are being
+ * enqueued: begin = 1 just before the launch of `stage`, begin = 0 just
+ * after it.  Work the callback enqueues on the same stream (an event
+ * record, for instance) is ordered between that launch and its
+ * neighbours, which is how a caller times one stage on the GPU. */
+typedef void (*swl_stage_fn)(int32_t stage, int32_t begin, void* user);
+
+/* swl_prefill with a stage callback (fn may be NULL: then it is
+ * swl_prefill). */
+int swl_prefill_traced(const swl_geom* geom, const swl_state* st,
+                       const float* q, const float* k, const float* v, int64_t rows,
+                       float* out, void* scratch, size_t scratch_bytes, void* stream,
+                       swl_stage_fn fn, void* user);
 
 /* One row, attended and committed (a sub-chunk of one row; o1c.rs
  * encode_tok): the window is split over blocks whose partials are merged

@@ -25,7 +25,11 @@ SUB = 64
 
 # Entry points declared by include/swl.h.
 EXPORTS = ("swl_scratch_bytes", "swl_init_state", "swl_attend_chunk", "swl_commit",
-           "swl_prefill", "swl_attend_token", "swl_status_str")
+           "swl_prefill", "swl_prefill_traced", "swl_attend_token", "swl_status_str")
+
+# Stage ids of swl_stage_fn (enum swl_stage).
+STAGES = ("far_score", "far_scan", "dtheta", "theta_scan", "near", "readout", "ring", "meta")
+STAGE_FN = ctypes.CFUNCTYPE(None, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p)
 
 
 class SwlError(RuntimeError):
@@ -69,6 +73,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.swl_commit.argtypes = [G, S, _P, _P, ctypes.c_int32, _P, ctypes.c_size_t, _P]
     lib.swl_prefill.restype = ctypes.c_int
     lib.swl_prefill.argtypes = [G, S, _P, _P, _P, ctypes.c_int64, _P, _P, ctypes.c_size_t, _P]
+    lib.swl_prefill_traced.restype = ctypes.c_int
+    lib.swl_prefill_traced.argtypes = [G, S, _P, _P, _P, ctypes.c_int64, _P, _P, ctypes.c_size_t,
+                                       _P, STAGE_FN, _P]
     lib.swl_attend_token.restype = ctypes.c_int
     lib.swl_attend_token.argtypes = [G, S, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.swl_status_str.restype = ctypes.c_char_p
@@ -232,6 +239,19 @@ def swl_prefill(state: LayerState, q, k, v, out, scratch, stream=None):
         ctypes.byref(state.geom.c()), ctypes.byref(state.c()), q.data_ptr(), k.data_ptr(),
         v.data_ptr(), rows, out.data_ptr(), scratch.data_ptr(), scratch.numel(), _stream(stream))
     _raise(rc, "swl_prefill")
+
+
+def swl_prefill_traced(state: LayerState, q, k, v, out, scratch, on_stage, stream=None):
+    """swl_prefill with ``on_stage(stage_name, begin)`` called on the host around
+    every launch (see swl_stage_fn)."""
+    rows = q.shape[0]
+    _rows_args(state, q, k, v, out, rows)
+    cb = STAGE_FN(lambda sid, begin, _u: on_stage(STAGES[sid], bool(begin)))
+    rc = load_library().swl_prefill_traced(
+        ctypes.byref(state.geom.c()), ctypes.byref(state.c()), q.data_ptr(), k.data_ptr(),
+        v.data_ptr(), rows, out.data_ptr(), scratch.data_ptr(), scratch.numel(), _stream(stream),
+        cb, None)
+    _raise(rc, "swl_prefill_traced")
 
 
 def swl_attend_token(state: LayerState, q, k, v, out, scratch, stream=None):

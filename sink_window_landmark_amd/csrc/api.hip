@@ -172,9 +172,9 @@ int swl_commit(const swl_geom* geom, const swl_state* st, const float* k, const 
     return run_commit(p, static_cast<hipStream_t>(stream));
 }
 
-int swl_prefill(const swl_geom* geom, const swl_state* st, const float* q, const float* k,
-                const float* v, int64_t rows, float* out, void* scratch, size_t scratch_bytes,
-                void* stream)
+int swl_prefill_traced(const swl_geom* geom, const swl_state* st, const float* q,
+                       const float* k, const float* v, int64_t rows, float* out, void* scratch,
+                       size_t scratch_bytes, void* stream, swl_stage_fn fn, void* user)
 {
     if (!geom_ok(geom) || !state_ok(geom, st)) return SWL_EINVAL;
     if (rows < 0) return SWL_EINVAL;
@@ -185,6 +185,13 @@ int swl_prefill(const swl_geom* geom, const swl_state* st, const float* q, const
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const int64_t cap = (int64_t)PASS_SUBS * SUB;
     const int nh = geom->G * geom->H;
+#define SWL_STAGE(id, launch)                   \
+    do {                                        \
+        if (fn) fn(id, 1, user);                \
+        hipError_t e_ = (launch);               \
+        if (fn) fn(id, 0, user);                \
+        if (e_ != hipSuccess) return SWL_EHIP;  \
+    } while (0)
     for (int64_t done = 0; done < rows;) {
         const int64_t T = rows - done < cap ? rows - done : cap;
         KParams p = make_params(geom, st);
@@ -197,17 +204,26 @@ int swl_prefill(const swl_geom* geom, const swl_state* st, const float* q, const
         set_scratch(p, geom, scratch, S_max);
         p.theta_prev = p.TH;
         p.theta_prev_stride = (int64_t)nh * geom->m * geom->dv;
-        SWL_TRY(launch_far_score(p, hs));
-        SWL_TRY(launch_far_scan(p, hs));
-        SWL_TRY(launch_dtheta(p, hs));
-        SWL_TRY(launch_theta_scan(p, true, hs));
-        SWL_TRY(launch_near(p, hs));
-        SWL_TRY(launch_readout(p, hs));
-        SWL_TRY(launch_ring_commit(p, hs));
-        SWL_TRY(launch_meta(p, hs));
+        SWL_STAGE(SWL_STAGE_FAR_SCORE, launch_far_score(p, hs));
+        SWL_STAGE(SWL_STAGE_FAR_SCAN, launch_far_scan(p, hs));
+        SWL_STAGE(SWL_STAGE_DTHETA, launch_dtheta(p, hs));
+        SWL_STAGE(SWL_STAGE_THETA_SCAN, launch_theta_scan(p, true, hs));
+        SWL_STAGE(SWL_STAGE_NEAR, launch_near(p, hs));
+        SWL_STAGE(SWL_STAGE_READOUT, launch_readout(p, hs));
+        SWL_STAGE(SWL_STAGE_RING, launch_ring_commit(p, hs));
+        SWL_STAGE(SWL_STAGE_META, launch_meta(p, hs));
         done += T;
     }
+#undef SWL_STAGE
     return SWL_OK;
+}
+
+int swl_prefill(const swl_geom* geom, const swl_state* st, const float* q, const float* k,
+                const float* v, int64_t rows, float* out, void* scratch, size_t scratch_bytes,
+                void* stream)
+{
+    return swl_prefill_traced(geom, st, q, k, v, rows, out, scratch, scratch_bytes, stream,
+                              nullptr, nullptr);
 }
 
 int swl_attend_token(const swl_geom* geom, const swl_state* st, const float* q, const float* k,
