@@ -140,7 +140,7 @@ def run_gpu(args, cfg):
     stages = {}
     for name, a, b in stage_ev:
         stages.setdefault(name, []).append(a.elapsed_time(b))
-    near_ms = stages["near"]
+    near_ms = stages["attend"]
     near_launch_ms = float(np.mean(near_ms))
     near_step_flops = near_flops(cfg, T)
     launches_per_step = len(near_ms) / args.steps
@@ -309,7 +309,7 @@ def main():
                                "w=2048, m=64 landmarks, 32768-row prompt from the empty state as "
                                "64-row sub-chunks (swl_init_state + swl_prefill)",
                    "rows_per_step": cfg.rows},
-        "roofline": {"bound": "mfma", "kernel": "k_near<128> (near attention)",
+        "roofline": {"bound": "mfma", "kernel": "k_attend<128,2> (near attention + far readout)",
                      "achieved": near["achieved_tflops"], "peak": MFMA_FP32_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": near["achieved_tflops"] / MFMA_FP32_PEAK_TFLOPS,
                      "traffic": None,

@@ -130,11 +130,10 @@ enum swl_stage {
     SWL_STAGE_FAR_SCAN = 1,   /* post-sub-chunk max, rescale, exp mass and its prefix */
     SWL_STAGE_DTHETA = 2,     /* value each sub-chunk adds to the far accumulator */
     SWL_STAGE_THETA_SCAN = 3, /* the accumulator before each sub-chunk; commit of M, Z, Theta */
-    SWL_STAGE_NEAR = 4,       /* sinks + window attention */
-    SWL_STAGE_READOUT = 5,    /* far readout merged with the near part */
-    SWL_STAGE_RING = 6,       /* ring commit */
-    SWL_STAGE_META = 7,       /* len, head, nfar */
-    SWL_STAGE_COUNT = 8
+    SWL_STAGE_ATTEND = 4,     /* sinks + window attention and the far readout */
+    SWL_STAGE_RING = 5,       /* ring commit */
+    SWL_STAGE_META = 6,       /* len, head, nfar */
+    SWL_STAGE_COUNT = 7
 };
 
 /* Host callback invoked around each launch while the launches are being

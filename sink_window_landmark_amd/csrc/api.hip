@@ -12,8 +12,6 @@
 
 namespace swl {
 
-size_t readout_lds_bytes(int d, int dv, int m);
-
 static bool geom_ok(const swl_geom* g)
 {
     if (!g) return false;
@@ -42,7 +40,7 @@ static bool state_ok(const swl_geom* g, const swl_state* st)
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Carve {
-    size_t e, p, ms, rs, th, ns, total;
+    size_t e, p, ms, rs, th, total;
 };
 
 static Carve carve(const swl_geom* g, int S)
@@ -55,7 +53,6 @@ static Carve carve(const swl_geom* g, int S)
     c.ms = off; off += align256(sizeof(float) * (size_t)S * nhm);
     c.rs = off; off += align256(sizeof(float) * (size_t)S * nhm);
     c.th = off; off += align256(sizeof(float) * (size_t)S * nhm * g->dv);
-    c.ns = off; off += align256(sizeof(float) * (size_t)S * SUB * g->G * g->H * 2);
     c.total = off;
     return c;
 }
@@ -90,7 +87,6 @@ static void set_scratch(KParams& p, const swl_geom* g, void* scratch, int S)
     p.Ms = reinterpret_cast<float*>(b + c.ms);
     p.Rs = reinterpret_cast<float*>(b + c.rs);
     p.TH = reinterpret_cast<float*>(b + c.th);
-    p.NS = reinterpret_cast<float*>(b + c.ns);
 }
 
 #define SWL_TRY(x)                          \
@@ -98,13 +94,12 @@ static void set_scratch(KParams& p, const swl_geom* g, void* scratch, int S)
         if ((x) != hipSuccess) return SWL_EHIP; \
     } while (0)
 
-// far_e + near + far readout of one call or pass (state unchanged).
+// far_e + attention (near part and far readout) of one call (state unchanged).
 static int run_attend(const KParams& p, hipStream_t st)
 {
     SWL_TRY(launch_far_score(p, st));
     SWL_TRY(launch_far_scan(p, st));
-    SWL_TRY(launch_near(p, st));
-    SWL_TRY(launch_readout(p, st));
+    SWL_TRY(launch_attend(p, st));
     return SWL_OK;
 }
 
@@ -208,8 +203,7 @@ int swl_prefill_traced(const swl_geom* geom, const swl_state* st, const float* q
         SWL_STAGE(SWL_STAGE_FAR_SCAN, launch_far_scan(p, hs));
         SWL_STAGE(SWL_STAGE_DTHETA, launch_dtheta(p, hs));
         SWL_STAGE(SWL_STAGE_THETA_SCAN, launch_theta_scan(p, true, hs));
-        SWL_STAGE(SWL_STAGE_NEAR, launch_near(p, hs));
-        SWL_STAGE(SWL_STAGE_READOUT, launch_readout(p, hs));
+        SWL_STAGE(SWL_STAGE_ATTEND, launch_attend(p, hs));
         SWL_STAGE(SWL_STAGE_RING, launch_ring_commit(p, hs));
         SWL_STAGE(SWL_STAGE_META, launch_meta(p, hs));
         done += T;

@@ -41,7 +41,6 @@ struct KParams {
     float* Ms;   // [S][nh*m]       post-sub-chunk max
     float* Rs;   // [S][nh*m]       rescale of the old mass
     float* TH;   // [S][nh*m][dv]   Theta increments, then Theta before each sub-chunk
-    float* NS;   // [S*SUB][nh][2]  near max and near mass of each row and head
     const float* theta_prev;  // Theta before sub-chunk s at theta_prev + s*theta_prev_stride
     int64_t theta_prev_stride;
 };
@@ -103,8 +102,7 @@ hipError_t launch_far_score(const KParams& p, hipStream_t st);
 hipError_t launch_far_scan(const KParams& p, hipStream_t st);
 hipError_t launch_dtheta(const KParams& p, hipStream_t st);
 hipError_t launch_theta_scan(const KParams& p, bool commit, hipStream_t st);
-hipError_t launch_near(const KParams& p, hipStream_t st);
-hipError_t launch_readout(const KParams& p, hipStream_t st);
+hipError_t launch_attend(const KParams& p, hipStream_t st);
 hipError_t launch_ring_commit(const KParams& p, hipStream_t st);
 hipError_t launch_meta(const KParams& p, hipStream_t st);
 
