@@ -150,9 +150,15 @@ int swl_prefill_traced(const swl_geom* geom, const swl_state* st,
                        float* out, void* scratch, size_t scratch_bytes, void* stream,
                        swl_stage_fn fn, void* user);
 
-/* One row, attended and committed (a sub-chunk of one row; o1c.rs
- * encode_tok): the window is split over blocks whose partials are merged
- * with the far part, then the state advances by one push. */
+/* One row, attended and committed: a sub-chunk of one row (o1c.rs
+ * encode_tok) in two launches.  The row's keys (sinks, then the window after
+ * the push) are split over blocks of 64 keys per group, each writing a
+ * partial (max, mass, value sum) for every head; alongside, each query
+ * head's landmarks fold in the key the row evicts (when the ring is full)
+ * and produce the far part.  A merge per group brings the partials to one
+ * exponent, drops a far part whose mass is not >= 0, writes out, and pushes
+ * the row into the ring.  Same result as attend_chunk + commit with
+ * rows = 1, up to rounding. */
 int swl_attend_token(const swl_geom* geom, const swl_state* st,
                      const float* q, const float* k, const float* v,
                      float* out, void* scratch, size_t scratch_bytes, void* stream);

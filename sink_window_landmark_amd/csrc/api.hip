@@ -40,7 +40,7 @@ static bool state_ok(const swl_geom* g, const swl_state* st)
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Carve {
-    size_t e, p, ms, rs, th, total;
+    size_t e, p, ms, rs, th, tok, total;
 };
 
 static Carve carve(const swl_geom* g, int S)
@@ -53,6 +53,7 @@ static Carve carve(const swl_geom* g, int S)
     c.ms = off; off += align256(sizeof(float) * (size_t)S * nhm);
     c.rs = off; off += align256(sizeof(float) * (size_t)S * nhm);
     c.th = off; off += align256(sizeof(float) * (size_t)S * nhm * g->dv);
+    c.tok = off; off += align256(sizeof(float) * tok_part_floats(g->G, g->H, g->dv, g->ns, g->W));
     c.total = off;
     return c;
 }
@@ -224,9 +225,16 @@ int swl_attend_token(const swl_geom* geom, const swl_state* st, const float* q, 
                      const float* v, float* out, void* scratch, size_t scratch_bytes,
                      void* stream)
 {
-    int rc = swl_attend_chunk(geom, st, q, k, v, 1, out, scratch, scratch_bytes, stream);
-    if (rc != SWL_OK) return rc;
-    return swl_commit(geom, st, k, v, 1, scratch, scratch_bytes, stream);
+    if (!geom_ok(geom) || !state_ok(geom, st)) return SWL_EINVAL;
+    if (!q || !k || !v || !out || !scratch) return SWL_EINVAL;
+    const Carve cv = carve(geom, 1);
+    if (scratch_bytes < cv.total) return SWL_EINVAL;
+    KParams p = make_params(geom, st);
+    p.q = q; p.k = k; p.v = v; p.out = out;
+    p.T = 1; p.S = 1;
+    float* part = reinterpret_cast<float*>(static_cast<char*>(scratch) + cv.tok);
+    SWL_TRY(launch_token(p, part, static_cast<hipStream_t>(stream)));
+    return SWL_OK;
 }
 
 const char* swl_status_str(int status)

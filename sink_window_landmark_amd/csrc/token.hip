@@ -1,0 +1,356 @@
+// One-row decode: a sub-chunk of one row with commit (cortiq-engine 0.8.82
+// src/gpu_metal/o1c.rs, encode_tok: near partials and the far part are
+// independent, then a merge, then the commit), in two launches.
+//
+// k_tok_part: blocks of two kinds run side by side.
+//   near (group g, split sp): keys sp*64 .. sp*64+63 of the row's keys
+//     (the sinks, then the window after the push: logical x of the new ring
+//     at slot (head' + x) mod w_g, the newest one being the row's own key),
+//     for every head of the group: a partial (max, mass, value sum) in
+//     base 2.
+//   far (query head gh, landmark range fb): when the ring is full the row
+//     evicts the key at slot head; every landmark b of the range folds it in
+//     (l = scale <q~_b, k_e>, M' = max(M, l), R = 1 if M' == M else
+//     e^{M-M'}, Z' = R Z + e^{l-M'}, Theta' = R Theta + e^{l-M'} v_e: o1b_far_e
+//     and o1b_far_commit for one row) and writes M', Z', Theta' back.  Then
+//     the far estimate of the range against M': u_b = sum_a e^{f_a-f_max}
+//     mu[a][b] (>= 0 with rect), gain_b against the range's own exponent,
+//     D = sum_b gain_b Z'_b and N = sum_b gain_b Theta'_b -- for a one-row
+//     chunk, the chunk form's R Theta + cf v_e is exactly Theta'.
+// k_tok_merge: one block per group: every head's partials brought to one
+//   exponent c = max of all partial maxima (the pages' c = max(c_near,
+//   f_max + M'_b)), the far part dropped when its total mass is not >= 0,
+//   out = (N + sum p v) / max(D + sum p, 1e-30); then the ring push (the row
+//   to slot head when the ring is full, else to (head + len)) and meta.
+#include "swl_internal.h"
+
+namespace swl {
+
+constexpr int TOK_KEYS = 64;    // keys per near block
+constexpr int TOK_FB = 2;       // far blocks per query head
+constexpr int TOK_THREADS = 256;
+constexpr float TOK_LOG2E = 1.4426950408889634f;
+
+int tok_splits(int ns, int W) { return (ns + W + TOK_KEYS - 1) / TOK_KEYS; }
+
+// partial record: [0] max (base 2), [1] mass, [2 .. 2+dv) value sum
+__host__ __device__ inline int64_t tok_rec(int dv) { return 2 + dv; }
+
+size_t tok_part_floats(int G, int H, int dv, int ns, int W)
+{
+    return (size_t)G * tok_splits(ns, W) * H * tok_rec(dv) + (size_t)G * H * TOK_FB * tok_rec(dv);
+}
+
+struct TokRow {
+    int full, slot, len1, head1, nfar1;
+};
+
+__device__ __forceinline__ TokRow tok_row(const GMeta& c)
+{
+    TokRow r;
+    r.full = c.len0 >= c.wg;
+    r.slot = r.full ? c.head0 : (c.head0 + c.len0) % c.wg;
+    r.len1 = r.full ? c.wg : c.len0 + 1;
+    r.head1 = r.full ? (c.head0 + 1) % c.wg : c.head0;
+    r.nfar1 = c.nfar0 + (r.full ? 1 : 0);
+    return r;
+}
+
+__device__ __forceinline__ float wsum(float x)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+__device__ __forceinline__ float wmax(float x)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+    return x;
+}
+
+__global__ __launch_bounds__(TOK_THREADS) void k_tok_part(KParams p, float* part, int nsplit)
+{
+    extern __shared__ float lds[];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int d = p.d, dv = p.dv, H = p.H, m = p.m;
+    const int nnear = p.G * nsplit;
+    float* nearp = part;                                           // [G][nsplit][H][rec]
+    float* farp = part + (int64_t)p.G * nsplit * H * tok_rec(dv);  // [nh][FB][rec]
+
+    if ((int)blockIdx.x < nnear) {
+        // ---------------- near partial ----------------
+        const int g = blockIdx.x / nsplit, sp = blockIdx.x % nsplit;
+        const GMeta c = load_gmeta(p.meta, g, p.W);
+        const TokRow r = tok_row(c);
+        const int n = p.ns + r.len1;
+        const int k0 = sp * TOK_KEYS, k1 = min(n, k0 + TOK_KEYS);
+        float* base = nearp + (int64_t)g * nsplit * H * tok_rec(dv);
+        if (k0 >= k1) {
+            for (int e = tid; e < H * tok_rec(dv); e += TOK_THREADS) {
+                const int h = e / tok_rec(dv), f = e % tok_rec(dv);
+                base[((int64_t)sp * H + h) * tok_rec(dv) + f] = f == 0 ? -INFINITY : 0.f;
+            }
+            return;
+        }
+        const int LDK = d + 4, LDV = dv + 4;
+        float* Kl = lds;                      // [64][d+4]
+        float* Vl = Kl + TOK_KEYS * LDK;      // [64][dv+4]
+        float* Ql = Vl + TOK_KEYS * LDV;      // [H][d]
+        for (int e = tid; e < TOK_KEYS * (d / 4); e += TOK_THREADS) {
+            const int row = e / (d / 4), c4 = (e % (d / 4)) * 4;
+            const int x = k0 + row;
+            float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
+            if (x < k1) {
+                const float *kp, *vp;
+                if (x < p.ns) {
+                    kp = p.sink_k + ((int64_t)g * p.ns + x) * d;
+                    vp = p.sink_v + ((int64_t)g * p.ns + x) * dv;
+                } else if (x - p.ns == r.len1 - 1) {   // the row's own key
+                    kp = p.k + (int64_t)g * d;
+                    vp = p.v + (int64_t)g * dv;
+                } else {
+                    const int slot = (r.head1 + x - p.ns) % c.wg;
+                    kp = p.ring_k + ((int64_t)g * p.W + slot) * d;
+                    vp = p.ring_v + ((int64_t)g * p.W + slot) * dv;
+                }
+                kx = *reinterpret_cast<const float4*>(kp + c4);
+                vx = *reinterpret_cast<const float4*>(vp + c4);
+            }
+            *reinterpret_cast<float4*>(Kl + row * LDK + c4) = kx;
+            *reinterpret_cast<float4*>(Vl + row * LDV + c4) = vx;
+        }
+        const float qs = p.scale * TOK_LOG2E;
+        for (int e = tid; e < H * d; e += TOK_THREADS) Ql[e] = p.q[(int64_t)g * H * d + e] * qs;
+        __syncthreads();
+        const int nk = k1 - k0;
+        for (int h = wave; h < H; h += TOK_THREADS / 64) {
+            // lane = key
+            float sc = -INFINITY;
+            if (lane < nk) {
+                const float* kr = Kl + lane * LDK;
+                const float* qr = Ql + h * d;
+                float acc = 0.f;
+                for (int t = 0; t < d; t += 4) {
+                    const float4 a = *reinterpret_cast<const float4*>(kr + t);
+                    const float4 b = *reinterpret_cast<const float4*>(qr + t);
+                    acc += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+                }
+                sc = acc;
+            }
+            const float mx = wmax(sc);
+            const float pv = lane < nk ? exp2f(sc - mx) : 0.f;
+            const float l = wsum(pv);
+            float* rec = base + ((int64_t)sp * H + h) * tok_rec(dv);
+            // value sum: lanes over value columns, p_j broadcast by shuffle
+            for (int t0 = 0; t0 < dv; t0 += 64) {
+                const int t = t0 + lane;
+                float acc = 0.f;
+                for (int j = 0; j < nk; ++j) {
+                    const float pj = __shfl(pv, j, 64);
+                    if (t < dv) acc += pj * Vl[j * LDV + t];
+                }
+                if (t < dv) rec[2 + t] = acc;
+            }
+            if (lane == 0) {
+                rec[0] = mx;
+                rec[1] = l;
+            }
+        }
+        return;
+    }
+
+    // ---------------- far partial ----------------
+    const int fbk = blockIdx.x - nnear;
+    const int gh = fbk / TOK_FB, fb = fbk % TOK_FB;
+    const int g = gh / H;
+    const GMeta c = load_gmeta(p.meta, g, p.W);
+    const TokRow r = tok_row(c);
+    float* rec = farp + ((int64_t)gh * TOK_FB + fb) * tok_rec(dv);
+    const int per = (m + TOK_FB - 1) / TOK_FB;
+    const int b0 = fb * per, b1 = min(m, b0 + per), nb = b1 - b0;
+    if (r.nfar1 == 0 || nb <= 0) {
+        for (int t = tid; t < tok_rec(dv); t += TOK_THREADS) rec[t] = t == 0 ? -INFINITY : 0.f;
+        return;
+    }
+    float* Ql = lds;      // [d]
+    float* KE = Ql + d;   // [d]   evicted key
+    float* VE = KE + d;   // [dv]  evicted value
+    float* EA = VE + dv;  // [64]  f_a, then e_a
+    float* MB = EA + 64;  // [64]  M'
+    float* RB = MB + 64;  // [64]  R
+    float* XB = RB + 64;  // [64]  exp(l - M')
+    float* ZB = XB + 64;  // [64]  Z'
+    float* UB = ZB + 64;  // [64]  u_b
+    float* GB = UB + 64;  // [64]  gains
+    float* RED = GB + 64; // [4]
+    for (int t = tid; t < d; t += TOK_THREADS) {
+        Ql[t] = p.q[(int64_t)gh * d + t];
+        KE[t] = r.full ? p.ring_k[((int64_t)g * p.W + c.head0) * d + t] : 0.f;
+    }
+    for (int t = tid; t < dv; t += TOK_THREADS)
+        VE[t] = r.full ? p.ring_v[((int64_t)g * p.W + c.head0) * dv + t] : 0.f;
+    __syncthreads();
+    float* mz = p.mz + (int64_t)gh * 2 * m;
+    if (tid < m) {
+        // f_a in base 2 for every landmark
+        const float* kt = p.k_tilde + ((int64_t)g * m + tid) * d;
+        float acc = 0.f;
+        for (int t = 0; t < d; t += 4) {
+            const float4 x = *reinterpret_cast<const float4*>(kt + t);
+            acc += x.x * Ql[t] + x.y * Ql[t + 1] + x.z * Ql[t + 2] + x.w * Ql[t + 3];
+        }
+        EA[tid] = acc * p.scale * TOK_LOG2E;
+    } else if (tid >= 64 && tid - 64 < nb) {
+        // the evicted key folded into landmark b
+        const int b = b0 + tid - 64;
+        const float Mo = mz[b], Zo = mz[m + b];
+        float Mn = Mo, R = 1.f, x = 0.f, Zn = Zo;
+        if (r.full) {
+            const float* qt = p.q_tilde + ((int64_t)gh * m + b) * d;
+            float acc = 0.f;
+            for (int t = 0; t < d; t += 4) {
+                const float4 y = *reinterpret_cast<const float4*>(qt + t);
+                acc += y.x * KE[t] + y.y * KE[t + 1] + y.z * KE[t + 2] + y.w * KE[t + 3];
+            }
+            const float l = acc * p.scale;
+            Mn = fmaxf(Mo, l);
+            R = (Mn == Mo) ? 1.f : expf(Mo - Mn);
+            x = expf(l - Mn);
+            Zn = Zo * R + x;
+            mz[b] = Mn;
+            mz[m + b] = Zn;
+        }
+        MB[b - b0] = Mn;
+        RB[b - b0] = R;
+        XB[b - b0] = x;
+        ZB[b - b0] = Zn;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const float f = lane < m ? EA[lane] : -INFINITY;
+        const float fmax = wmax(f);
+        if (lane < m) EA[lane] = exp2f(f - fmax);
+        if (lane == 0) RED[0] = fmax;
+    } else if (wave == 1) {
+        const float mm = wmax(lane < nb ? MB[lane] : -INFINITY);
+        if (lane == 0) RED[1] = mm;
+    }
+    __syncthreads();
+    const float fmax = RED[0];
+    const float cl = fmax + RED[1] * TOK_LOG2E;   // the range's exponent, base 2
+    if (tid < nb) {
+        const int b = b0 + tid;
+        const float* mu = p.mu + (int64_t)gh * m * m;
+        float u = 0.f;
+        for (int a = 0; a < m; ++a) u += EA[a] * mu[(int64_t)a * m + b];
+        if (p.rect) u = fmaxf(u, 0.f);
+        GB[tid] = u * exp2f(fmax + MB[tid] * TOK_LOG2E - cl);
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const float dd = wsum(lane < nb ? GB[lane] * ZB[lane] : 0.f);
+        if (lane == 0) {
+            rec[0] = cl;
+            rec[1] = dd;
+        }
+    }
+    float* th = p.theta + ((int64_t)gh * m + b0) * dv;
+    for (int t = tid; t < dv; t += TOK_THREADS) {
+        float acc = 0.f;
+        for (int j = 0; j < nb; ++j) {
+            float v = th[(int64_t)j * dv + t];
+            if (r.full) {
+                v = v * RB[j] + XB[j] * VE[t];
+                th[(int64_t)j * dv + t] = v;
+            }
+            acc += GB[j] * v;
+        }
+        rec[2 + t] = acc;
+    }
+}
+
+__global__ __launch_bounds__(TOK_THREADS) void k_tok_merge(KParams p, const float* part, int nsplit)
+{
+    const int g = blockIdx.x;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int H = p.H, dv = p.dv;
+    const GMeta c = load_gmeta(p.meta, g, p.W);
+    const TokRow r = tok_row(c);
+    const float* nearp = part + (int64_t)g * nsplit * H * tok_rec(dv);
+    const float* farp = part + (int64_t)p.G * nsplit * H * tok_rec(dv);
+    for (int h = wave; h < H; h += TOK_THREADS / 64) {
+        const int gh = g * H + h;
+        float cmax = -INFINITY;
+        for (int sp = lane; sp < nsplit; sp += 64)
+            cmax = fmaxf(cmax, nearp[((int64_t)sp * H + h) * tok_rec(dv)]);
+        if (r.nfar1 > 0)
+            for (int fb = lane; fb < TOK_FB; fb += 64)
+                cmax = fmaxf(cmax, farp[((int64_t)gh * TOK_FB + fb) * tok_rec(dv)]);
+        cmax = wmax(cmax);
+        float den = 0.f;
+        for (int sp = lane; sp < nsplit; sp += 64) {
+            const float* rc = nearp + ((int64_t)sp * H + h) * tok_rec(dv);
+            den += rc[1] * exp2f(rc[0] - cmax);
+        }
+        den = wsum(den);
+        float dfar = 0.f;
+        if (r.nfar1 > 0) {
+            for (int fb = 0; fb < TOK_FB; ++fb) {
+                const float* rc = farp + ((int64_t)gh * TOK_FB + fb) * tok_rec(dv);
+                dfar += rc[1] * exp2f(rc[0] - cmax);
+            }
+        }
+        const bool have = r.nfar1 > 0 && dfar >= 0.f;
+        const float inv = 1.f / fmaxf(den + (have ? dfar : 0.f), 1e-30f);
+        float* orow = p.out + (int64_t)gh * dv;
+        for (int t = lane; t < dv; t += 64) {
+            float acc = 0.f;
+            for (int sp = 0; sp < nsplit; ++sp) {
+                const float* rc = nearp + ((int64_t)sp * H + h) * tok_rec(dv);
+                acc += rc[2 + t] * exp2f(rc[0] - cmax);
+            }
+            if (have)
+                for (int fb = 0; fb < TOK_FB; ++fb) {
+                    const float* rc = farp + ((int64_t)gh * TOK_FB + fb) * tok_rec(dv);
+                    acc += rc[2 + t] * exp2f(rc[0] - cmax);
+                }
+            orow[t] = acc * inv;
+        }
+    }
+    // commit: ring push and meta (every reader of this group is done)
+    float* kd = p.ring_k + ((int64_t)g * p.W + r.slot) * p.d;
+    float* vd = p.ring_v + ((int64_t)g * p.W + r.slot) * dv;
+    for (int t = tid; t < p.d; t += TOK_THREADS) kd[t] = p.k[(int64_t)g * p.d + t];
+    for (int t = tid; t < dv; t += TOK_THREADS) vd[t] = p.v[(int64_t)g * dv + t];
+    if (tid == 0) {
+        p.meta[4 * g + 0] = (uint32_t)r.len1;
+        p.meta[4 * g + 1] = (uint32_t)r.head1;
+        p.meta[4 * g + 2] = (uint32_t)r.nfar1;
+    }
+}
+
+hipError_t launch_token(const KParams& p, float* part, hipStream_t st)
+{
+    const int nsplit = tok_splits(p.ns, p.W);
+    const size_t lds_near = sizeof(float) * ((size_t)TOK_KEYS * (p.d + 4) +
+                                             (size_t)TOK_KEYS * (p.dv + 4) + (size_t)p.H * p.d);
+    const size_t lds_far = sizeof(float) * ((size_t)2 * p.d + p.dv + 7 * 64 + 4);
+    const size_t lds = lds_near > lds_far ? lds_near : lds_far;
+    const int blocks = p.G * nsplit + p.nh * TOK_FB;
+    static bool attr_set = false;
+    if (!attr_set) {
+        (void)hipFuncSetAttribute((const void*)k_tok_part,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(k_tok_part, dim3(blocks), dim3(TOK_THREADS), lds, st, p, part, nsplit);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_tok_merge, dim3(p.G), dim3(TOK_THREADS), 0, st, p, (const float*)part,
+                       nsplit);
+    return hipGetLastError();
+}
+
+}  // namespace swl

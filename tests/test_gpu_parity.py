@@ -257,3 +257,67 @@ def test_zero_rows_is_a_noop():
     after = read_state(st)
     for f in before:
         np.testing.assert_array_equal(before[f], after[f])
+
+
+def _tokens(cfg, st, q, k, v):
+    t = torch()
+    scratch = swl.alloc_scratch(st.geom, 1)
+    scratch.view(t.float32)[: scratch.numel() // 4].fill_(float("nan"))
+    n = q.shape[0]
+    outs = t.empty((n, cfg.nh, cfg.dv), dtype=t.float32, device="cuda")
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    for i in range(n):
+        swl.swl_attend_token(st, qd[i:i + 1], kd[i:i + 1], vd[i:i + 1], outs[i:i + 1], scratch)
+    t.cuda.synchronize()
+    return outs.cpu().numpy()
+
+
+@pytest.mark.parametrize("head0", [0, 13])
+def test_tokens_fill_then_evict(head0):
+    """The one-row path from a ring 10/16 with an empty far field: the ring
+    fills, the first eviction meets M = -inf, then every row evicts."""
+    banner(f"tokens on the tiny layer, head0={head0}")
+    cfg = synth.TINY.replace(head0=head0)
+    host = synth.make_state(cfg)
+    q, k, v = synth.rows(cfg, 0, 40)
+    st = _state(cfg, host)
+    got = _tokens(cfg, st, q, k, v)
+    orc = oracle.from_config(cfg, host)
+    check_out(got, orc.step(q, k, v))
+    check_state(read_state(st), orc)
+
+
+@pytest.mark.parametrize("rect", [False, True])
+def test_tokens_windows_and_guard(rect):
+    banner(f"tokens with per-group windows and mixed-sign mu, rect={rect}")
+    cfg = synth.Config("tokw", G=2, H=3, d=64, dv=64, ns=3, W=20, m=16, rows=0,
+                       windows=(12, 20), len0=0, rect=rect)
+    host = synth.make_state(cfg)
+    r = np.random.default_rng(5)
+    host.mu = (r.standard_normal(host.mu.shape) / cfg.m).astype(np.float32)
+    host.mu[1] = -np.abs(host.mu[1])
+    q, k, v = synth.rows(cfg, 0, 70)
+    st = _state(cfg, host)
+    got = _tokens(cfg, st, q, k, v)
+    orc = oracle.from_config(cfg, host)
+    check_out(got, orc.step(q, k, v))
+    check_state(read_state(st), orc)
+
+
+def test_tokens_after_chunks_match_chunk_path():
+    """Tokens and one-row chunks agree from the same state."""
+    banner("tokens vs one-row chunks")
+    cfg = synth.SMALL.replace(rows=1100, W=1024)
+    host = synth.make_state(cfg)
+    q, k, v = synth.rows(cfg, 0, 1100)
+    a = _state(cfg, host)
+    _prefill(cfg, a, q[:1000], k[:1000], v[:1000])
+    b = a.clone()
+    got_t = _tokens(cfg, a, q[1000:], k[1000:], v[1000:])
+    got_c = _chunks(cfg, b, q[1000:], k[1000:], v[1000:], [1] * 100)
+    orc = oracle.from_config(cfg, host, threads=oracle_threads())
+    orc.step(q[:1000], k[:1000], v[:1000], want=np.zeros(1000, bool))
+    want = orc.step(q[1000:], k[1000:], v[1000:])
+    check_out(got_t, want, "tokens")
+    check_out(got_c, want, "chunks")
+    check_state(read_state(a), orc)
