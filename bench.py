@@ -282,6 +282,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-exact", dest="exact", action="store_false")
     ap.add_argument("--no-chunk-api", dest="chunk_api", action="store_false")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB device-to-device copy (the reference kernel "
+                         "for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this layer runs on a single MI355X here "
@@ -290,6 +293,13 @@ def main():
 
     import synth
     cfg = synth.MAXWIN
+    if args.calibrate_copy:
+        import torch
+        a = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
     res = run_gpu(args, cfg)
     near = res["near"]
     line = {

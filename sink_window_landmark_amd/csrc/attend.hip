@@ -49,6 +49,10 @@ __device__ __forceinline__ floatx16 mfma32(float a, float b, floatx16 c)
 
 __device__ __forceinline__ int kap(int v, int hf) { return (v >> 2) * 8 + hf * 4 + (v & 3); }
 
+// 2^x as the bare v_exp_f32 (results below 2^-126 flush to 0, which only
+// drops softmax weights far below the running maximum)
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ void zero16(floatx16& x)
 {
 #pragma unroll
@@ -89,10 +93,14 @@ __global__ __launch_bounds__(AT_THREADS) void k_attend(KParams p)
     __shared__ float Ks[2 * KT][LD];
     __shared__ float Vs[2 * KT][LD];
 
-    const int s = blockIdx.x, g = blockIdx.y;
+    // work item = (head group, group, sub-chunk), sub-chunk fastest, dealt
+    // to XCDs in contiguous runs
+    const int hgroups = (p.H + 3) / 4;
+    const int w = xcd_work_item(blockIdx.x, p.S * p.G * hgroups);
+    const int s = w % p.S, g = (w / p.S) % p.G, hgrp = w / (p.S * p.G);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int hf = lane >> 5, ln = lane & 31;
-    const int h = blockIdx.z * 4 + (wave >> 1);
+    const int h = hgrp * 4 + (wave >> 1);
     const bool active = h < p.H;
     const int gh = g * p.H + h;
     const int r0 = s * SUB;
@@ -139,24 +147,33 @@ __global__ __launch_bounds__(AT_THREADS) void k_attend(KParams p)
             float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
             if (e < F4) {
                 const int row = e / (D / 4), c4 = (e % (D / 4)) * 4;
-                const float* kp = nullptr;
-                const float* vp = nullptr;
+                const float* kb = nullptr;
+                const float* vb = nullptr;
+                uint32_t off = 0;
                 if (tt < nst) {
                     const int x = tt * KT + row;
                     if (x < p.ns) {
-                        kp = p.sink_k + ((int64_t)g * p.ns + x) * D;
-                        vp = p.sink_v + ((int64_t)g * p.ns + x) * D;
+                        kb = p.sink_k;
+                        vb = p.sink_v;
+                        off = (uint32_t)(g * p.ns + x) * D;
                     }
                 } else {
                     const int pos = lo_blk + (tt - nst) * KT + row;
                     if (pos <= hi_blk) {
-                        kp = key_row(p, c, g, pos);
-                        vp = val_row(p, c, g, pos);
+                        if (pos < c.len0) {
+                            kb = p.ring_k;
+                            vb = p.ring_v;
+                            off = (uint32_t)(g * p.W + (uint32_t)(c.head0 + pos) % (uint32_t)c.wg) * D;
+                        } else {
+                            kb = p.k;
+                            vb = p.v;
+                            off = (uint32_t)((pos - c.len0) * p.G + g) * D;
+                        }
                     }
                 }
-                if (kp) {
-                    kx = *reinterpret_cast<const float4*>(kp + c4);
-                    vx = *reinterpret_cast<const float4*>(vp + c4);
+                if (kb) {
+                    kx = *reinterpret_cast<const float4*>(kb + off + c4);
+                    vx = *reinterpret_cast<const float4*>(vb + off + c4);
                 }
             }
             kreg[u] = kx;
@@ -205,43 +222,49 @@ __global__ __launch_bounds__(AT_THREADS) void k_attend(KParams p)
             sacc = mfma32(a.w, qf[st + 3], sacc);
         }
         // sinks are always visible; the window key at position tb + kappa is
-        // visible to row i when lo_q <= pos <= hi_q
-        const bool full = !sink && tb >= lo_ib && tb + KT - 1 <= base + ia;
+        // visible to row i when lo_q <= pos <= hi_q (every row of the wave
+        // sees every key of a "full" tile)
         float tmax = -INFINITY;
+        if (!sink && tb >= lo_ib && tb + KT - 1 <= base + ia) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int kp = kap(v, hf);
-            bool ok;
-            if (sink) ok = tb + kp < p.ns;
-            else if (full) ok = true;
-            else {
-                const int pos = tb + kp;
-                ok = pos >= lo_q && pos <= hi_q;
+            for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sacc[v]);
+        } else if (sink) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float sv = tb + kap(v, hf) < p.ns ? sacc[v] : -INFINITY;
+                sacc[v] = sv;
+                tmax = fmaxf(tmax, sv);
             }
-            const float sv = ok ? sacc[v] : -INFINITY;
-            sacc[v] = sv;
-            tmax = fmaxf(tmax, sv);
+        } else {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int pos = tb + kap(v, hf);
+                const float sv = (pos >= lo_q && pos <= hi_q) ? sacc[v] : -INFINITY;
+                sacc[v] = sv;
+                tmax = fmaxf(tmax, sv);
+            }
         }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float mnew = fmaxf(mrun, tmax);
-        float alpha = 1.f, msub = 0.f;
-        if (mnew != -INFINITY) {
-            alpha = exp2f(mrun - mnew);
-            msub = mnew;
+        // rescale the running sums only when some query's maximum rises
+        if (__any(tmax > mrun)) {
+            const float mnew = fmaxf(mrun, tmax);
+            const float alpha = mnew == -INFINITY ? 1.f : ex2(mrun - mnew);
+            lsum *= alpha;
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) O[b][v] *= alpha;
+            mrun = mnew;
         }
+        const float msub = mrun == -INFINITY ? 0.f : mrun;
         float ts = 0.f;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const float pv = exp2f(sacc[v] - msub);
+            const float pv = ex2(sacc[v] - msub);
             sacc[v] = pv;
             ts += pv;
         }
-        lsum = lsum * alpha + ts;
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) O[b][v] *= alpha;
-        mrun = mnew;
+        lsum += ts;
 #pragma unroll
         for (int t = 0; t < 16; ++t) pv_step<D, NB>(O, &Vs[buf * KT + kap(t, hf)][0], ln, sacc[t]);
     }
@@ -306,7 +329,7 @@ __global__ __launch_bounds__(AT_THREADS) void k_attend(KParams p)
 #pragma unroll
             for (int at = 0; at < MT; ++at)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) ef[at][v] = exp2f(ef[at][v] - fmax);
+                for (int v = 0; v < 16; ++v) ef[at][v] = ex2(ef[at][v] - fmax);
 
             // u^T = mu^T e^T: A[b][a] = mu[a][b] straight from memory
             const float* mu = p.mu + (int64_t)gh * m * m;
@@ -348,7 +371,7 @@ __global__ __launch_bounds__(AT_THREADS) void k_attend(KParams p)
                     const int b = bt * 32 + kap(v, hf);
                     float u = gn[bt][v];
                     if (p.rect) u = fmaxf(u, 0.f);
-                    const float gain = (lane_far && b < m) ? u * exp2f(fmax + mb[bt][v] - cexp) : 0.f;
+                    const float gain = (lane_far && b < m) ? u * ex2(fmax + mb[bt][v] - cexp) : 0.f;
                     gn[bt][v] = gain;
                     if (b < m && lane_far) dfar += gain * Pb[(int64_t)b * SUB + i];
                 }
@@ -383,7 +406,7 @@ __global__ __launch_bounds__(AT_THREADS) void k_attend(KParams p)
                 }
             }
             // near part to the common exponent, then the far numerator
-            const float wn = exp2f(mrun - cexp);
+            const float wn = ex2(mrun - cexp);
 #pragma unroll
             for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -431,7 +454,7 @@ __global__ __launch_bounds__(AT_THREADS) void k_attend(KParams p)
 template <int D>
 static hipError_t launch_d(const KParams& p, hipStream_t st)
 {
-    dim3 grid(p.S, p.G, (p.H + 3) / 4);
+    dim3 grid(p.S * p.G * ((p.H + 3) / 4));
     if (p.m <= 32) hipLaunchKernelGGL((k_attend<D, 1>), grid, dim3(AT_THREADS), 0, st, p);
     else hipLaunchKernelGGL((k_attend<D, 2>), grid, dim3(AT_THREADS), 0, st, p);
     return hipGetLastError();

@@ -96,6 +96,18 @@ __device__ __forceinline__ const float* val_row(const KParams& p, const GMeta& c
     return p.v + ((int64_t)(pos - c.len0) * p.G + g) * p.dv;
 }
 
+// Work item of linear workgroup b out of n when the hardware deals
+// workgroups round-robin over the 8 XCDs (b goes to XCD b mod 8, each with
+// its own L2): XCD x takes the contiguous run of work items
+// [x*q + min(x, r), ...) with q = n / 8, r = n % 8, so neighbouring work
+// items (which share keys) meet in the same L2.
+__device__ __forceinline__ int xcd_work_item(int b, int n)
+{
+    const int x = b & 7, k = b >> 3;
+    const int q = n >> 3, r = n & 7;
+    return x * q + (x < r ? x : r) + k;
+}
+
 // Launchers (each returns the launch's hipGetLastError).
 hipError_t launch_init(const KParams& p, const uint32_t* windows, hipStream_t st);
 hipError_t launch_far_score(const KParams& p, hipStream_t st);

@@ -17,17 +17,19 @@
 //     mu[a][b] (>= 0 with rect), gain_b against the range's own exponent,
 //     D = sum_b gain_b Z'_b and N = sum_b gain_b Theta'_b -- for a one-row
 //     chunk, the chunk form's R Theta + cf v_e is exactly Theta'.
-// k_tok_merge: one block per group: every head's partials brought to one
+// k_tok_merge: one block per query head: the head's partials brought to one
 //   exponent c = max of all partial maxima (the pages' c = max(c_near,
 //   f_max + M'_b)), the far part dropped when its total mass is not >= 0,
-//   out = (N + sum p v) / max(D + sum p, 1e-30); then the ring push (the row
-//   to slot head when the ring is full, else to (head + len)) and meta.
+//   out = (N + sum p v) / max(D + sum p, 1e-30); the first head of each
+//   group then pushes the row into the ring (slot head when the ring is full,
+//   else (head + len)) and advances meta.
 #include "swl_internal.h"
 
 namespace swl {
 
 constexpr int TOK_KEYS = 64;    // keys per near block
-constexpr int TOK_FB = 2;       // far blocks per query head
+constexpr int TOK_FB = 4;       // far blocks per query head (landmark ranges)
+constexpr int TOK_BMAX = 16;    // landmarks per far block (m <= 64)
 constexpr int TOK_THREADS = 256;
 constexpr float TOK_LOG2E = 1.4426950408889634f;
 
@@ -168,23 +170,23 @@ __global__ __launch_bounds__(TOK_THREADS) void k_tok_part(KParams p, float* part
     const GMeta c = load_gmeta(p.meta, g, p.W);
     const TokRow r = tok_row(c);
     float* rec = farp + ((int64_t)gh * TOK_FB + fb) * tok_rec(dv);
-    const int per = (m + TOK_FB - 1) / TOK_FB;
+    const int per = (m + TOK_FB - 1) / TOK_FB;   // <= TOK_BMAX
     const int b0 = fb * per, b1 = min(m, b0 + per), nb = b1 - b0;
     if (r.nfar1 == 0 || nb <= 0) {
         for (int t = tid; t < tok_rec(dv); t += TOK_THREADS) rec[t] = t == 0 ? -INFINITY : 0.f;
         return;
     }
-    float* Ql = lds;      // [d]
-    float* KE = Ql + d;   // [d]   evicted key
-    float* VE = KE + d;   // [dv]  evicted value
-    float* EA = VE + dv;  // [64]  f_a, then e_a
-    float* MB = EA + 64;  // [64]  M'
-    float* RB = MB + 64;  // [64]  R
-    float* XB = RB + 64;  // [64]  exp(l - M')
-    float* ZB = XB + 64;  // [64]  Z'
-    float* UB = ZB + 64;  // [64]  u_b
-    float* GB = UB + 64;  // [64]  gains
-    float* RED = GB + 64; // [4]
+    float* Ql = lds;         // [d]
+    float* KE = Ql + d;      // [d]   evicted key
+    float* VE = KE + d;      // [dv]  evicted value
+    float* EA = VE + dv;     // [64]  f_a, then e_a
+    float* MB = EA + 64;     // [16]  M'
+    float* RB = MB + 16;     // [16]  R
+    float* XB = RB + 16;     // [16]  exp(l - M')
+    float* ZB = XB + 16;     // [16]  Z'
+    float* GB = ZB + 16;     // [16]  gains
+    float* RED = GB + 16;    // [4]
+    float* NP = RED + 4;     // [2][dv] partial numerators of the two b halves
     for (int t = tid; t < d; t += TOK_THREADS) {
         Ql[t] = p.q[(int64_t)gh * d + t];
         KE[t] = r.full ? p.ring_k[((int64_t)g * p.W + c.head0) * d + t] : 0.f;
@@ -195,24 +197,36 @@ __global__ __launch_bounds__(TOK_THREADS) void k_tok_part(KParams p, float* part
     float* mz = p.mz + (int64_t)gh * 2 * m;
     if (tid < m) {
         // f_a in base 2 for every landmark
-        const float* kt = p.k_tilde + ((int64_t)g * m + tid) * d;
+        const float4* kt = reinterpret_cast<const float4*>(p.k_tilde + ((int64_t)g * m + tid) * d);
         float acc = 0.f;
-        for (int t = 0; t < d; t += 4) {
-            const float4 x = *reinterpret_cast<const float4*>(kt + t);
-            acc += x.x * Ql[t] + x.y * Ql[t + 1] + x.z * Ql[t + 2] + x.w * Ql[t + 3];
+        for (int t4 = 0; t4 < d / 4; t4 += 8) {
+            float4 x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) x[u] = t4 + u < d / 4 ? kt[t4 + u] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int t = 4 * (t4 + u);
+                if (t < d) acc += x[u].x * Ql[t] + x[u].y * Ql[t + 1] + x[u].z * Ql[t + 2] + x[u].w * Ql[t + 3];
+            }
         }
         EA[tid] = acc * p.scale * TOK_LOG2E;
     } else if (tid >= 64 && tid - 64 < nb) {
         // the evicted key folded into landmark b
-        const int b = b0 + tid - 64;
+        const int j = tid - 64, b = b0 + j;
         const float Mo = mz[b], Zo = mz[m + b];
         float Mn = Mo, R = 1.f, x = 0.f, Zn = Zo;
         if (r.full) {
-            const float* qt = p.q_tilde + ((int64_t)gh * m + b) * d;
+            const float4* qt = reinterpret_cast<const float4*>(p.q_tilde + ((int64_t)gh * m + b) * d);
             float acc = 0.f;
-            for (int t = 0; t < d; t += 4) {
-                const float4 y = *reinterpret_cast<const float4*>(qt + t);
-                acc += y.x * KE[t] + y.y * KE[t + 1] + y.z * KE[t + 2] + y.w * KE[t + 3];
+            for (int t4 = 0; t4 < d / 4; t4 += 8) {
+                float4 y[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) y[u] = t4 + u < d / 4 ? qt[t4 + u] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int t = 4 * (t4 + u);
+                    if (t < d) acc += y[u].x * KE[t] + y[u].y * KE[t + 1] + y[u].z * KE[t + 2] + y[u].w * KE[t + 3];
+                }
             }
             const float l = acc * p.scale;
             Mn = fmaxf(Mo, l);
@@ -222,10 +236,10 @@ __global__ __launch_bounds__(TOK_THREADS) void k_tok_part(KParams p, float* part
             mz[b] = Mn;
             mz[m + b] = Zn;
         }
-        MB[b - b0] = Mn;
-        RB[b - b0] = R;
-        XB[b - b0] = x;
-        ZB[b - b0] = Zn;
+        MB[j] = Mn;
+        RB[j] = R;
+        XB[j] = x;
+        ZB[j] = Zn;
     }
     __syncthreads();
     if (wave == 0) {
@@ -241,10 +255,16 @@ __global__ __launch_bounds__(TOK_THREADS) void k_tok_part(KParams p, float* part
     const float fmax = RED[0];
     const float cl = fmax + RED[1] * TOK_LOG2E;   // the range's exponent, base 2
     if (tid < nb) {
-        const int b = b0 + tid;
-        const float* mu = p.mu + (int64_t)gh * m * m;
+        // u_b = sum_a e_a mu[a][b]; loads batched ahead of the sum
+        const float* mu = p.mu + (int64_t)gh * m * m + b0 + tid;
         float u = 0.f;
-        for (int a = 0; a < m; ++a) u += EA[a] * mu[(int64_t)a * m + b];
+        for (int a0 = 0; a0 < m; a0 += 16) {
+            float mv[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) mv[k] = a0 + k < m ? mu[(int64_t)(a0 + k) * m] : 0.f;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) if (a0 + k < m) u += EA[a0 + k] * mv[k];
+        }
         if (p.rect) u = fmaxf(u, 0.f);
         GB[tid] = u * exp2f(fmax + MB[tid] * TOK_LOG2E - cl);
     }
@@ -256,78 +276,111 @@ __global__ __launch_bounds__(TOK_THREADS) void k_tok_part(KParams p, float* part
             rec[1] = dd;
         }
     }
+    // Theta' = R Theta + x v_e (written back) and N = sum_b gain_b Theta'_b:
+    // two halves of the range, value columns across threads, every load of a
+    // thread issued before its stores
+    const int half = tid / (TOK_THREADS / 2), tt0 = tid % (TOK_THREADS / 2);
+    const int hb = (nb + 1) / 2;
+    const int jb0 = half * hb, jb1 = min(nb, jb0 + hb);
     float* th = p.theta + ((int64_t)gh * m + b0) * dv;
-    for (int t = tid; t < dv; t += TOK_THREADS) {
+    for (int t = tt0; t < dv; t += TOK_THREADS / 2) {
+        float v[TOK_BMAX / 2 + 1];
+#pragma unroll
+        for (int k = 0; k < TOK_BMAX / 2 + 1; ++k) v[k] = jb0 + k < jb1 ? th[(int64_t)(jb0 + k) * dv + t] : 0.f;
         float acc = 0.f;
-        for (int j = 0; j < nb; ++j) {
-            float v = th[(int64_t)j * dv + t];
-            if (r.full) {
-                v = v * RB[j] + XB[j] * VE[t];
-                th[(int64_t)j * dv + t] = v;
+#pragma unroll
+        for (int k = 0; k < TOK_BMAX / 2 + 1; ++k) {
+            const int j = jb0 + k;
+            if (j < jb1) {
+                float x = v[k];
+                if (r.full) {
+                    x = x * RB[j] + XB[j] * VE[t];
+                    th[(int64_t)j * dv + t] = x;
+                }
+                acc += GB[j] * x;
             }
-            acc += GB[j] * v;
         }
-        rec[2 + t] = acc;
+        NP[half * dv + t] = acc;
     }
+    __syncthreads();
+    for (int t = tid; t < dv; t += TOK_THREADS) rec[2 + t] = NP[t] + NP[dv + t];
 }
 
+// One block per query head: the head's partials to one exponent, the far
+// part dropped when its total mass is not >= 0, out.  The first head of a
+// group also pushes the row into the ring and advances meta (no other block
+// of this kernel reads them).
 __global__ __launch_bounds__(TOK_THREADS) void k_tok_merge(KParams p, const float* part, int nsplit)
 {
-    const int g = blockIdx.x;
+    extern __shared__ float lds[];
+    const int gh = blockIdx.x, g = gh / p.H, h = gh % p.H;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int H = p.H, dv = p.dv;
-    const GMeta c = load_gmeta(p.meta, g, p.W);
-    const TokRow r = tok_row(c);
-    const float* nearp = part + (int64_t)g * nsplit * H * tok_rec(dv);
-    const float* farp = part + (int64_t)p.G * nsplit * H * tok_rec(dv);
-    for (int h = wave; h < H; h += TOK_THREADS / 64) {
-        const int gh = g * H + h;
+    const int64_t rl = tok_rec(dv);
+    const float* nearp = part + (int64_t)g * nsplit * H * rl + (int64_t)h * rl;   // stride H*rl
+    const float* farp = part + (int64_t)p.G * nsplit * H * rl + (int64_t)gh * TOK_FB * rl;
+    float* WN = lds;              // [nsplit] near weights
+    float* WF = WN + nsplit;      // [TOK_FB] far weights
+    float* RED = WF + TOK_FB;     // [4]
+    if (wave == 0) {
         float cmax = -INFINITY;
-        for (int sp = lane; sp < nsplit; sp += 64)
-            cmax = fmaxf(cmax, nearp[((int64_t)sp * H + h) * tok_rec(dv)]);
-        if (r.nfar1 > 0)
-            for (int fb = lane; fb < TOK_FB; fb += 64)
-                cmax = fmaxf(cmax, farp[((int64_t)gh * TOK_FB + fb) * tok_rec(dv)]);
+        for (int sp = lane; sp < nsplit; sp += 64) cmax = fmaxf(cmax, nearp[(int64_t)sp * H * rl]);
+        const bool farok = farp[0] != -INFINITY;   // far records hold -inf when the far field is empty
+        if (farok && lane < TOK_FB) cmax = fmaxf(cmax, farp[(int64_t)lane * rl]);
         cmax = wmax(cmax);
         float den = 0.f;
         for (int sp = lane; sp < nsplit; sp += 64) {
-            const float* rc = nearp + ((int64_t)sp * H + h) * tok_rec(dv);
-            den += rc[1] * exp2f(rc[0] - cmax);
+            const float* rc = nearp + (int64_t)sp * H * rl;
+            const float w = exp2f(rc[0] - cmax);
+            WN[sp] = w;
+            den += rc[1] * w;
         }
         den = wsum(den);
         float dfar = 0.f;
-        if (r.nfar1 > 0) {
-            for (int fb = 0; fb < TOK_FB; ++fb) {
-                const float* rc = farp + ((int64_t)gh * TOK_FB + fb) * tok_rec(dv);
-                dfar += rc[1] * exp2f(rc[0] - cmax);
-            }
+        if (farok && lane < TOK_FB) {
+            const float w = exp2f(farp[(int64_t)lane * rl] - cmax);
+            WF[lane] = w;
+            dfar = farp[(int64_t)lane * rl + 1] * w;
         }
-        const bool have = r.nfar1 > 0 && dfar >= 0.f;
-        const float inv = 1.f / fmaxf(den + (have ? dfar : 0.f), 1e-30f);
-        float* orow = p.out + (int64_t)gh * dv;
-        for (int t = lane; t < dv; t += 64) {
-            float acc = 0.f;
-            for (int sp = 0; sp < nsplit; ++sp) {
-                const float* rc = nearp + ((int64_t)sp * H + h) * tok_rec(dv);
-                acc += rc[2 + t] * exp2f(rc[0] - cmax);
-            }
-            if (have)
-                for (int fb = 0; fb < TOK_FB; ++fb) {
-                    const float* rc = farp + ((int64_t)gh * TOK_FB + fb) * tok_rec(dv);
-                    acc += rc[2 + t] * exp2f(rc[0] - cmax);
-                }
-            orow[t] = acc * inv;
+        dfar = wsum(dfar);
+        const bool have = farok && dfar >= 0.f;
+        if (lane == 0) {
+            RED[0] = 1.f / fmaxf(den + (have ? dfar : 0.f), 1e-30f);
+            RED[1] = have ? 1.f : 0.f;
         }
     }
-    // commit: ring push and meta (every reader of this group is done)
-    float* kd = p.ring_k + ((int64_t)g * p.W + r.slot) * p.d;
-    float* vd = p.ring_v + ((int64_t)g * p.W + r.slot) * dv;
-    for (int t = tid; t < p.d; t += TOK_THREADS) kd[t] = p.k[(int64_t)g * p.d + t];
-    for (int t = tid; t < dv; t += TOK_THREADS) vd[t] = p.v[(int64_t)g * dv + t];
-    if (tid == 0) {
-        p.meta[4 * g + 0] = (uint32_t)r.len1;
-        p.meta[4 * g + 1] = (uint32_t)r.head1;
-        p.meta[4 * g + 2] = (uint32_t)r.nfar1;
+    __syncthreads();
+    const float inv = RED[0];
+    const bool have = RED[1] > 0.5f;
+    float* orow = p.out + (int64_t)gh * dv;
+    for (int t = tid; t < dv; t += TOK_THREADS) {
+        float acc = 0.f;
+        for (int sp0 = 0; sp0 < nsplit; sp0 += 8) {
+            float x[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) x[k] = sp0 + k < nsplit ? nearp[(int64_t)(sp0 + k) * H * rl + 2 + t] : 0.f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) if (sp0 + k < nsplit) acc += x[k] * WN[sp0 + k];
+        }
+        if (have)
+            for (int fb = 0; fb < TOK_FB; ++fb) acc += farp[(int64_t)fb * rl + 2 + t] * WF[fb];
+        orow[t] = acc * inv;
+    }
+    if (h == 0) {
+        // commit: ring push and meta (every reader of the ring and meta of
+        // this group ran in the previous kernel)
+        const GMeta c = load_gmeta(p.meta, g, p.W);
+        const TokRow r = tok_row(c);
+        __syncthreads();   // all threads have read meta before thread 0 writes it
+        float* kd = p.ring_k + ((int64_t)g * p.W + r.slot) * p.d;
+        float* vd = p.ring_v + ((int64_t)g * p.W + r.slot) * dv;
+        for (int t = tid; t < p.d; t += TOK_THREADS) kd[t] = p.k[(int64_t)g * p.d + t];
+        for (int t = tid; t < dv; t += TOK_THREADS) vd[t] = p.v[(int64_t)g * dv + t];
+        if (tid == 0) {
+            p.meta[4 * g + 0] = (uint32_t)r.len1;
+            p.meta[4 * g + 1] = (uint32_t)r.head1;
+            p.meta[4 * g + 2] = (uint32_t)r.nfar1;
+        }
     }
 }
 
@@ -336,7 +389,7 @@ hipError_t launch_token(const KParams& p, float* part, hipStream_t st)
     const int nsplit = tok_splits(p.ns, p.W);
     const size_t lds_near = sizeof(float) * ((size_t)TOK_KEYS * (p.d + 4) +
                                              (size_t)TOK_KEYS * (p.dv + 4) + (size_t)p.H * p.d);
-    const size_t lds_far = sizeof(float) * ((size_t)2 * p.d + p.dv + 7 * 64 + 4);
+    const size_t lds_far = sizeof(float) * ((size_t)2 * p.d + p.dv + 64 + 5 * 16 + 4 + 2 * p.dv);
     const size_t lds = lds_near > lds_far ? lds_near : lds_far;
     const int blocks = p.G * nsplit + p.nh * TOK_FB;
     static bool attr_set = false;
@@ -348,8 +401,9 @@ hipError_t launch_token(const KParams& p, float* part, hipStream_t st)
     hipLaunchKernelGGL(k_tok_part, dim3(blocks), dim3(TOK_THREADS), lds, st, p, part, nsplit);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_tok_merge, dim3(p.G), dim3(TOK_THREADS), 0, st, p, (const float*)part,
-                       nsplit);
+    const size_t lds_merge = sizeof(float) * ((size_t)nsplit + TOK_FB + 4);
+    hipLaunchKernelGGL(k_tok_merge, dim3(p.nh), dim3(TOK_THREADS), lds_merge, st, p,
+                       (const float*)part, nsplit);
     return hipGetLastError();
 }
 
