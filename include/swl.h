@@ -108,7 +108,9 @@ int swl_attend_chunk(const swl_geom* geom, const swl_state* st,
                      float* out, void* scratch, size_t scratch_bytes, void* stream);
 
 /* The state after the rows of the preceding swl_attend_chunk (same k, v,
- * rows and scratch, nothing else on the state in between): far commit
+ * rows and scratch, nothing else on the state or the scratch in between;
+ * the value the rows add to the far accumulator is already in the
+ * scratch): far commit
  * (Theta <- R Theta + sum_j E_j v_evicted(j), M, Z; o1b_far_commit), ring
  * commit (row j to slot (head0 + len0 + j) mod w_g; o1b_ring_commit) and
  * meta (len, head, nfar after `rows` pushes; o1b_meta). */
@@ -127,8 +129,8 @@ int swl_prefill(const swl_geom* geom, const swl_state* st,
 /* Stages of a call, in launch order, as reported to a swl_stage_fn. */
 enum swl_stage {
     SWL_STAGE_FAR_SCORE = 0,  /* evicted key x landmark scores */
-    SWL_STAGE_FAR_SCAN = 1,   /* post-sub-chunk max, rescale, exp mass and its prefix */
-    SWL_STAGE_DTHETA = 2,     /* value each sub-chunk adds to the far accumulator */
+    SWL_STAGE_FAR_SCAN = 1,   /* post-sub-chunk max, rescale and incoming mass */
+    SWL_STAGE_DTHETA = 2,     /* exp mass, its prefix and the value added to the accumulator */
     SWL_STAGE_THETA_SCAN = 3, /* the accumulator before each sub-chunk; commit of M, Z, Theta */
     SWL_STAGE_ATTEND = 4,     /* sinks + window attention and the far readout */
     SWL_STAGE_RING = 5,       /* ring commit */

@@ -40,7 +40,7 @@ static bool state_ok(const swl_geom* g, const swl_state* st)
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Carve {
-    size_t e, p, ms, rs, th, tok, total;
+    size_t e, p, ms, rs, tz, th, tok, total;
 };
 
 static Carve carve(const swl_geom* g, int S)
@@ -52,6 +52,7 @@ static Carve carve(const swl_geom* g, int S)
     c.p = off;  off += align256(sizeof(float) * (size_t)S * nhm * SUB);
     c.ms = off; off += align256(sizeof(float) * (size_t)S * nhm);
     c.rs = off; off += align256(sizeof(float) * (size_t)S * nhm);
+    c.tz = off; off += align256(sizeof(float) * (size_t)(S + 1) * nhm);
     c.th = off; off += align256(sizeof(float) * (size_t)S * nhm * g->dv);
     c.tok = off; off += align256(sizeof(float) * tok_part_floats(g->G, g->H, g->dv, g->ns, g->W));
     c.total = off;
@@ -87,6 +88,7 @@ static void set_scratch(KParams& p, const swl_geom* g, void* scratch, int S)
     p.P = reinterpret_cast<float*>(b + c.p);
     p.Ms = reinterpret_cast<float*>(b + c.ms);
     p.Rs = reinterpret_cast<float*>(b + c.rs);
+    p.TZ = reinterpret_cast<float*>(b + c.tz);
     p.TH = reinterpret_cast<float*>(b + c.th);
 }
 
@@ -95,19 +97,20 @@ static void set_scratch(KParams& p, const swl_geom* g, void* scratch, int S)
         if ((x) != hipSuccess) return SWL_EHIP; \
     } while (0)
 
-// far_e + attention (near part and far readout) of one call (state unchanged).
+// far_e (scores, scan, E/P and the accumulator increment) + attention (near
+// part and far readout) of one call; the state is unchanged.
 static int run_attend(const KParams& p, hipStream_t st)
 {
     SWL_TRY(launch_far_score(p, st));
     SWL_TRY(launch_far_scan(p, st));
+    SWL_TRY(launch_dtheta(p, st));
     SWL_TRY(launch_attend(p, st));
     return SWL_OK;
 }
 
-// far commit + ring commit + meta of one call or pass.
+// far commit + ring commit + meta of one call (after run_attend on its rows).
 static int run_commit(const KParams& p, hipStream_t st)
 {
-    SWL_TRY(launch_dtheta(p, st));
     SWL_TRY(launch_theta_scan(p, true, st));
     SWL_TRY(launch_ring_commit(p, st));
     SWL_TRY(launch_meta(p, st));

@@ -1,169 +1,275 @@
-// Far-field kernels: eviction scores, the running max / mass scan, and the
+// Far-field kernels: eviction scores, the running max / mass scan and the
 // value accumulator.  cortiq-engine 0.8.51 src/gpu_wgpu/o1_batch.rs,
 // o1b_far_e and o1b_far_commit, generalised from one sub-chunk to the S
 // sub-chunks of a call: the score and value products of every sub-chunk run
-// in parallel, and only the cheap per-landmark recurrences (M, Z, Theta) walk
-// the sub-chunks in order.
+// in parallel on fp32 MFMA, and only the per-landmark recurrences (M and Z
+// as scalars, Theta elementwise) walk the sub-chunks in order.
+//
+// Per sub-chunk s and landmark row (gh, b), with l_j the score of the key
+// evicted by chunk row j (rows j0 <= j < k_s evict):
+//   M'_s = max(M_{s-1}, max_j l_j);  R_s = 1 if M'_s == M_{s-1} else
+//   exp(M_{s-1} - M'_s) (an empty field at -inf keeps R = 1 until its first
+//   eviction, which then rescales the zero mass by exp(-inf) = 0);
+//   E_sj = exp(l_j - M'_s);  P_sj = R_s Z_{s-1} + sum_{j'<=j} E_sj';
+//   Z_s = P_s,63;  Theta_s = R_s Theta_{s-1} + sum_j E_sj v_evicted(j).
 #include "swl_internal.h"
 
 namespace swl {
 
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ floatx16 fmfma(float a, float b, floatx16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int fkap(int v, int hf) { return (v >> 2) * 8 + hf * 4 + (v & 3); }
+
 // ---------------------------------------------------------------------------
-// far_score: L[s][gh*m+b][j] = scale * <q~_{gh,b}, key evicted by row j of
-// sub-chunk s>, for the evicting rows j0 <= j < k_s; the other lanes hold
-// -inf.  One block per (sub-chunk, group); the group's evicted keys of the
-// sub-chunk are staged in LDS and every landmark row of the group reads them.
+// far_score: L[s][gh*m+b][j] = scale <q~_{gh,b}, key evicted by row j>, -inf
+// for rows that do not evict, and per landmark row the local max mx and mass
+// zl = sum_j exp(l_j - mx) of the sub-chunk.  One block per (sub-chunk,
+// group); the evicted keys are staged in LDS.  MFMA C[hb][j] = Q~ K_e^T with
+// the d index of step st split over the two lane halves (hf*D/2 + st), so
+// both operands are row-contiguous per lane.
 // ---------------------------------------------------------------------------
 constexpr int FS_THREADS = 256;
-constexpr int FS_J = 16;  // evicted rows per register tile
 
+template <int D>
 __global__ __launch_bounds__(FS_THREADS) void k_far_score(KParams p)
 {
-    extern __shared__ float lds[];
-    const int s = blockIdx.x, g = blockIdx.y;
+    constexpr int LD = D + 4;
+    __shared__ float ek[SUB][LD];
+    const int w = xcd_work_item(blockIdx.x, p.S * p.G);
+    const int s = w % p.S, g = w / p.S;
     const int r0 = s * SUB;
     const int ks = min(SUB, p.T - r0);
     const GMeta c = load_gmeta(p.meta, g, p.W);
     const SubMeta sm = sub_meta(c, r0);
     const int jlo = max(sm.j0, 0);
-    const int d = p.d;
     const int hm = p.H * p.m;
-    const int nhm = p.nh * p.m;
-    float* ek = lds;  // [SUB][d]
-    for (int e = threadIdx.x; e < SUB * d; e += FS_THREADS) {
-        int j = e / d, t = e % d;
-        float x = 0.f;
-        if (j >= jlo && j < ks) x = key_row(p, c, g, c.len0 + r0 + j - c.wg)[t];
-        ek[e] = x;
+    const int64_t nhm = (int64_t)p.nh * p.m;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, ln = lane & 31;
+    for (int e = tid; e < SUB * (D / 4); e += FS_THREADS) {
+        const int j = e / (D / 4), c4 = (e % (D / 4)) * 4;
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (j >= jlo && j < ks)
+            x = *reinterpret_cast<const float4*>(key_row(p, c, g, c.len0 + r0 + j - c.wg) + c4);
+        *reinterpret_cast<float4*>(&ek[j][c4]) = x;
     }
     __syncthreads();
     float* L = p.E + ((int64_t)s * nhm + (int64_t)g * hm) * SUB;
-    // work item: (landmark row hb, tile of FS_J evicted rows)
-    const int ntile = SUB / FS_J;
-    for (int w = threadIdx.x; w < hm * ntile; w += FS_THREADS) {
-        const int hb = w / ntile, jt = (w % ntile) * FS_J;
-        const float* qt = p.q_tilde + ((int64_t)g * hm + hb) * d;
-        float acc[FS_J];
+    float* MX = p.Ms + (int64_t)s * nhm + (int64_t)g * hm;   // local max (the scan overwrites)
+    float* ZL = p.Rs + (int64_t)s * nhm + (int64_t)g * hm;   // local mass (the scan overwrites)
+    const int nht = (hm + 31) / 32;
+    for (int ht = wave; ht < nht; ht += FS_THREADS / 64) {
+        const int hb_a = ht * 32 + ln;   // A row of this lane
+        float qa[D / 2];
+        {
+            const float* qr = p.q_tilde + ((int64_t)g * hm + min(hb_a, hm - 1)) * D + hf * (D / 2);
 #pragma unroll
-        for (int u = 0; u < FS_J; ++u) acc[u] = 0.f;
-        for (int t = 0; t < d; t += 4) {
-            float4 qv = *reinterpret_cast<const float4*>(qt + t);
-#pragma unroll
-            for (int u = 0; u < FS_J; ++u) {
-                float4 kv = *reinterpret_cast<const float4*>(ek + (jt + u) * d + t);
-                acc[u] += qv.x * kv.x + qv.y * kv.y + qv.z * kv.z + qv.w * kv.w;
+            for (int st = 0; st < D / 2; st += 4) {
+                const float4 x = *reinterpret_cast<const float4*>(qr + st);
+                qa[st] = x.x; qa[st + 1] = x.y; qa[st + 2] = x.z; qa[st + 3] = x.w;
             }
         }
+        floatx16 acc[2];
 #pragma unroll
-        for (int u = 0; u < FS_J; ++u) {
-            int j = jt + u;
-            L[(int64_t)hb * SUB + j] = (j >= jlo && j < ks) ? acc[u] * p.scale : -INFINITY;
+        for (int jt = 0; jt < 2; ++jt) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[jt][v] = 0.f;
+            const float* kr = &ek[jt * 32 + ln][hf * (D / 2)];
+#pragma unroll
+            for (int st = 0; st < D / 2; st += 4) {
+                const float4 b = *reinterpret_cast<const float4*>(kr + st);
+                acc[jt] = fmfma(qa[st], b.x, acc[jt]);
+                acc[jt] = fmfma(qa[st + 1], b.y, acc[jt]);
+                acc[jt] = fmfma(qa[st + 2], b.z, acc[jt]);
+                acc[jt] = fmfma(qa[st + 3], b.w, acc[jt]);
+            }
+        }
+        // lane holds rows hb = ht*32 + kappa(v, hf), columns j = jt*32 + ln
+        float mx[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            float m2 = -INFINITY;
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt) {
+                const int j = jt * 32 + ln;
+                const float l = (j >= jlo && j < ks) ? acc[jt][v] * p.scale : -INFINITY;
+                acc[jt][v] = l;
+                m2 = fmaxf(m2, l);
+            }
+#pragma unroll
+            for (int o = 16; o >= 1; o >>= 1) m2 = fmaxf(m2, __shfl_xor(m2, o, 64));
+            mx[v] = m2;
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int hb = ht * 32 + fkap(v, hf);
+            float z = 0.f;
+            if (mx[v] != -INFINITY) {
+#pragma unroll
+                for (int jt = 0; jt < 2; ++jt) z += expf(acc[jt][v] - mx[v]);
+            }
+#pragma unroll
+            for (int o = 16; o >= 1; o >>= 1) z += __shfl_xor(z, o, 64);
+            if (hb < hm) {
+#pragma unroll
+                for (int jt = 0; jt < 2; ++jt) L[(int64_t)hb * SUB + jt * 32 + ln] = acc[jt][v];
+                if (ln == 0) {
+                    MX[hb] = mx[v];
+                    ZL[hb] = z;
+                }
+            }
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// far_scan: one wave per (gh, b), lane j = chunk row j (as o1b_far_e), walking
-// the sub-chunks in order.  Per sub-chunk: M' = max(M, max_j l_j); R = 1 if
-// M' == M else exp(M - M') (an empty field at -inf gets R = 1 until its first
-// eviction, which then rescales the zero mass by exp(-inf) = 0);
-// E_j = exp(l_j - M') for evicting rows, else 0; P_j = R*Z + inclusive
-// prefix of E (a wave scan in place of the pages' serial lane-0 loop);
-// Z <- P_63; M <- M'.
+// mz_scan: one thread per landmark row (gh, b), walking the sub-chunks in
+// order on scalars: M'_s, R_s and the incoming mass Z_{s-1} (into TZ[s]),
+// with Z_s = R_s Z_{s-1} + zl_s exp(mx_s - M'_s) (the same sum as
+// P_{s,63}, up to rounding), and the final mass into TZ[S].  Reads the local
+// (mx, zl) that far_score left in Ms/Rs and replaces them with M'_s and R_s.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float wave_max(float x)
-{
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-    return x;
-}
+constexpr int SCAN_AHEAD = 8;
 
-__device__ __forceinline__ float wave_incl_scan(float x, int lane)
+__global__ __launch_bounds__(256) void k_mz_scan(KParams p)
 {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        float y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
-    return x;
-}
-
-__global__ __launch_bounds__(256) void k_far_scan(KParams p)
-{
-    const int lane = threadIdx.x & 63;
-    const int ghb = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int nhm = p.nh * p.m;
+    const int64_t nhm = (int64_t)p.nh * p.m;
+    const int64_t ghb = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (ghb >= nhm) return;
-    const int gh = ghb / p.m, b = ghb % p.m, g = gh / p.H;
-    const GMeta c = load_gmeta(p.meta, g, p.W);
-    float M = p.mz[(int64_t)gh * 2 * p.m + b];
-    float Z = p.mz[(int64_t)gh * 2 * p.m + p.m + b];
-    float lnext = p.E[(int64_t)ghb * SUB + lane];
-    for (int s = 0; s < p.S; ++s) {
-        const float l = lnext;
-        if (s + 1 < p.S) lnext = p.E[((int64_t)(s + 1) * nhm + ghb) * SUB + lane];
-        const int r0 = s * SUB;
-        const int ks = min(SUB, p.T - r0);
-        const SubMeta sm = sub_meta(c, r0);
-        const bool ev = lane >= sm.j0 && lane < ks;
-        const float mx = wave_max(ev ? l : -INFINITY);
-        const float Mn = fmaxf(M, mx);
-        const float R = (Mn == M) ? 1.0f : expf(M - Mn);
-        const float e = ev ? expf(l - Mn) : 0.0f;
-        const float pf = R * Z + wave_incl_scan(e, lane);
-        const int64_t at = ((int64_t)s * nhm + ghb) * SUB + lane;
-        p.E[at] = e;
-        p.P[at] = pf;
-        if (lane == 0) {
-            p.Ms[(int64_t)s * nhm + ghb] = Mn;
-            p.Rs[(int64_t)s * nhm + ghb] = R;
+    const int64_t gh = ghb / p.m, b = ghb % p.m;
+    float M = p.mz[gh * 2 * p.m + b];
+    float Z = p.mz[gh * 2 * p.m + p.m + b];
+    for (int s0 = 0; s0 < p.S; s0 += SCAN_AHEAD) {
+        float mx[SCAN_AHEAD], zl[SCAN_AHEAD];
+#pragma unroll
+        for (int k = 0; k < SCAN_AHEAD; ++k) {
+            const int s = min(s0 + k, p.S - 1);
+            mx[k] = p.Ms[(int64_t)s * nhm + ghb];
+            zl[k] = p.Rs[(int64_t)s * nhm + ghb];
         }
-        Z = __shfl(pf, 63, 64);
-        M = Mn;
+#pragma unroll
+        for (int k = 0; k < SCAN_AHEAD; ++k) {
+            const int s = s0 + k;
+            if (s < p.S) {
+                const float Mn = fmaxf(M, mx[k]);
+                const float R = (Mn == M) ? 1.0f : expf(M - Mn);
+                const int64_t at = (int64_t)s * nhm + ghb;
+                p.Ms[at] = Mn;
+                p.Rs[at] = R;
+                p.TZ[at] = Z;
+                Z = R * Z + (mx[k] == -INFINITY ? 0.f : zl[k] * expf(mx[k] - Mn));
+                M = Mn;
+            }
+        }
     }
+    // the mass after the last sub-chunk, which a commit stores: a call that
+    // resumes from the committed state then carries exactly this value
+    p.TZ[(int64_t)p.S * nhm + ghb] = Z;
 }
 
 // ---------------------------------------------------------------------------
-// dtheta: TH[s][gh*m+b][t] = sum_j E[s][gh*m+b][j] * v_evicted(s, j)[t], the
-// value the sub-chunk adds to each landmark's accumulator (o1b_far_commit's
-// sum over the evicted rows).  One block per (sub-chunk, query head).
+// dtheta: per (sub-chunk, group): E = exp(l - M'_s) and P = R_s Z_{s-1} +
+// prefix_j E for every landmark row (written for the attention epilogue and
+// the commit), and TH[s][gh*m+b][t] = sum_j E_bj v_evicted(j)[t] on MFMA
+// (C[b][t], step st pairs rows hf*32 + st of E and of the evicted values,
+// so each lane's E row is 32 contiguous values whose prefix is a register
+// loop).  The evicted values are staged in LDS.
 // ---------------------------------------------------------------------------
+template <int DV>
 __global__ __launch_bounds__(256) void k_dtheta(KParams p)
 {
-    extern __shared__ float lds[];
-    const int s = blockIdx.x, gh = blockIdx.y, g = gh / p.H;
+    constexpr int NT = DV >= 32 ? DV / 32 : 1;   // 32-column output tiles
+    constexpr int LD = DV + 4;
+    __shared__ float ve[SUB][LD];
+    const int w = xcd_work_item(blockIdx.x, p.S * p.G);
+    const int s = w % p.S, g = w / p.S;
     const int r0 = s * SUB;
     const int ks = min(SUB, p.T - r0);
     const GMeta c = load_gmeta(p.meta, g, p.W);
     const SubMeta sm = sub_meta(c, r0);
     const int jlo = max(sm.j0, 0);
-    const int dv = p.dv, m = p.m;
-    const int nhm = p.nh * m;
-    float* vev = lds;               // [SUB][dv]
-    float* eb = lds + SUB * dv;     // [m][SUB]
-    for (int e = threadIdx.x; e < SUB * dv; e += 256) {
-        int j = e / dv, t = e % dv;
-        float x = 0.f;
-        if (j >= jlo && j < ks) x = val_row(p, c, g, c.len0 + r0 + j - c.wg)[t];
-        vev[e] = x;
+    const int hm = p.H * p.m;
+    const int64_t nhm = (int64_t)p.nh * p.m;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, ln = lane & 31;
+    for (int e = tid; e < SUB * (DV / 4); e += 256) {
+        const int j = e / (DV / 4), c4 = (e % (DV / 4)) * 4;
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (j >= jlo && j < ks)
+            x = *reinterpret_cast<const float4*>(val_row(p, c, g, c.len0 + r0 + j - c.wg) + c4);
+        *reinterpret_cast<float4*>(&ve[j][c4]) = x;
     }
-    const float* E = p.E + ((int64_t)s * nhm + (int64_t)gh * m) * SUB;
-    for (int e = threadIdx.x; e < m * SUB; e += 256) eb[e] = E[e];
     __syncthreads();
-    float* out = p.TH + ((int64_t)s * nhm + (int64_t)gh * m) * dv;
-    const int nq = dv / 4;
-    for (int w = threadIdx.x; w < m * nq; w += 256) {
-        const int b = w / nq, t = (w % nq) * 4;
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int j = jlo; j < ks; ++j) {
-            const float ej = eb[b * SUB + j];
-            const float4 vv = *reinterpret_cast<const float4*>(vev + j * dv + t);
-            acc.x += ej * vv.x;
-            acc.y += ej * vv.y;
-            acc.z += ej * vv.z;
-            acc.w += ej * vv.w;
+    const int64_t row0 = (int64_t)s * nhm + (int64_t)g * hm;   // landmark row (s, g*H*m)
+    const int nht = (hm + 31) / 32;
+    for (int ht = wave; ht < nht; ht += 4) {
+        const int hb = ht * 32 + ln;              // this lane's E row
+        const bool rv = hb < hm;
+        float e[32];
+        {
+            float* Lr = p.E + (row0 + min(hb, hm - 1)) * SUB + hf * 32;
+            float* Pr = p.P + (row0 + min(hb, hm - 1)) * SUB + hf * 32;
+            const float Mn = p.Ms[row0 + min(hb, hm - 1)];
+            const float base = p.Rs[row0 + min(hb, hm - 1)] * p.TZ[row0 + min(hb, hm - 1)];
+#pragma unroll
+            for (int k = 0; k < 32; k += 4) {
+                const float4 x = *reinterpret_cast<const float4*>(Lr + k);
+                e[k] = x.x; e[k + 1] = x.y; e[k + 2] = x.z; e[k + 3] = x.w;
+            }
+            float run = 0.f;
+#pragma unroll
+            for (int k = 0; k < 32; ++k) {
+                e[k] = (rv && e[k] != -INFINITY) ? expf(e[k] - Mn) : 0.f;
+                run += e[k];
+            }
+            // the second half's prefix starts after the first half's total
+            const float first = __shfl(run, ln, 64);
+            float pre = base + (hf ? first : 0.f);
+            if (rv) {
+#pragma unroll
+                for (int k = 0; k < 32; k += 4) {
+                    float4 pe, pp;
+                    pe.x = e[k]; pe.y = e[k + 1]; pe.z = e[k + 2]; pe.w = e[k + 3];
+                    pre += e[k]; pp.x = pre;
+                    pre += e[k + 1]; pp.y = pre;
+                    pre += e[k + 2]; pp.z = pre;
+                    pre += e[k + 3]; pp.w = pre;
+                    *reinterpret_cast<float4*>(Lr + k) = pe;
+                    *reinterpret_cast<float4*>(Pr + k) = pp;
+                }
+            }
         }
-        *reinterpret_cast<float4*>(out + (int64_t)b * dv + t) = acc;
+        floatx16 acc[NT];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[tt][v] = 0.f;
+#pragma unroll
+        for (int st = 0; st < 32; ++st) {
+            const float* vr = &ve[hf * 32 + st][0];
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                const int t = tt * 32 + ln;
+                const float b = t < DV ? vr[t] : 0.f;
+                acc[tt] = fmfma(e[st], b, acc[tt]);
+            }
+        }
+        // lane holds rows hb = ht*32 + kappa(v, hf), columns t = tt*32 + ln
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int hbo = ht * 32 + fkap(v, hf);
+            if (hbo < hm) {
+                float* out = p.TH + (row0 + hbo) * DV;
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt) {
+                    const int t = tt * 32 + ln;
+                    if (t < DV) out[t] = acc[tt][v];
+                }
+            }
+        }
     }
 }
 
@@ -171,7 +277,7 @@ __global__ __launch_bounds__(256) void k_dtheta(KParams p)
 // theta_scan: one thread per (gh, b, t), walking the sub-chunks in order:
 // TH[s] <- Theta (the value before sub-chunk s, which the readout of s uses),
 // Theta <- R_s Theta + dTheta_s.  With `commit` the final Theta, M and Z go
-// to the state (o1b_far_commit: M <- M', Z <- P_{k-1}).
+// to the state (o1b_far_commit: M <- M', Z <- the mass after the rows).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_theta_scan(KParams p, int commit)
 {
@@ -179,13 +285,24 @@ __global__ __launch_bounds__(256) void k_theta_scan(KParams p, int commit)
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= nhm * p.dv) return;
     const int64_t ghb = idx / p.dv;
+    const int64_t stride = nhm * p.dv;
     float th = p.theta[idx];
-    float dnext = p.TH[idx];
-    for (int s = 0; s < p.S; ++s) {
-        const float dth = dnext;
-        if (s + 1 < p.S) dnext = p.TH[(int64_t)(s + 1) * nhm * p.dv + idx];
-        p.TH[(int64_t)s * nhm * p.dv + idx] = th;
-        th = p.Rs[(int64_t)s * nhm + ghb] * th + dth;
+    for (int s0 = 0; s0 < p.S; s0 += SCAN_AHEAD) {
+        float dth[SCAN_AHEAD], rs[SCAN_AHEAD];
+#pragma unroll
+        for (int k = 0; k < SCAN_AHEAD; ++k) {
+            const int s = min(s0 + k, p.S - 1);
+            dth[k] = p.TH[(int64_t)s * stride + idx];
+            rs[k] = p.Rs[(int64_t)s * nhm + ghb];
+        }
+#pragma unroll
+        for (int k = 0; k < SCAN_AHEAD; ++k) {
+            const int s = s0 + k;
+            if (s < p.S) {
+                p.TH[(int64_t)s * stride + idx] = th;
+                th = rs[k] * th + dth[k];
+            }
+        }
     }
     if (commit) {
         p.theta[idx] = th;
@@ -193,30 +310,54 @@ __global__ __launch_bounds__(256) void k_theta_scan(KParams p, int commit)
             const int64_t gh = ghb / p.m, b = ghb % p.m;
             const int64_t last = (int64_t)(p.S - 1) * nhm + ghb;
             p.mz[gh * 2 * p.m + b] = p.Ms[last];
-            p.mz[gh * 2 * p.m + p.m + b] = p.P[last * SUB + (SUB - 1)];
+            p.mz[gh * 2 * p.m + p.m + b] = p.TZ[(int64_t)p.S * nhm + ghb];
         }
     }
 }
 
 // ---------------------------------------------------------------------------
+template <int D>
+static void launch_fs(const KParams& p, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_far_score<D>, dim3(p.S * p.G), dim3(FS_THREADS), 0, st, p);
+}
+
 hipError_t launch_far_score(const KParams& p, hipStream_t st)
 {
-    size_t lds = sizeof(float) * SUB * p.d;
-    hipLaunchKernelGGL(k_far_score, dim3(p.S, p.G), dim3(FS_THREADS), lds, st, p);
+    switch (p.d) {
+    case 8: launch_fs<8>(p, st); break;
+    case 16: launch_fs<16>(p, st); break;
+    case 32: launch_fs<32>(p, st); break;
+    case 64: launch_fs<64>(p, st); break;
+    case 128: launch_fs<128>(p, st); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_far_scan(const KParams& p, hipStream_t st)
 {
-    int nhm = p.nh * p.m;
-    hipLaunchKernelGGL(k_far_scan, dim3((nhm + 3) / 4), dim3(256), 0, st, p);
+    const int64_t nhm = (int64_t)p.nh * p.m;
+    hipLaunchKernelGGL(k_mz_scan, dim3((unsigned)((nhm + 255) / 256)), dim3(256), 0, st, p);
     return hipGetLastError();
+}
+
+template <int DV>
+static void launch_dt(const KParams& p, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_dtheta<DV>, dim3(p.S * p.G), dim3(256), 0, st, p);
 }
 
 hipError_t launch_dtheta(const KParams& p, hipStream_t st)
 {
-    size_t lds = sizeof(float) * (SUB * p.dv + p.m * SUB);
-    hipLaunchKernelGGL(k_dtheta, dim3(p.S, p.nh), dim3(256), lds, st, p);
+    switch (p.dv) {
+    case 8: launch_dt<8>(p, st); break;
+    case 16: launch_dt<16>(p, st); break;
+    case 32: launch_dt<32>(p, st); break;
+    case 64: launch_dt<64>(p, st); break;
+    case 128: launch_dt<128>(p, st); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

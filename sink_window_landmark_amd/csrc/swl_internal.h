@@ -38,8 +38,9 @@ struct KParams {
     // scratch planes (see scratch_layout)
     float* E;    // [S][nh*m][SUB]  scores, then exp mass against the post-sub-chunk max
     float* P;    // [S][nh*m][SUB]  far mass prefix R*Z + sum_{j'<=j} E
-    float* Ms;   // [S][nh*m]       post-sub-chunk max
-    float* Rs;   // [S][nh*m]       rescale of the old mass
+    float* Ms;   // [S][nh*m]       local max of the scores, then the post-sub-chunk max
+    float* Rs;   // [S][nh*m]       local mass of the scores, then the rescale of the old mass
+    float* TZ;   // [S+1][nh*m]     mass before each sub-chunk, then after the last
     float* TH;   // [S][nh*m][dv]   Theta increments, then Theta before each sub-chunk
     const float* theta_prev;  // Theta before sub-chunk s at theta_prev + s*theta_prev_stride
     int64_t theta_prev_stride;
