@@ -213,6 +213,9 @@ __global__ __launch_bounds__(AT_THREADS) void k_attend(KParams p)
         floatx16 sacc;
         zero16(sacc);
         const float* kr = &Ks[buf * KT + ln][hf * (D / 2)];
+        // a wave in an MFMA stretch gets issue priority over its SIMD partner
+        // in its softmax stretch, so the two overlap
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int st = 0; st < D / 2; st += 4) {
             const float4 a = *reinterpret_cast<const float4*>(kr + st);
@@ -221,6 +224,7 @@ __global__ __launch_bounds__(AT_THREADS) void k_attend(KParams p)
             sacc = mfma32(a.z, qf[st + 2], sacc);
             sacc = mfma32(a.w, qf[st + 3], sacc);
         }
+        __builtin_amdgcn_s_setprio(0);
         // sinks are always visible; the window key at position tb + kappa is
         // visible to row i when lo_q <= pos <= hi_q (every row of the wave
         // sees every key of a "full" tile)
@@ -265,8 +269,10 @@ __global__ __launch_bounds__(AT_THREADS) void k_attend(KParams p)
             ts += pv;
         }
         lsum += ts;
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int t = 0; t < 16; ++t) pv_step<D, NB>(O, &Vs[buf * KT + kap(t, hf)][0], ln, sacc[t]);
+        __builtin_amdgcn_s_setprio(0);
     }
     float den = lsum + __shfl_xor(lsum, 32, 64);   // near mass relative to mrun
 
