@@ -40,7 +40,7 @@ static bool state_ok(const swl_geom* g, const swl_state* st)
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Carve {
-    size_t e, p, ms, rs, tz, th, tok, total;
+    size_t tok, e, p, ms, rs, tz, th, total;
 };
 
 static Carve carve(const swl_geom* g, int S)
@@ -48,13 +48,14 @@ static Carve carve(const swl_geom* g, int S)
     const size_t nhm = (size_t)g->G * g->H * g->m;
     Carve c;
     size_t off = 0;
+    // the decode plane comes first, at an offset that does not depend on S
+    c.tok = off; off += align256(sizeof(float) * tok_part_floats(g->G, g->H, g->dv, g->ns, g->W));
     c.e = off;  off += align256(sizeof(float) * (size_t)S * nhm * SUB);
     c.p = off;  off += align256(sizeof(float) * (size_t)S * nhm * SUB);
     c.ms = off; off += align256(sizeof(float) * (size_t)S * nhm);
     c.rs = off; off += align256(sizeof(float) * (size_t)S * nhm);
     c.tz = off; off += align256(sizeof(float) * (size_t)(S + 1) * nhm);
     c.th = off; off += align256(sizeof(float) * (size_t)S * nhm * g->dv);
-    c.tok = off; off += align256(sizeof(float) * tok_part_floats(g->G, g->H, g->dv, g->ns, g->W));
     c.total = off;
     return c;
 }

@@ -72,6 +72,15 @@ __device__ __forceinline__ float wmax(float x)
     return x;
 }
 
+// Sum of x over groups of n consecutive lanes (n a power of two <= 64).
+__device__ __forceinline__ float group_sum(float x, int n)
+{
+    for (int o = n >> 1; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+// Every block first issues all of its global loads into LDS (one round
+// trip), then computes from LDS.
 __global__ __launch_bounds__(TOK_THREADS) void k_tok_part(KParams p, float* part, int nsplit)
 {
     extern __shared__ float lds[];
@@ -96,10 +105,13 @@ __global__ __launch_bounds__(TOK_THREADS) void k_tok_part(KParams p, float* part
             }
             return;
         }
+        const int nk = k1 - k0;
         const int LDK = d + 4, LDV = dv + 4;
         float* Kl = lds;                      // [64][d+4]
         float* Vl = Kl + TOK_KEYS * LDK;      // [64][dv+4]
         float* Ql = Vl + TOK_KEYS * LDV;      // [H][d]
+        float* Pl = Ql + H * d;               // [H][64] scores, then weights
+        float* ST = Pl + H * TOK_KEYS;        // [H][2] max, mass
         for (int e = tid; e < TOK_KEYS * (d / 4); e += TOK_THREADS) {
             const int row = e / (d / 4), c4 = (e % (d / 4)) * 4;
             const int x = k0 + row;
@@ -126,38 +138,49 @@ __global__ __launch_bounds__(TOK_THREADS) void k_tok_part(KParams p, float* part
         const float qs = p.scale * TOK_LOG2E;
         for (int e = tid; e < H * d; e += TOK_THREADS) Ql[e] = p.q[(int64_t)g * H * d + e] * qs;
         __syncthreads();
-        const int nk = k1 - k0;
-        for (int h = wave; h < H; h += TOK_THREADS / 64) {
-            // lane = key
-            float sc = -INFINITY;
-            if (lane < nk) {
-                const float* kr = Kl + lane * LDK;
+        // scores: thread per (head, key)
+        for (int e = tid; e < H * TOK_KEYS; e += TOK_THREADS) {
+            const int h = e / TOK_KEYS, j = e % TOK_KEYS;
+            float acc = -INFINITY;
+            if (j < nk) {
+                const float* kr = Kl + j * LDK;
                 const float* qr = Ql + h * d;
-                float acc = 0.f;
+                acc = 0.f;
+#pragma unroll 8
                 for (int t = 0; t < d; t += 4) {
                     const float4 a = *reinterpret_cast<const float4*>(kr + t);
                     const float4 b = *reinterpret_cast<const float4*>(qr + t);
                     acc += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
                 }
-                sc = acc;
             }
+            Pl[e] = acc;
+        }
+        __syncthreads();
+        // per head: max, weights, mass (a wave per head, lane = key)
+        for (int h = wave; h < H; h += TOK_THREADS / 64) {
+            const float sc = Pl[h * TOK_KEYS + lane];
             const float mx = wmax(sc);
             const float pv = lane < nk ? exp2f(sc - mx) : 0.f;
             const float l = wsum(pv);
-            float* rec = base + ((int64_t)sp * H + h) * tok_rec(dv);
-            // value sum: lanes over value columns, p_j broadcast by shuffle
-            for (int t0 = 0; t0 < dv; t0 += 64) {
-                const int t = t0 + lane;
-                float acc = 0.f;
-                for (int j = 0; j < nk; ++j) {
-                    const float pj = __shfl(pv, j, 64);
-                    if (t < dv) acc += pj * Vl[j * LDV + t];
-                }
-                if (t < dv) rec[2 + t] = acc;
-            }
+            Pl[h * TOK_KEYS + lane] = pv;
             if (lane == 0) {
-                rec[0] = mx;
-                rec[1] = l;
+                ST[2 * h] = mx;
+                ST[2 * h + 1] = l;
+            }
+        }
+        __syncthreads();
+        // value sums: thread per (head, value column)
+        for (int e = tid; e < H * dv; e += TOK_THREADS) {
+            const int h = e / dv, t = e % dv;
+            const float* pr = Pl + h * TOK_KEYS;
+            float acc = 0.f;
+#pragma unroll 8
+            for (int j = 0; j < nk; ++j) acc += pr[j] * Vl[j * LDV + t];
+            float* rec = base + ((int64_t)sp * H + h) * tok_rec(dv);
+            rec[2 + t] = acc;
+            if (t == 0) {
+                rec[0] = ST[2 * h];
+                rec[1] = ST[2 * h + 1];
             }
         }
         return;
@@ -176,70 +199,91 @@ __global__ __launch_bounds__(TOK_THREADS) void k_tok_part(KParams p, float* part
         for (int t = tid; t < tok_rec(dv); t += TOK_THREADS) rec[t] = t == 0 ? -INFINITY : 0.f;
         return;
     }
-    float* Ql = lds;         // [d]
-    float* KE = Ql + d;      // [d]   evicted key
-    float* VE = KE + d;      // [dv]  evicted value
-    float* EA = VE + dv;     // [64]  f_a, then e_a
-    float* MB = EA + 64;     // [16]  M'
-    float* RB = MB + 16;     // [16]  R
-    float* XB = RB + 16;     // [16]  exp(l - M')
-    float* ZB = XB + 16;     // [16]  Z'
-    float* GB = ZB + 16;     // [16]  gains
-    float* RED = GB + 16;    // [4]
-    float* NP = RED + 4;     // [2][dv] partial numerators of the two b halves
+    const int LDT = d + 4;
+    float* Ql = lds;                  // [d]
+    float* KE = Ql + d;               // [d]       evicted key
+    float* VE = KE + d;               // [dv]      evicted value
+    float* KT = VE + dv;              // [m][d+4]  landmark keys
+    float* QT = KT + m * LDT;         // [16][d+4] this range's landmark queries
+    float* TH = QT + TOK_BMAX * LDT;  // [16][dv]  this range's accumulators
+    float* MU = TH + TOK_BMAX * dv;   // [m][16]   mu[a][b0 + j]
+    float* EA = MU + m * TOK_BMAX;    // [64]      f_a, then e_a
+    float* MB = EA + 64;              // [16]      M'
+    float* RB = MB + 16;              // [16]      R
+    float* XB = RB + 16;              // [16]      exp(l - M')
+    float* ZB = XB + 16;              // [16]      Z'
+    float* GB = ZB + 16;              // [16]      gains
+    float* RED = GB + 16;             // [4]
+    float* mz = p.mz + (int64_t)gh * 2 * m;
+    const float* ring_k_e = p.ring_k + ((int64_t)g * p.W + c.head0) * d;
+    const float* ring_v_e = p.ring_v + ((int64_t)g * p.W + c.head0) * dv;
     for (int t = tid; t < d; t += TOK_THREADS) {
         Ql[t] = p.q[(int64_t)gh * d + t];
-        KE[t] = r.full ? p.ring_k[((int64_t)g * p.W + c.head0) * d + t] : 0.f;
+        KE[t] = r.full ? ring_k_e[t] : 0.f;
     }
-    for (int t = tid; t < dv; t += TOK_THREADS)
-        VE[t] = r.full ? p.ring_v[((int64_t)g * p.W + c.head0) * dv + t] : 0.f;
+    for (int t = tid; t < dv; t += TOK_THREADS) VE[t] = r.full ? ring_v_e[t] : 0.f;
+    for (int e = tid; e < m * (d / 4); e += TOK_THREADS) {
+        const int a = e / (d / 4), c4 = (e % (d / 4)) * 4;
+        *reinterpret_cast<float4*>(KT + a * LDT + c4) =
+            *reinterpret_cast<const float4*>(p.k_tilde + ((int64_t)g * m + a) * d + c4);
+    }
+    for (int e = tid; e < nb * (d / 4); e += TOK_THREADS) {
+        const int j = e / (d / 4), c4 = (e % (d / 4)) * 4;
+        *reinterpret_cast<float4*>(QT + j * LDT + c4) =
+            *reinterpret_cast<const float4*>(p.q_tilde + ((int64_t)gh * m + b0 + j) * d + c4);
+    }
+    const float* th_g = p.theta + ((int64_t)gh * m + b0) * dv;
+    for (int e = tid; e < nb * (dv / 4); e += TOK_THREADS)
+        *reinterpret_cast<float4*>(TH + e * 4) = *reinterpret_cast<const float4*>(th_g + e * 4);
+    for (int e = tid; e < m * nb; e += TOK_THREADS) {
+        const int a = e / nb, j = e % nb;
+        MU[a * TOK_BMAX + j] = p.mu[((int64_t)gh * m + a) * m + b0 + j];
+    }
     __syncthreads();
-    float* mz = p.mz + (int64_t)gh * 2 * m;
-    if (tid < m) {
-        // f_a in base 2 for every landmark
-        const float4* kt = reinterpret_cast<const float4*>(p.k_tilde + ((int64_t)g * m + tid) * d);
+    // f_a (base 2) for every landmark: 4 lanes per landmark
+    for (int e = tid; e < 64 * 4; e += TOK_THREADS) {
+        const int a = e >> 2, qq = e & 3;
         float acc = 0.f;
-        for (int t4 = 0; t4 < d / 4; t4 += 8) {
-            float4 x[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) x[u] = t4 + u < d / 4 ? kt[t4 + u] : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int t = 4 * (t4 + u);
-                if (t < d) acc += x[u].x * Ql[t] + x[u].y * Ql[t + 1] + x[u].z * Ql[t + 2] + x[u].w * Ql[t + 3];
+        if (a < m) {
+            const float* kr = KT + a * LDT;
+            for (int t = qq * 4; t < d; t += 16) {
+                const float4 x = *reinterpret_cast<const float4*>(kr + t);
+                acc += x.x * Ql[t] + x.y * Ql[t + 1] + x.z * Ql[t + 2] + x.w * Ql[t + 3];
             }
         }
-        EA[tid] = acc * p.scale * TOK_LOG2E;
-    } else if (tid >= 64 && tid - 64 < nb) {
-        // the evicted key folded into landmark b
-        const int j = tid - 64, b = b0 + j;
-        const float Mo = mz[b], Zo = mz[m + b];
-        float Mn = Mo, R = 1.f, x = 0.f, Zn = Zo;
-        if (r.full) {
-            const float4* qt = reinterpret_cast<const float4*>(p.q_tilde + ((int64_t)gh * m + b) * d);
-            float acc = 0.f;
-            for (int t4 = 0; t4 < d / 4; t4 += 8) {
-                float4 y[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) y[u] = t4 + u < d / 4 ? qt[t4 + u] : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int t = 4 * (t4 + u);
-                    if (t < d) acc += y[u].x * KE[t] + y[u].y * KE[t + 1] + y[u].z * KE[t + 2] + y[u].w * KE[t + 3];
-                }
+        acc = group_sum(acc, 4);
+        if (qq == 0 && a < m) EA[a] = acc * p.scale * TOK_LOG2E;
+    }
+    // the evicted key folded into each landmark of the range: 16 lanes each
+    {
+        const int j = tid >> 4, qq = tid & 15;   // 16 landmarks x 16 lanes
+        float acc = 0.f;
+        if (j < nb && r.full) {
+            const float* qr = QT + j * LDT;
+            for (int t = qq * 4; t < d; t += 64) {
+                const float4 y = *reinterpret_cast<const float4*>(qr + t);
+                acc += y.x * KE[t] + y.y * KE[t + 1] + y.z * KE[t + 2] + y.w * KE[t + 3];
             }
-            const float l = acc * p.scale;
-            Mn = fmaxf(Mo, l);
-            R = (Mn == Mo) ? 1.f : expf(Mo - Mn);
-            x = expf(l - Mn);
-            Zn = Zo * R + x;
-            mz[b] = Mn;
-            mz[m + b] = Zn;
         }
-        MB[j] = Mn;
-        RB[j] = R;
-        XB[j] = x;
-        ZB[j] = Zn;
+        acc = group_sum(acc, 16);
+        if (qq == 0 && j < nb) {
+            const int b = b0 + j;
+            const float Mo = mz[b], Zo = mz[m + b];
+            float Mn = Mo, R = 1.f, x = 0.f, Zn = Zo;
+            if (r.full) {
+                const float l = acc * p.scale;
+                Mn = fmaxf(Mo, l);
+                R = (Mn == Mo) ? 1.f : expf(Mo - Mn);
+                x = expf(l - Mn);
+                Zn = Zo * R + x;
+                mz[b] = Mn;
+                mz[m + b] = Zn;
+            }
+            MB[j] = Mn;
+            RB[j] = R;
+            XB[j] = x;
+            ZB[j] = Zn;
+        }
     }
     __syncthreads();
     if (wave == 0) {
@@ -254,19 +298,17 @@ __global__ __launch_bounds__(TOK_THREADS) void k_tok_part(KParams p, float* part
     __syncthreads();
     const float fmax = RED[0];
     const float cl = fmax + RED[1] * TOK_LOG2E;   // the range's exponent, base 2
-    if (tid < nb) {
-        // u_b = sum_a e_a mu[a][b]; loads batched ahead of the sum
-        const float* mu = p.mu + (int64_t)gh * m * m + b0 + tid;
+    // u_b = sum_a e_a mu[a][b] and the gains: 16 lanes per landmark
+    {
+        const int j = tid >> 4, qq = tid & 15;
         float u = 0.f;
-        for (int a0 = 0; a0 < m; a0 += 16) {
-            float mv[16];
-#pragma unroll
-            for (int k = 0; k < 16; ++k) mv[k] = a0 + k < m ? mu[(int64_t)(a0 + k) * m] : 0.f;
-#pragma unroll
-            for (int k = 0; k < 16; ++k) if (a0 + k < m) u += EA[a0 + k] * mv[k];
+        if (j < nb)
+            for (int a = qq; a < m; a += 16) u += EA[a] * MU[a * TOK_BMAX + j];
+        u = group_sum(u, 16);
+        if (qq == 0 && j < nb) {
+            if (p.rect) u = fmaxf(u, 0.f);
+            GB[j] = u * exp2f(fmax + MB[j] * TOK_LOG2E - cl);
         }
-        if (p.rect) u = fmaxf(u, 0.f);
-        GB[tid] = u * exp2f(fmax + MB[tid] * TOK_LOG2E - cl);
     }
     __syncthreads();
     if (wave == 0) {
@@ -276,34 +318,20 @@ __global__ __launch_bounds__(TOK_THREADS) void k_tok_part(KParams p, float* part
             rec[1] = dd;
         }
     }
-    // Theta' = R Theta + x v_e (written back) and N = sum_b gain_b Theta'_b:
-    // two halves of the range, value columns across threads, every load of a
-    // thread issued before its stores
-    const int half = tid / (TOK_THREADS / 2), tt0 = tid % (TOK_THREADS / 2);
-    const int hb = (nb + 1) / 2;
-    const int jb0 = half * hb, jb1 = min(nb, jb0 + hb);
+    // Theta' = R Theta + x v_e (written back) and N = sum_b gain_b Theta'_b
     float* th = p.theta + ((int64_t)gh * m + b0) * dv;
-    for (int t = tt0; t < dv; t += TOK_THREADS / 2) {
-        float v[TOK_BMAX / 2 + 1];
-#pragma unroll
-        for (int k = 0; k < TOK_BMAX / 2 + 1; ++k) v[k] = jb0 + k < jb1 ? th[(int64_t)(jb0 + k) * dv + t] : 0.f;
+    for (int t = tid; t < dv; t += TOK_THREADS) {
         float acc = 0.f;
-#pragma unroll
-        for (int k = 0; k < TOK_BMAX / 2 + 1; ++k) {
-            const int j = jb0 + k;
-            if (j < jb1) {
-                float x = v[k];
-                if (r.full) {
-                    x = x * RB[j] + XB[j] * VE[t];
-                    th[(int64_t)j * dv + t] = x;
-                }
-                acc += GB[j] * x;
+        for (int j = 0; j < nb; ++j) {
+            float x = TH[j * dv + t];
+            if (r.full) {
+                x = x * RB[j] + XB[j] * VE[t];
+                th[(int64_t)j * dv + t] = x;
             }
+            acc += GB[j] * x;
         }
-        NP[half * dv + t] = acc;
+        rec[2 + t] = acc;
     }
-    __syncthreads();
-    for (int t = tid; t < dv; t += TOK_THREADS) rec[2 + t] = NP[t] + NP[dv + t];
 }
 
 // One block per query head: the head's partials to one exponent, the far
@@ -319,29 +347,28 @@ __global__ __launch_bounds__(TOK_THREADS) void k_tok_merge(KParams p, const floa
     const int64_t rl = tok_rec(dv);
     const float* nearp = part + (int64_t)g * nsplit * H * rl + (int64_t)h * rl;   // stride H*rl
     const float* farp = part + (int64_t)p.G * nsplit * H * rl + (int64_t)gh * TOK_FB * rl;
-    float* WN = lds;              // [nsplit] near weights
-    float* WF = WN + nsplit;      // [TOK_FB] far weights
-    float* RED = WF + TOK_FB;     // [4]
+    const int nrec = nsplit + TOK_FB;
+    float* WS = lds;              // [nrec] weights (near splits, then far ranges)
+    float* ACC = WS + nrec;       // [TOK_THREADS / dv >= 1][dv] partial sums
+    float* RED = ACC + 2 * dv;    // [4]
+    const bool farok = farp[0] != -INFINITY;   // far records hold -inf when the far field is empty
     if (wave == 0) {
         float cmax = -INFINITY;
-        for (int sp = lane; sp < nsplit; sp += 64) cmax = fmaxf(cmax, nearp[(int64_t)sp * H * rl]);
-        const bool farok = farp[0] != -INFINITY;   // far records hold -inf when the far field is empty
-        if (farok && lane < TOK_FB) cmax = fmaxf(cmax, farp[(int64_t)lane * rl]);
+        for (int k = lane; k < nrec; k += 64) {
+            const float* rc = k < nsplit ? nearp + (int64_t)k * H * rl : farp + (int64_t)(k - nsplit) * rl;
+            if (k < nsplit || farok) cmax = fmaxf(cmax, rc[0]);
+        }
         cmax = wmax(cmax);
-        float den = 0.f;
-        for (int sp = lane; sp < nsplit; sp += 64) {
-            const float* rc = nearp + (int64_t)sp * H * rl;
-            const float w = exp2f(rc[0] - cmax);
-            WN[sp] = w;
-            den += rc[1] * w;
+        float den = 0.f, dfar = 0.f;
+        for (int k = lane; k < nrec; k += 64) {
+            const float* rc = k < nsplit ? nearp + (int64_t)k * H * rl : farp + (int64_t)(k - nsplit) * rl;
+            float w = 0.f;
+            if (k < nsplit || farok) w = exp2f(rc[0] - cmax);
+            if (k < nsplit) den += rc[1] * w;
+            else dfar += rc[1] * w;
+            WS[k] = w;
         }
         den = wsum(den);
-        float dfar = 0.f;
-        if (farok && lane < TOK_FB) {
-            const float w = exp2f(farp[(int64_t)lane * rl] - cmax);
-            WF[lane] = w;
-            dfar = farp[(int64_t)lane * rl + 1] * w;
-        }
         dfar = wsum(dfar);
         const bool have = farok && dfar >= 0.f;
         if (lane == 0) {
@@ -352,20 +379,33 @@ __global__ __launch_bounds__(TOK_THREADS) void k_tok_merge(KParams p, const floa
     __syncthreads();
     const float inv = RED[0];
     const bool have = RED[1] > 0.5f;
-    float* orow = p.out + (int64_t)gh * dv;
-    for (int t = tid; t < dv; t += TOK_THREADS) {
+    // two halves of the records over value columns; each thread issues all
+    // of its loads before it sums
+    const int halves = dv <= TOK_THREADS / 2 ? 2 : 1;
+    const int t = tid % (TOK_THREADS / halves), hb = tid / (TOK_THREADS / halves);
+    const int kend = have ? nrec : nsplit;
+    const int per = (kend + halves - 1) / halves;
+    const int ka = hb * per, kb = min(kend, ka + per);
+    if (t < dv) {
         float acc = 0.f;
-        for (int sp0 = 0; sp0 < nsplit; sp0 += 8) {
+        for (int k0 = ka; k0 < kb; k0 += 8) {
             float x[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) x[k] = sp0 + k < nsplit ? nearp[(int64_t)(sp0 + k) * H * rl + 2 + t] : 0.f;
+            for (int u = 0; u < 8; ++u) {
+                const int k = k0 + u;
+                const float* rc = k < nsplit ? nearp + (int64_t)k * H * rl : farp + (int64_t)(k - nsplit) * rl;
+                x[u] = k < kb ? rc[2 + t] : 0.f;
+            }
 #pragma unroll
-            for (int k = 0; k < 8; ++k) if (sp0 + k < nsplit) acc += x[k] * WN[sp0 + k];
+            for (int u = 0; u < 8; ++u)
+                if (k0 + u < kb) acc += x[u] * WS[k0 + u];
         }
-        if (have)
-            for (int fb = 0; fb < TOK_FB; ++fb) acc += farp[(int64_t)fb * rl + 2 + t] * WF[fb];
-        orow[t] = acc * inv;
+        ACC[hb * dv + t] = acc;
     }
+    __syncthreads();
+    float* orow = p.out + (int64_t)gh * dv;
+    for (int c2 = tid; c2 < dv; c2 += TOK_THREADS)
+        orow[c2] = (ACC[c2] + (halves == 2 ? ACC[dv + c2] : 0.f)) * inv;
     if (h == 0) {
         // commit: ring push and meta (every reader of the ring and meta of
         // this group ran in the previous kernel)
@@ -374,8 +414,8 @@ __global__ __launch_bounds__(TOK_THREADS) void k_tok_merge(KParams p, const floa
         __syncthreads();   // all threads have read meta before thread 0 writes it
         float* kd = p.ring_k + ((int64_t)g * p.W + r.slot) * p.d;
         float* vd = p.ring_v + ((int64_t)g * p.W + r.slot) * dv;
-        for (int t = tid; t < p.d; t += TOK_THREADS) kd[t] = p.k[(int64_t)g * p.d + t];
-        for (int t = tid; t < dv; t += TOK_THREADS) vd[t] = p.v[(int64_t)g * dv + t];
+        for (int e = tid; e < p.d; e += TOK_THREADS) kd[e] = p.k[(int64_t)g * p.d + e];
+        for (int e = tid; e < dv; e += TOK_THREADS) vd[e] = p.v[(int64_t)g * dv + e];
         if (tid == 0) {
             p.meta[4 * g + 0] = (uint32_t)r.len1;
             p.meta[4 * g + 1] = (uint32_t)r.head1;
@@ -387,21 +427,25 @@ __global__ __launch_bounds__(TOK_THREADS) void k_tok_merge(KParams p, const floa
 hipError_t launch_token(const KParams& p, float* part, hipStream_t st)
 {
     const int nsplit = tok_splits(p.ns, p.W);
-    const size_t lds_near = sizeof(float) * ((size_t)TOK_KEYS * (p.d + 4) +
-                                             (size_t)TOK_KEYS * (p.dv + 4) + (size_t)p.H * p.d);
-    const size_t lds_far = sizeof(float) * ((size_t)2 * p.d + p.dv + 64 + 5 * 16 + 4 + 2 * p.dv);
+    const size_t lds_near = sizeof(float) * ((size_t)TOK_KEYS * (p.d + 4) + (size_t)TOK_KEYS * (p.dv + 4) +
+                                             (size_t)p.H * p.d + (size_t)p.H * TOK_KEYS + 2 * p.H);
+    const size_t lds_far = sizeof(float) * ((size_t)2 * p.d + p.dv + (size_t)p.m * (p.d + 4) +
+                                            (size_t)TOK_BMAX * (p.d + 4) + (size_t)TOK_BMAX * p.dv +
+                                            (size_t)p.m * TOK_BMAX + 64 + 5 * 16 + 4);
     const size_t lds = lds_near > lds_far ? lds_near : lds_far;
     const int blocks = p.G * nsplit + p.nh * TOK_FB;
-    static bool attr_set = false;
-    if (!attr_set) {
-        (void)hipFuncSetAttribute((const void*)k_tok_part,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        attr_set = true;
+    // dynamic LDS beyond 64 KiB has to be allowed explicitly
+    static size_t lds_allowed = 64 * 1024;
+    if (lds > lds_allowed) {
+        const hipError_t e = hipFuncSetAttribute((const void*)k_tok_part,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        lds_allowed = lds;
     }
     hipLaunchKernelGGL(k_tok_part, dim3(blocks), dim3(TOK_THREADS), lds, st, p, part, nsplit);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t lds_merge = sizeof(float) * ((size_t)nsplit + TOK_FB + 4);
+    const size_t lds_merge = sizeof(float) * ((size_t)nsplit + TOK_FB + 2 * p.dv + 4);
     hipLaunchKernelGGL(k_tok_merge, dim3(p.nh), dim3(TOK_THREADS), lds_merge, st, p,
                        (const float*)part, nsplit);
     return hipGetLastError();
