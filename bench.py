@@ -161,27 +161,48 @@ def run_gpu(args, cfg):
     )
 
     # decode: one row at a time after the 32768-row prompt (the state left by
-    # the last timed step), through swl_attend_token
+    # the last timed step), through swl_attend_token.  Timed two ways: a host
+    # loop through the Python binding, and HIP-graph replays of captured
+    # 256-token segments (the GPU time of the path, without Python).
     if nd > 0:
         qd = torch.from_numpy(qh[T:]).to(dev)
         kd = torch.from_numpy(kh[T:]).to(dev)
         vd = torch.from_numpy(vh[T:]).to(dev)
         od = torch.empty((nd, cfg.nh, cfg.dv), dtype=torch.float32, device=dev)
         tscr = swl.alloc_scratch(geom, 1, device=dev)
+        views = [(qd[i:i + 1], kd[i:i + 1], vd[i:i + 1], od[i:i + 1]) for i in range(nd)]
+        sh = torch.cuda.current_stream().cuda_stream
         nw = min(16, nd)
         for i in range(nw):
-            swl.swl_attend_token(st, qd[i:i + 1], kd[i:i + 1], vd[i:i + 1], od[i:i + 1], tscr)
+            swl.swl_attend_token(st, *views[i], tscr, stream=sh)
         torch.cuda.synchronize()
         d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         d0.record()
         for i in range(nw, nd):
-            swl.swl_attend_token(st, qd[i:i + 1], kd[i:i + 1], vd[i:i + 1], od[i:i + 1], tscr)
+            swl.swl_attend_token(st, *views[i], tscr, stream=sh)
         d1.record()
         torch.cuda.synchronize()
-        us = d0.elapsed_time(d1) * 1e3 / (nd - nw)
+        us_host = d0.elapsed_time(d1) * 1e3 / (nd - nw)
+        seg = min(256, nd)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            gs = torch.cuda.current_stream().cuda_stream
+            for i in range(seg):
+                swl.swl_attend_token(st, *views[i], tscr, stream=gs)
+        graph.replay()
+        torch.cuda.synchronize()
+        reps = max(1, (nd - nw) // seg)
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(reps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        us = g0.elapsed_time(g1) * 1e3 / (reps * seg)
         db = decode_bytes(cfg)
-        res["decode"] = dict(tokens=nd - nw, us_per_token=us, bytes_per_token=db,
-                             achieved_gbs=db / (us * 1e-6) / 1e9,
+        res["decode"] = dict(tokens=reps * seg, us_per_token=us, timing="HIP graph replay of "
+                             f"{seg}-token segments", us_per_token_host_loop=us_host,
+                             bytes_per_token=db, achieved_gbs=db / (us * 1e-6) / 1e9,
                              frac_hbm=db / (us * 1e-6) / 1e9 / HBM_PEAK_GBS)
 
     # the per-sub-chunk API (attend_chunk + commit per 64 rows), for comparison

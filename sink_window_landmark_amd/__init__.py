@@ -103,8 +103,14 @@ class Geom:
         return self.G * self.H
 
     def c(self) -> _Geom:
-        sc = self.scale if self.scale is not None else 1.0 / math.sqrt(self.d)
-        return _Geom(self.G, self.H, self.m, self.W, self.ns, self.d, self.dv, sc, int(self.rect))
+        """The swl_geom struct (built once per Geom)."""
+        cached = self.__dict__.get("_c")
+        if cached is None:
+            sc = self.scale if self.scale is not None else 1.0 / math.sqrt(self.d)
+            cached = _Geom(self.G, self.H, self.m, self.W, self.ns, self.d, self.dv, sc,
+                           int(self.rect))
+            object.__setattr__(self, "_c", cached)
+        return cached
 
 
 class LayerState:
@@ -154,15 +160,30 @@ class LayerState:
     def clone(self) -> "LayerState":
         return LayerState(self.geom, **{f: getattr(self, f).clone() for f in self.FIELDS})
 
+    def __setattr__(self, name, value):
+        if name in self.FIELDS:
+            self.__dict__.pop("_c", None)   # a replaced field needs a new struct
+        object.__setattr__(self, name, value)
+
     def c(self) -> _State:
-        return _State(*(getattr(self, f).data_ptr() for f in self.FIELDS))
+        """The swl_state struct of device pointers (built once, and again after
+        a field is replaced)."""
+        cached = self.__dict__.get("_c")
+        if cached is None:
+            cached = _State(*(getattr(self, f).data_ptr() for f in self.FIELDS))
+            self.__dict__["_c"] = cached
+        return cached
 
 
 def _stream(stream) -> Optional[int]:
-    import torch
+    """A hipStream_t handle: torch's current stream by default, a torch
+    Stream, or an integer handle as is."""
+    if isinstance(stream, int):
+        return stream
     if stream is None:
+        import torch
         stream = torch.cuda.current_stream()
-    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return stream.cuda_stream
 
 
 def _check(name, t, shape, dtype=None):

@@ -321,3 +321,46 @@ def test_tokens_after_chunks_match_chunk_path():
     check_out(got_t, want, "tokens")
     check_out(got_c, want, "chunks")
     check_state(read_state(a), orc)
+
+
+def test_token_graph_replays_match_eager():
+    """Tokens captured in a HIP graph, replayed several times with eager work
+    in between, give the eager results every time."""
+    banner("token path under HIP graph replay")
+    t = torch()
+    cfg = synth.SMALL.replace(rows=300, W=256, m=16)
+    host = synth.make_state(cfg)
+    q, k, v = synth.rows(cfg, 0, 300 + 8)
+    base = _state(cfg, host)
+    _prefill(cfg, base, q[:300], k[:300], v[:300])
+    qd, kd, vd = dev(q[300:]), dev(k[300:]), dev(v[300:])
+    n = 8
+    # eager reference: three consecutive passes over the same 8 rows
+    ref = base.clone()
+    scr = swl.alloc_scratch(ref.geom, 1)
+    want = []
+    for rep in range(3):
+        o = t.empty((n, cfg.nh, cfg.dv), dtype=t.float32, device="cuda")
+        for i in range(n):
+            swl.swl_attend_token(ref, qd[i:i + 1], kd[i:i + 1], vd[i:i + 1], o[i:i + 1], scr)
+        want.append(o.cpu().numpy())
+    want_state = read_state(ref)
+    # the same three passes as replays of one captured pass
+    st = base.clone()
+    scr2 = swl.alloc_scratch(st.geom, 1)
+    out = t.zeros((n, cfg.nh, cfg.dv), dtype=t.float32, device="cuda")
+    swl.swl_attend_token(st.clone(), qd[0:1], kd[0:1], vd[0:1], out[0:1], scr2)   # first-call set-up
+    t.cuda.synchronize()
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g):
+        for i in range(n):
+            swl.swl_attend_token(st, qd[i:i + 1], kd[i:i + 1], vd[i:i + 1], out[i:i + 1], scr2)
+    for rep in range(3):
+        g.replay()
+        t.cuda.synchronize()
+        got = out.cpu().numpy()
+        np.testing.assert_array_equal(got, want[rep])
+        _ = (dev(np.ones(1000, np.float32)) * 2).sum().item()   # eager work between replays
+    got_state = read_state(st)
+    for f in want_state:
+        np.testing.assert_array_equal(got_state[f], want_state[f])
