@@ -83,208 +83,253 @@ __device__ __forceinline__ float group_sum(float x, int n)
     return x;
 }
 
-// Every block first issues all of its global loads into LDS (one round
-// trip), then computes from LDS.
-__global__ __launch_bounds__(TOK_THREADS) void k_tok_part(KParams p, float* part, int nsplit)
-{
-    extern __shared__ float lds[];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int d = p.d, dv = p.dv, H = p.H, m = p.m;
-    const int nnear = p.G * nsplit;
-    float* nearp = part;                                           // [G][nsplit][H][rec]
-    float* farp = part + (int64_t)p.G * nsplit * H * tok_rec(dv);  // [nh][FB][rec]
+constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
 
-    if ((int)blockIdx.x < nnear) {
-        // ---------------- near partial ----------------
-        // Keys are taken by physical position (sinks, then ring slots 0 ..
-        // W-1), which needs no bookkeeping to address: the softmax does not
-        // depend on their order.  Once meta is in, slots outside the window
-        // are masked and the new row's key stands in at its slot.
-        const int g = blockIdx.x / nsplit, sp = blockIdx.x % nsplit;
-        const int k0 = sp * TOK_KEYS;
-        float* base = nearp + (int64_t)g * nsplit * H * tok_rec(dv);
-        const int LDK = d + 4, LDV = dv + 4;
-        float* Kl = lds;                      // [64][d+4]
-        float* Vl = Kl + TOK_KEYS * LDK;      // [64][dv+4]
-        float* Ql = Vl + TOK_KEYS * LDV;      // [H][d]
-        float* Pl = Ql + H * d;               // [H][64] scores, then weights
-        float* ST = Pl + H * TOK_KEYS;        // [H][2] max, mass
-        constexpr int NL = TOK_KEYS * (128 / 4) / TOK_THREADS;   // f4 per thread at d = 128
-        constexpr int NQ = 16 * (128 / 4) / TOK_THREADS;         // queries, f4 per thread
-        const f4 z4 = {0.f, 0.f, 0.f, 0.f};
-        f4 kx[NL], vx[NL], qx[NQ];
-        // every load is issued before the first use of any of them; the loads
-        // take clamped (in-bounds) addresses and carry no condition, so no
-        // load waits for another
-        const int nkv = p.ns + p.W;
-#pragma unroll
-        for (int u = 0; u < NL; ++u) {
-            const int e = min(tid + u * TOK_THREADS, TOK_KEYS * (d / 4) - 1);
-            const int row = e / (d / 4), c4 = (e % (d / 4)) * 4;
-            const int x = min(k0 + row, nkv - 1);
-            // both candidates computed, then selected: no branch around the loads
-            const int xs = max(min(x, p.ns - 1), 0), xr = max(x - p.ns, 0);
-            const float* ks = p.sink_k + ((int64_t)g * p.ns + xs) * d;
-            const float* vs = p.sink_v + ((int64_t)g * p.ns + xs) * dv;
-            const float* kr = p.ring_k + ((int64_t)g * p.W + xr) * d;
-            const float* vr = p.ring_v + ((int64_t)g * p.W + xr) * dv;
-            const float* kp = x < p.ns ? ks : kr;
-            const float* vp = x < p.ns ? vs : vr;
-            kx[u] = *reinterpret_cast<const f4*>(kp + c4);
-            vx[u] = *reinterpret_cast<const f4*>(vp + c4);
+// Sum, over groups of L lanes (L a power of two; the lanes of a group differ
+// only in their low log2 L bits), of N partial values held by each lane.
+// While a lane holds more than one value, each step hands half of them to the
+// partner lane and keeps the other half (a reduce-scatter); once one is left,
+// the remaining steps add it across.  Afterwards slot i (i < slots) of lane
+// li holds the group sum of original index index(i, li).  The steps are
+// template recursions, so that every array index is a constant from the
+// start (a select between two elements must not become a per-lane index).
+template <int N, int L>
+struct LaneReduce {
+    static constexpr int slots = N >= L ? N / L : 1;
+    static constexpr int share = L > N ? L / N : 1;   // lanes holding the same sum
+    __device__ static int index(int i, int li) { return i + (li / share) * slots; }
+
+    template <int I, int HALF>
+    __device__ static void pairs(float (&v)[N], bool up, int s)
+    {
+        if constexpr (I < HALF) {
+            const float lo = v[I], hi = v[I + HALF];
+            const float send = up ? lo : hi, keep = up ? hi : lo;
+            v[I] = keep + __shfl_xor(send, s, 64);
+            pairs<I + 1, HALF>(v, up, s);
         }
-#pragma unroll
-        for (int u = 0; u < NQ; ++u) {
-            const int e = min(tid + u * TOK_THREADS, H * (d / 4) - 1);
-            qx[u] = *reinterpret_cast<const f4*>(p.q + (int64_t)g * H * d + e * 4);
-        }
-        const bool nrow = tid < d / 4;   // threads that carry the new row's key and value
-        const int tn = min(tid, d / 4 - 1);
-        const f4 knew = *reinterpret_cast<const f4*>(p.k + (int64_t)g * d + tn * 4);
-        const f4 vnew = *reinterpret_cast<const f4*>(p.v + (int64_t)g * dv + tn * 4);
-        const GMeta c = load_gmeta(p.meta, g, p.W);
-        const TokRow r = tok_row(c);
-        // key x of this block is live: a sink, or a slot inside the window
-        // after the push (written with no short-circuit and no division, so
-        // that it compiles to selects rather than branches)
-        auto live = [&](int x) {
-            const int sl = x - p.ns;
-            const int md = sl >= c.head0 ? sl - c.head0 : sl - c.head0 + c.wg;   // age order of slot sl
-            return (x < nkv) & ((x < p.ns) | ((sl < c.wg) & (md < r.len1)));
-        };
-        const int xnew = p.ns + r.slot;   // where the new row's key sits
-#pragma unroll
-        for (int u = 0; u < NL; ++u) {
-            const int e = tid + u * TOK_THREADS;
-            const int row = e / (d / 4), c4 = (e % (d / 4)) * 4;
-            const int x = k0 + row;
-            if (e < TOK_KEYS * (d / 4) && x != xnew) {   // the new row's threads write that row
-                const bool ok = live(x);
-                *reinterpret_cast<f4*>(Kl + row * LDK + c4) = ok ? kx[u] : z4;
-                *reinterpret_cast<f4*>(Vl + row * LDV + c4) = ok ? vx[u] : z4;
-            }
-        }
-        if (nrow && xnew >= k0 && xnew < k0 + TOK_KEYS) {
-            *reinterpret_cast<f4*>(Kl + (xnew - k0) * LDK + tid * 4) = knew;
-            *reinterpret_cast<f4*>(Vl + (xnew - k0) * LDV + tid * 4) = vnew;
-        }
-        const float qs = p.scale * TOK_LOG2E;
-#pragma unroll
-        for (int u = 0; u < NQ; ++u) {
-            const int e = tid + u * TOK_THREADS;
-            if (e < H * (d / 4))
-                *reinterpret_cast<f4*>(Ql + e * 4) =
-                    qx[u] * qs;
-        }
-        __syncthreads();
-        // scores: thread per (head, key); dead keys score -inf
-        for (int e = tid; e < H * TOK_KEYS; e += TOK_THREADS) {
-            const int h = e / TOK_KEYS, j = e % TOK_KEYS;
-            const int x = k0 + j;
-            float acc = -INFINITY;
-            if (live(x)) {
-                const float* kr = Kl + j * LDK;
-                const float* qr = Ql + h * d;
-                acc = 0.f;
-#pragma unroll 8
-                for (int t = 0; t < d; t += 4) {
-                    const f4 a = *reinterpret_cast<const f4*>(kr + t);
-                    const f4 b = *reinterpret_cast<const f4*>(qr + t);
-                    acc += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
-                }
-            }
-            Pl[e] = acc;
-        }
-        __syncthreads();
-        // per head: max, weights, mass (a wave per head, lane = key)
-        for (int h = wave; h < H; h += TOK_THREADS / 64) {
-            const float sc = Pl[h * TOK_KEYS + lane];
-            const float mx = wmax(sc);
-            const float pv = sc == -INFINITY ? 0.f : exp2f(sc - mx);
-            const float l = wsum(pv);
-            Pl[h * TOK_KEYS + lane] = pv;
-            if (lane == 0) {
-                ST[2 * h] = mx;
-                ST[2 * h + 1] = l;
-            }
-        }
-        __syncthreads();
-        // value sums: thread per (head, value column); dead keys hold zero rows
-        for (int e = tid; e < H * dv; e += TOK_THREADS) {
-            const int h = e / dv, t = e % dv;
-            const float* pr = Pl + h * TOK_KEYS;
-            float acc = 0.f;
-#pragma unroll 8
-            for (int j = 0; j < TOK_KEYS; ++j) acc += pr[j] * Vl[j * LDV + t];
-            float* rec = base + ((int64_t)sp * H + h) * tok_rec(dv);
-            rec[2 + t] = acc;
-            if (t == 0) {
-                rec[0] = ST[2 * h];
-                rec[1] = ST[2 * h + 1];
-            }
-        }
-        return;
     }
+    template <int S, int n>   // partner distance, values held
+    __device__ static void step(float (&v)[N], int li)
+    {
+        if constexpr (S >= 1) {
+            if constexpr (n > 1)
+                pairs<0, n / 2>(v, (li & S) != 0, S);
+            else
+                v[0] += __shfl_xor(v[0], S, 64);
+            step<S / 2, (n > 1 ? n / 2 : 1)>(v, li);
+        }
+    }
+    __device__ static void run(float (&v)[N], int li) { step<L / 2, N>(v, li); }
+};
 
-    // ---------------- far partial ----------------
-    const int fbk = blockIdx.x - nnear;
-    const int gh = fbk / TOK_FB, fb = fbk % TOK_FB;
-    const int g = gh / H;
+__device__ __forceinline__ float dot4(f4 a, f4 b) { return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w; }
+
+// Near partial of group g, keys k0 .. k0+63 taken by physical position (the
+// sinks, then ring slots 0 .. W-1), which needs no bookkeeping to address:
+// the softmax does not depend on their order.  Thread (rb, li) holds columns
+// 4li .. 4li+3 of key rows rb, rb + RPP, ... in registers, straight from
+// global memory: scores are lane-group sums, and the value sums are formed in
+// registers and summed over the block through LDS.  Once meta is in, slots
+// outside the window are masked and the new row's key stands in at its slot.
+template <int D>
+__device__ __forceinline__ void tok_near(const KParams& p, float* nearp, int nsplit, int blk, float* lds)
+{
+    constexpr int L = D / 4;                                   // lanes per key row
+    constexpr int RPP = TOK_THREADS / L;                       // key rows per pass
+    constexpr int NL = RPP >= TOK_KEYS ? 1 : TOK_KEYS / RPP;   // passes
+    constexpr int HC = 4;                                      // heads per chunk
+    using LR = LaneReduce<NL * HC, L>;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int li = tid % L, rb = tid / L, c4 = li * 4;
+    const int H = p.H;
+    const int g = blk / nsplit, sp = blk % nsplit, k0 = sp * TOK_KEYS;
+    const int nkv = p.ns + p.W;
+    float* SC = lds;                  // [H][64] scores, then weights
+    float* ST = SC + H * TOK_KEYS;    // [16][2] max, mass
+    float* PS = ST + 32;              // [4][H][D] value sums of each wave
+    const f4 z4 = {0.f, 0.f, 0.f, 0.f};
+    // every load is issued before the first use of any of them: clamped
+    // (in-bounds) addresses, no condition on the loads
+    f4 kx[NL], vx[NL], q0[HC];
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+        const int row = min(rb + u * RPP, TOK_KEYS - 1);
+        const int x = min(k0 + row, nkv - 1);
+        // both candidates computed, then selected: no branch around the loads
+        const int xs = max(min(x, p.ns - 1), 0), xr = max(x - p.ns, 0);
+        const float* ks = p.sink_k + ((int64_t)g * p.ns + xs) * D;
+        const float* vs = p.sink_v + ((int64_t)g * p.ns + xs) * D;
+        const float* kr = p.ring_k + ((int64_t)g * p.W + xr) * D;
+        const float* vr = p.ring_v + ((int64_t)g * p.W + xr) * D;
+        kx[u] = *reinterpret_cast<const f4*>((x < p.ns ? ks : kr) + c4);
+        vx[u] = *reinterpret_cast<const f4*>((x < p.ns ? vs : vr) + c4);
+    }
+#pragma unroll
+    for (int j = 0; j < HC; ++j) q0[j] = *reinterpret_cast<const f4*>(p.q + ((int64_t)g * H + min(j, H - 1)) * D + c4);
+    const f4 knew = *reinterpret_cast<const f4*>(p.k + (int64_t)g * D + c4);
+    const f4 vnew = *reinterpret_cast<const f4*>(p.v + (int64_t)g * D + c4);
     const GMeta c = load_gmeta(p.meta, g, p.W);
     const TokRow r = tok_row(c);
-    float* rec = farp + ((int64_t)gh * TOK_FB + fb) * tok_rec(dv);
+    // key x is live: a sink, or a slot inside the window after the push
+    // (no short-circuit and no division: selects rather than branches)
+    auto live = [&](int x) {
+        const int sl = x - p.ns;
+        const int md = sl >= c.head0 ? sl - c.head0 : sl - c.head0 + c.wg;   // age order of slot sl
+        return (x < nkv) & ((x < p.ns) | ((sl < c.wg) & (md < r.len1)));
+    };
+    const int xnew = p.ns + r.slot;   // where the new row's key sits
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+        const int row = rb + u * RPP, x = k0 + row;
+        const bool ok = (row < TOK_KEYS) & live(x), nw = (row < TOK_KEYS) & (x == xnew);
+        kx[u] = nw ? knew : (ok ? kx[u] : z4);   // dead rows hold zeros (their memory may hold anything)
+        vx[u] = nw ? vnew : (ok ? vx[u] : z4);
+    }
+    const float qs = p.scale * TOK_LOG2E;   // scores in base 2
+    for (int hc = 0; hc < H; hc += HC) {
+        f4 qc[HC];
+#pragma unroll
+        for (int j = 0; j < HC; ++j)
+            qc[j] = hc == 0 ? q0[j] : *reinterpret_cast<const f4*>(p.q + ((int64_t)g * H + min(hc + j, H - 1)) * D + c4);
+        float s[NL * HC];
+#pragma unroll
+        for (int u = 0; u < NL; ++u)
+#pragma unroll
+            for (int j = 0; j < HC; ++j) s[u * HC + j] = dot4(kx[u], qc[j]);
+        LR::run(s, li);
+#pragma unroll
+        for (int i = 0; i < LR::slots; ++i) {
+            const int idx = LR::index(i, li), u = idx / HC, h = hc + idx % HC, row = rb + u * RPP;
+            if (li % LR::share == 0 && row < TOK_KEYS && h < H)
+                SC[h * TOK_KEYS + row] = live(k0 + row) ? s[i] * qs : -INFINITY;
+        }
+    }
+    __syncthreads();
+    // per head: max, weights, mass (a wave per head, lane = key)
+    for (int h = wave; h < H; h += TOK_THREADS / 64) {
+        const float sc = lane < TOK_KEYS ? SC[h * TOK_KEYS + lane] : -INFINITY;
+        const float mx = wmax(sc);
+        const float pv = sc == -INFINITY ? 0.f : exp2f(sc - mx);
+        const float l = wsum(pv);
+        if (lane < TOK_KEYS) SC[h * TOK_KEYS + lane] = pv;
+        if (lane == 0) {
+            ST[2 * h] = mx;
+            ST[2 * h + 1] = l;
+        }
+    }
+    __syncthreads();
+    // value sums: registers, then over the row groups of the wave, then over the waves
+    for (int hc = 0; hc < H; hc += HC) {
+        f4 acc[HC];
+#pragma unroll
+        for (int j = 0; j < HC; ++j) acc[j] = z4;
+#pragma unroll
+        for (int u = 0; u < NL; ++u) {
+            const int row = min(rb + u * RPP, TOK_KEYS - 1);   // rows past the block hold zero values
+#pragma unroll
+            for (int j = 0; j < HC; ++j) {
+                const float w = hc + j < H ? SC[min(hc + j, H - 1) * TOK_KEYS + row] : 0.f;
+                acc[j] += w * vx[u];
+            }
+        }
+#pragma unroll
+        for (int k = ilog2(L); k < 6; ++k) {
+            const int s = 1 << k;
+#pragma unroll
+            for (int j = 0; j < HC; ++j) {
+                acc[j].x += __shfl_xor(acc[j].x, s, 64);
+                acc[j].y += __shfl_xor(acc[j].y, s, 64);
+                acc[j].z += __shfl_xor(acc[j].z, s, 64);
+                acc[j].w += __shfl_xor(acc[j].w, s, 64);
+            }
+        }
+        if (lane < L)
+#pragma unroll
+            for (int j = 0; j < HC; ++j)
+                if (hc + j < H) *reinterpret_cast<f4*>(PS + ((int64_t)wave * H + hc + j) * D + c4) = acc[j];
+    }
+    __syncthreads();
+    float* base = nearp + (int64_t)g * nsplit * H * tok_rec(D);
+    for (int e = tid; e < H * D; e += TOK_THREADS) {
+        const int h = e / D, t = e % D;
+        float a = 0.f;
+#pragma unroll
+        for (int w = 0; w < TOK_THREADS / 64; ++w) a += PS[((int64_t)w * H + h) * D + t];
+        float* rec = base + ((int64_t)sp * H + h) * tok_rec(D);
+        rec[2 + t] = a;
+        if (t == 0) {
+            rec[0] = ST[2 * h];
+            rec[1] = ST[2 * h + 1];
+        }
+    }
+}
+
+// Far partial of query head gh over landmark range fb.  When the ring is full
+// the row evicts the key at slot head; every landmark b of the range folds it
+// in (l = scale <q~_b, k_e>, M' = max(M, l), R = 1 if M' == M else e^{M-M'},
+// Z' = R Z + e^{l-M'}, Theta' = R Theta + e^{l-M'} v_e) and writes M', Z',
+// Theta' back.  Then the far estimate of the range against M': u_b = sum_a
+// e^{f_a-f_max} mu[a][b] (>= 0 with rect), gain_b against the range's own
+// exponent, D = sum_b gain_b Z'_b and N = sum_b gain_b Theta'_b -- for a
+// one-row chunk the chunk form's R Theta + cf v_e is exactly Theta'.  The
+// landmark keys and queries stay in registers (lane-group sums, as in the
+// near blocks); the accumulators and mu pass through LDS.
+template <int D>
+__device__ __forceinline__ void tok_far(const KParams& p, float* farp, int fbk, float* lds)
+{
+    constexpr int L = D / 4, RPP = TOK_THREADS / L;
+    constexpr int NK = RPP >= 64 ? 1 : 64 / RPP;                 // landmark-key passes (m <= 64)
+    constexpr int NQ = RPP >= TOK_BMAX ? 1 : TOK_BMAX / RPP;     // landmark-query passes
+    constexpr int NTH = TOK_BMAX * (D / 4) / TOK_THREADS > 0 ? TOK_BMAX * (D / 4) / TOK_THREADS : 1;
+    constexpr int NMU = 64 * TOK_BMAX / TOK_THREADS;
+    using LRK = LaneReduce<NK, L>;
+    using LRQ = LaneReduce<NQ, L>;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int li = tid % L, rb = tid / L, c4 = li * 4;
+    const int H = p.H, m = p.m;
+    const int gh = fbk / TOK_FB, fb = fbk % TOK_FB, g = gh / H;
+    const GMeta c = load_gmeta(p.meta, g, p.W);
+    const TokRow r = tok_row(c);
+    float* rec = farp + ((int64_t)gh * TOK_FB + fb) * tok_rec(D);
     const int per = (m + TOK_FB - 1) / TOK_FB;   // <= TOK_BMAX
     const int b0 = fb * per, b1 = min(m, b0 + per), nb = b1 - b0;
     if (r.nfar1 == 0 || nb <= 0) {
-        for (int t = tid; t < tok_rec(dv); t += TOK_THREADS) rec[t] = t == 0 ? -INFINITY : 0.f;
+        for (int t = tid; t < tok_rec(D); t += TOK_THREADS) rec[t] = t == 0 ? -INFINITY : 0.f;
         return;
     }
-    const int LDT = d + 4;
-    float* Ql = lds;                  // [d]
-    float* KE = Ql + d;               // [d]       evicted key
-    float* VE = KE + d;               // [dv]      evicted value
-    float* KT = VE + dv;              // [64][d+4] landmark keys
-    float* QT = KT + 64 * LDT;        // [16][d+4] this range's landmark queries
-    float* TH = QT + TOK_BMAX * LDT;  // [16][dv]  this range's accumulators
-    float* MU = TH + TOK_BMAX * dv;   // [64][16]  mu[a][b0 + j]
-    float* EA = MU + 64 * TOK_BMAX;   // [64]      f_a, then e_a
-    float* MB = EA + 64;              // [16]      M'
+    float* TH = lds;                  // [16][D]   this range's accumulators
+    float* MU = TH + TOK_BMAX * D;    // [64][16]  mu[a][b0 + j]
+    float* VE = MU + 64 * TOK_BMAX;   // [D]       evicted value
+    float* EA = VE + D;               // [64]      f_a, then e_a
+    float* LB = EA + 64;              // [16]      evicted key's score per landmark
+    float* MB = LB + 16;              // [16]      M'
     float* RB = MB + 16;              // [16]      R
     float* XB = RB + 16;              // [16]      exp(l - M')
     float* ZB = XB + 16;              // [16]      Z'
     float* GB = ZB + 16;              // [16]      gains
     float* RED = GB + 16;             // [4]
     float* mz = p.mz + (int64_t)gh * 2 * m;
-    const float* ring_k_e = p.ring_k + ((int64_t)g * p.W + c.head0) * d;
-    const float* ring_v_e = p.ring_v + ((int64_t)g * p.W + c.head0) * dv;
-    // every global load of the block is issued before the first LDS store
-    constexpr int NKT = 64 * (128 / 4) / TOK_THREADS;         // landmark keys, f4 per thread
-    constexpr int NQT = TOK_BMAX * (128 / 4) / TOK_THREADS;   // landmark queries
-    constexpr int NTH = TOK_BMAX * (128 / 4) / TOK_THREADS;   // accumulators
-    constexpr int NMU = 64 * TOK_BMAX / TOK_THREADS;          // mu entries
     const f4 z4 = {0.f, 0.f, 0.f, 0.f};
-    f4 kt[NKT], qt[NQT], tv[NTH];
+    // loads, unconditional from clamped addresses; the evicted key's come
+    // last, as their address needs meta
+    f4 kt[NK], qt[NQ], tv[NTH];
     float mu[NMU];
-    // unconditional loads from clamped addresses (see the near blocks)
-    const float qv = p.q[(int64_t)gh * d + min(tid, d - 1)];
-    const float ke = ring_k_e[min(tid, d - 1)];
-    const float ve = ring_v_e[min(tid, dv - 1)];
-    const float* th_g = p.theta + ((int64_t)gh * m + b0) * dv;
 #pragma unroll
-    for (int u = 0; u < NKT; ++u) {
-        const int e = tid + u * TOK_THREADS;
-        const int a = min(e / (d / 4), m - 1), c4 = (e % (d / 4)) * 4;
-        kt[u] = *reinterpret_cast<const f4*>(p.k_tilde + ((int64_t)g * m + a) * d + c4);
+    for (int u = 0; u < NK; ++u) {
+        const int a = min(rb + u * RPP, m - 1);
+        kt[u] = *reinterpret_cast<const f4*>(p.k_tilde + ((int64_t)g * m + a) * D + c4);
     }
+    const f4 qh = *reinterpret_cast<const f4*>(p.q + (int64_t)gh * D + c4);
 #pragma unroll
-    for (int u = 0; u < NQT; ++u) {
-        const int e = tid + u * TOK_THREADS;
-        const int j = min(e / (d / 4), nb - 1), c4 = (e % (d / 4)) * 4;
-        qt[u] = *reinterpret_cast<const f4*>(p.q_tilde + ((int64_t)gh * m + b0 + j) * d + c4);
+    for (int u = 0; u < NQ; ++u) {
+        const int j = min(rb + u * RPP, nb - 1);
+        qt[u] = *reinterpret_cast<const f4*>(p.q_tilde + ((int64_t)gh * m + b0 + j) * D + c4);
     }
+    const float* th_g = p.theta + ((int64_t)gh * m + b0) * D;
 #pragma unroll
     for (int u = 0; u < NTH; ++u) {
-        const int e = min(tid + u * TOK_THREADS, nb * (dv / 4) - 1);
+        const int e = min(tid + u * TOK_THREADS, nb * (D / 4) - 1);
         tv[u] = *reinterpret_cast<const f4*>(th_g + e * 4);
     }
 #pragma unroll
@@ -293,86 +338,69 @@ __global__ __launch_bounds__(TOK_THREADS) void k_tok_part(KParams p, float* part
         const int a = min(e / TOK_BMAX, m - 1), j = min(e % TOK_BMAX, nb - 1);
         mu[u] = p.mu[((int64_t)gh * m + a) * m + b0 + j];
     }
-    if (tid < d) {
-        Ql[tid] = qv;
-        KE[tid] = r.full ? ke : 0.f;
-    }
-    if (tid < dv) VE[tid] = r.full ? ve : 0.f;
-#pragma unroll
-    for (int u = 0; u < NKT; ++u) {
-        const int e = tid + u * TOK_THREADS;
-        const int a = e / (d / 4), c4 = (e % (d / 4)) * 4;
-        if (a < 64) *reinterpret_cast<f4*>(KT + a * LDT + c4) = a < m ? kt[u] : z4;
-    }
-#pragma unroll
-    for (int u = 0; u < NQT; ++u) {
-        const int e = tid + u * TOK_THREADS;
-        const int j = e / (d / 4), c4 = (e % (d / 4)) * 4;
-        if (j < TOK_BMAX) *reinterpret_cast<f4*>(QT + j * LDT + c4) = j < nb ? qt[u] : z4;
-    }
+    const int bj = b0 + min(tid, nb - 1);
+    const float Mo = mz[bj], Zo = mz[m + bj];
+    const f4 ke = *reinterpret_cast<const f4*>(p.ring_k + ((int64_t)g * p.W + c.head0) * D + c4);
+    const float ve = p.ring_v[((int64_t)g * p.W + c.head0) * D + min(tid, D - 1)];
+    // LDS: accumulators, mu, evicted value
 #pragma unroll
     for (int u = 0; u < NTH; ++u) {
         const int e = tid + u * TOK_THREADS;
-        if (e < TOK_BMAX * (dv / 4)) *reinterpret_cast<f4*>(TH + e * 4) = e < nb * (dv / 4) ? tv[u] : z4;
+        if (e < TOK_BMAX * (D / 4)) *reinterpret_cast<f4*>(TH + e * 4) = e < nb * (D / 4) ? tv[u] : z4;
     }
 #pragma unroll
     for (int u = 0; u < NMU; ++u) {
         const int e = tid + u * TOK_THREADS;
         MU[e] = (e / TOK_BMAX < m && e % TOK_BMAX < nb) ? mu[u] : 0.f;
     }
-    __syncthreads();
-    // f_a (base 2) for every landmark: 4 lanes per landmark
-    for (int e = tid; e < 64 * 4; e += TOK_THREADS) {
-        const int a = e >> 2, qq = e & 3;
-        float acc = 0.f;
-        if (a < m) {
-            const float* kr = KT + a * LDT;
-            for (int t = qq * 4; t < d; t += 16) {
-                const f4 x = *reinterpret_cast<const f4*>(kr + t);
-                acc += x.x * Ql[t] + x.y * Ql[t + 1] + x.z * Ql[t + 2] + x.w * Ql[t + 3];
-            }
-        }
-        acc = group_sum(acc, 4);
-        if (qq == 0 && a < m) EA[a] = acc * p.scale * TOK_LOG2E;
-    }
-    // the evicted key folded into each landmark of the range: 16 lanes each
+    if (tid < D) VE[tid] = r.full ? ve : 0.f;
+    // f_a (base 2) for every landmark, and the evicted key's score per landmark of the range
     {
-        const int j = tid >> 4, qq = tid & 15;   // 16 landmarks x 16 lanes
-        float acc = 0.f;
-        if (j < nb && r.full) {
-            const float* qr = QT + j * LDT;
-            for (int t = qq * 4; t < d; t += 64) {
-                const f4 y = *reinterpret_cast<const f4*>(qr + t);
-                acc += y.x * KE[t] + y.y * KE[t + 1] + y.z * KE[t + 2] + y.w * KE[t + 3];
-            }
+        float s[NK];
+#pragma unroll
+        for (int u = 0; u < NK; ++u) s[u] = dot4(kt[u], qh);
+        LRK::run(s, li);
+#pragma unroll
+        for (int i = 0; i < LRK::slots; ++i) {
+            const int a = rb + LRK::index(i, li) * RPP;
+            if (li % LRK::share == 0 && a < m) EA[a] = s[i] * p.scale * TOK_LOG2E;
         }
-        acc = group_sum(acc, 16);
-        if (qq == 0 && j < nb) {
-            const int b = b0 + j;
-            const float Mo = mz[b], Zo = mz[m + b];
-            float Mn = Mo, R = 1.f, x = 0.f, Zn = Zo;
-            if (r.full) {
-                const float l = acc * p.scale;
-                Mn = fmaxf(Mo, l);
-                R = (Mn == Mo) ? 1.f : expf(Mo - Mn);
-                x = expf(l - Mn);
-                Zn = Zo * R + x;
-                mz[b] = Mn;
-                mz[m + b] = Zn;
-            }
-            MB[j] = Mn;
-            RB[j] = R;
-            XB[j] = x;
-            ZB[j] = Zn;
+        float t[NQ];
+#pragma unroll
+        for (int u = 0; u < NQ; ++u) t[u] = dot4(qt[u], ke);
+        LRQ::run(t, li);
+#pragma unroll
+        for (int i = 0; i < LRQ::slots; ++i) {
+            const int j = rb + LRQ::index(i, li) * RPP;
+            if (li % LRQ::share == 0 && j < nb) LB[j] = t[i] * p.scale;
         }
     }
     __syncthreads();
-    if (wave == 0) {
+    // the fold, a thread per landmark of the range
+    if (tid < nb) {
+        float Mn = Mo, R = 1.f, x = 0.f, Zn = Zo;
+        if (r.full) {
+            const float l = LB[tid];
+            Mn = fmaxf(Mo, l);
+            R = (Mn == Mo) ? 1.f : expf(Mo - Mn);
+            x = expf(l - Mn);
+            Zn = Zo * R + x;
+            mz[bj] = Mn;
+            mz[m + bj] = Zn;
+        }
+        MB[tid] = Mn;
+        RB[tid] = R;
+        XB[tid] = x;
+        ZB[tid] = Zn;
+    }
+    if (wave == 1) {
         const float f = lane < m ? EA[lane] : -INFINITY;
         const float fmax = wmax(f);
         if (lane < m) EA[lane] = exp2f(f - fmax);
         if (lane == 0) RED[0] = fmax;
-    } else if (wave == 1) {
+    }
+    __syncthreads();
+    if (wave == 0) {
         const float mm = wmax(lane < nb ? MB[lane] : -INFINITY);
         if (lane == 0) RED[1] = mm;
     }
@@ -400,19 +428,30 @@ __global__ __launch_bounds__(TOK_THREADS) void k_tok_part(KParams p, float* part
         }
     }
     // Theta' = R Theta + x v_e (written back) and N = sum_b gain_b Theta'_b
-    float* th = p.theta + ((int64_t)gh * m + b0) * dv;
-    for (int t = tid; t < dv; t += TOK_THREADS) {
+    float* th = p.theta + ((int64_t)gh * m + b0) * D;
+    for (int t = tid; t < D; t += TOK_THREADS) {
         float acc = 0.f;
         for (int j = 0; j < nb; ++j) {
-            float x = TH[j * dv + t];
+            float x = TH[j * D + t];
             if (r.full) {
                 x = x * RB[j] + XB[j] * VE[t];
-                th[(int64_t)j * dv + t] = x;
+                th[(int64_t)j * D + t] = x;
             }
             acc += GB[j] * x;
         }
         rec[2 + t] = acc;
     }
+}
+
+template <int D>
+__global__ __launch_bounds__(TOK_THREADS) void k_tok_part(KParams p, float* part, int nsplit)
+{
+    extern __shared__ float lds[];
+    const int nnear = p.G * nsplit;
+    if ((int)blockIdx.x < nnear)
+        tok_near<D>(p, part, nsplit, blockIdx.x, lds);
+    else
+        tok_far<D>(p, part + (int64_t)nnear * p.H * tok_rec(D), blockIdx.x - nnear, lds);
 }
 
 // One block per query head: the head's partials to one exponent, the far
@@ -534,26 +573,29 @@ __global__ __launch_bounds__(TOK_MT) void k_tok_merge(KParams p, const float* pa
     }
 }
 
+template <int D>
+static hipError_t launch_part(const KParams& p, float* part, int nsplit, hipStream_t st)
+{
+    const size_t lds_near = sizeof(float) * ((size_t)p.H * TOK_KEYS + 32 + (size_t)4 * p.H * D);
+    const size_t lds_far = sizeof(float) * ((size_t)TOK_BMAX * D + 64 * TOK_BMAX + D + 64 + 6 * 16 + 4);
+    const size_t lds = lds_near > lds_far ? lds_near : lds_far;   // <= 37 KiB
+    hipLaunchKernelGGL(k_tok_part<D>, dim3(p.G * nsplit + p.nh * TOK_FB), dim3(TOK_THREADS), lds, st, p, part,
+                       nsplit);
+    return hipGetLastError();
+}
+
 hipError_t launch_token(const KParams& p, float* part, hipStream_t st)
 {
     const int nsplit = tok_splits(p.ns, p.W);
-    const size_t lds_near = sizeof(float) * ((size_t)TOK_KEYS * (p.d + 4) + (size_t)TOK_KEYS * (p.dv + 4) +
-                                             (size_t)p.H * p.d + (size_t)p.H * TOK_KEYS + 2 * p.H);
-    const size_t lds_far = sizeof(float) * ((size_t)2 * p.d + p.dv + (size_t)64 * (p.d + 4) +
-                                            (size_t)TOK_BMAX * (p.d + 4) + (size_t)TOK_BMAX * p.dv +
-                                            (size_t)64 * TOK_BMAX + 64 + 5 * 16 + 4);
-    const size_t lds = lds_near > lds_far ? lds_near : lds_far;
-    const int blocks = p.G * nsplit + p.nh * TOK_FB;
-    // dynamic LDS beyond 64 KiB has to be allowed explicitly
-    static size_t lds_allowed = 64 * 1024;
-    if (lds > lds_allowed) {
-        const hipError_t e = hipFuncSetAttribute((const void*)k_tok_part,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        lds_allowed = lds;
+    hipError_t e;
+    switch (p.d) {
+    case 8: e = launch_part<8>(p, part, nsplit, st); break;
+    case 16: e = launch_part<16>(p, part, nsplit, st); break;
+    case 32: e = launch_part<32>(p, part, nsplit, st); break;
+    case 64: e = launch_part<64>(p, part, nsplit, st); break;
+    case 128: e = launch_part<128>(p, part, nsplit, st); break;
+    default: return hipErrorInvalidValue;
     }
-    hipLaunchKernelGGL(k_tok_part, dim3(blocks), dim3(TOK_THREADS), lds, st, p, part, nsplit);
-    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t lds_merge = sizeof(float) * ((size_t)(TOK_MT / p.dv + 1) * (p.dv + 2));
     hipLaunchKernelGGL(k_tok_merge, dim3(p.nh), dim3(TOK_MT), lds_merge, st, p,
