@@ -30,7 +30,7 @@ namespace swl {
 constexpr int TOK_KEYS = 64;    // keys per near block
 constexpr int TOK_FB = 4;       // far blocks per query head (landmark ranges)
 constexpr int TOK_BMAX = 16;    // landmarks per far block (m <= 64)
-constexpr int TOK_THREADS = 256;
+constexpr int TOK_THREADS = 512;
 constexpr float TOK_LOG2E = 1.4426950408889634f;
 
 // a native 4-wide vector: arrays of it stay in registers (HIP's float4 is a
@@ -39,8 +39,9 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 
 int tok_splits(int ns, int W) { return (ns + W + TOK_KEYS - 1) / TOK_KEYS; }
 
-// partial record: [0] max (base 2), [1] mass, [2 .. 2+dv) value sum
-__host__ __device__ inline int64_t tok_rec(int dv) { return 2 + dv; }
+// partial record: [0] max (base 2), [1] mass, [4 .. 4+dv) value sum (16-byte aligned)
+constexpr int TOK_V0 = 4;
+__host__ __device__ inline int64_t tok_rec(int dv) { return TOK_V0 + dv; }
 
 size_t tok_part_floats(int G, int H, int dv, int ns, int W)
 {
@@ -62,25 +63,127 @@ __device__ __forceinline__ TokRow tok_row(const GMeta& c)
     return r;
 }
 
+// Lane exchanges without LDS.  The partner of a lane at bit B is the lane
+// index xor 1, 2, 7, 15, 16, 32 for B = 0 .. 5: DPP quad permutes, the 8- and
+// 16-lane mirrors, then the gfx950 permlane swaps across rows.  The masks
+// are linearly independent with top bit B, which is all that sums over a
+// whole group of lanes need (for a sum that must keep the lanes below bit B
+// apart, use xor_sum).
+template <int C>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), C, 0xF, 0xF, false));
+}
+template <int B>
+struct DppCtl;
+template <> struct DppCtl<0> { static constexpr int v = 0xB1; };    // quad_perm 1,0,3,2
+template <> struct DppCtl<1> { static constexpr int v = 0x4E; };    // quad_perm 2,3,0,1
+template <> struct DppCtl<2> { static constexpr int v = 0x141; };   // row_half_mirror
+template <> struct DppCtl<3> { static constexpr int v = 0x140; };   // row_mirror
+
+// the two halves of a permlane swap of (a, b), as floats
+template <int B>
+__device__ __forceinline__ void pl_swap(float a, float b, float& r0, float& r1)
+{
+    static_assert(B == 4 || B == 5, "cross-row swaps only");
+    if constexpr (B == 4) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+        r0 = __uint_as_float(r[0]);
+        r1 = __uint_as_float(r[1]);
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+        r0 = __uint_as_float(r[0]);
+        r1 = __uint_as_float(r[1]);
+    }
+}
+
+// x plus (or max with) the partner's x at bit B
+template <int B>
+__device__ __forceinline__ float pair_sum(float x)
+{
+    if constexpr (B <= 3) {
+        return x + dpp<DppCtl<B>::v>(x);
+    } else {
+        float r0, r1;
+        pl_swap<B>(x, x, r0, r1);   // lanes of both halves see (lower x, upper x)
+        return r0 + r1;
+    }
+}
+template <int B>
+__device__ __forceinline__ float pair_max(float x)
+{
+    if constexpr (B <= 3) {
+        return fmaxf(x, dpp<DppCtl<B>::v>(x));
+    } else {
+        float r0, r1;
+        pl_swap<B>(x, x, r0, r1);
+        return fmaxf(r0, r1);
+    }
+}
+// One reduce-scatter step: lanes with bit B clear get lo + the partner's lo,
+// lanes with it set hi + the partner's hi.
+template <int B>
+__device__ __forceinline__ float pair_split(float lo, float hi, int lane)
+{
+    if constexpr (B <= 3) {
+        const float a = lo + dpp<DppCtl<B>::v>(lo), b = hi + dpp<DppCtl<B>::v>(hi);
+        return (lane >> B) & 1 ? b : a;
+    } else {
+        float r0, r1;
+        pl_swap<B>(lo, hi, r0, r1);   // (own lo, partner lo) below, (partner hi, own hi) above
+        return r0 + r1;
+    }
+}
+// x plus the x of lane ^ (1 << B) exactly (the lanes below bit B kept apart)
+template <int B>
+__device__ __forceinline__ float xor_sum(float x)
+{
+    if constexpr (B <= 1 || B >= 4) return pair_sum<B>(x);
+    else return x + __shfl_xor(x, 1 << B, 64);
+}
+
+// the x of lane ^ (1 << B), exactly
+template <int B>
+__device__ __forceinline__ float xor_get(float x, int lane)
+{
+    if constexpr (B <= 1) {
+        return dpp<DppCtl<B>::v>(x);
+    } else if constexpr (B <= 3) {
+        return __shfl_xor(x, 1 << B, 64);
+    } else {
+        float r0, r1;
+        pl_swap<B>(x, x, r0, r1);   // (lower x, upper x) in every lane
+        return (lane >> B) & 1 ? r0 : r1;
+    }
+}
+
 __device__ __forceinline__ float wsum(float x)
 {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
-    return x;
+    x = pair_sum<0>(x);
+    x = pair_sum<1>(x);
+    x = pair_sum<2>(x);
+    x = pair_sum<3>(x);
+    x = pair_sum<4>(x);
+    return pair_sum<5>(x);
 }
 
 __device__ __forceinline__ float wmax(float x)
 {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-    return x;
+    x = pair_max<0>(x);
+    x = pair_max<1>(x);
+    x = pair_max<2>(x);
+    x = pair_max<3>(x);
+    x = pair_max<4>(x);
+    return pair_max<5>(x);
 }
 
-// Sum of x over groups of n consecutive lanes (n a power of two <= 64).
-__device__ __forceinline__ float group_sum(float x, int n)
+// Sum of x over aligned groups of 16 lanes.
+__device__ __forceinline__ float sum16(float x)
 {
-    for (int o = n >> 1; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
-    return x;
+    x = pair_sum<0>(x);
+    x = pair_sum<1>(x);
+    x = pair_sum<2>(x);
+    return pair_sum<3>(x);
 }
 
 constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
@@ -99,29 +202,45 @@ struct LaneReduce {
     static constexpr int share = L > N ? L / N : 1;   // lanes holding the same sum
     __device__ static int index(int i, int li) { return i + (li / share) * slots; }
 
-    template <int I, int HALF>
-    __device__ static void pairs(float (&v)[N], bool up, int s)
+    template <int I, int HALF, int B>
+    __device__ static void pairs(float (&v)[N], int lane)
     {
         if constexpr (I < HALF) {
-            const float lo = v[I], hi = v[I + HALF];
-            const float send = up ? lo : hi, keep = up ? hi : lo;
-            v[I] = keep + __shfl_xor(send, s, 64);
-            pairs<I + 1, HALF>(v, up, s);
+            v[I] = pair_split<B>(v[I], v[I + HALF], lane);
+            pairs<I + 1, HALF, B>(v, lane);
         }
     }
-    template <int S, int n>   // partner distance, values held
-    __device__ static void step(float (&v)[N], int li)
+    template <int B, int n>   // bit of the partner lane, values held
+    __device__ static void step(float (&v)[N], int lane)
     {
-        if constexpr (S >= 1) {
+        if constexpr (B >= 0) {
             if constexpr (n > 1)
-                pairs<0, n / 2>(v, (li & S) != 0, S);
+                pairs<0, n / 2, B>(v, lane);
             else
-                v[0] += __shfl_xor(v[0], S, 64);
-            step<S / 2, (n > 1 ? n / 2 : 1)>(v, li);
+                v[0] = pair_sum<B>(v[0]);
+            step<B - 1, (n > 1 ? n / 2 : 1)>(v, lane);
         }
     }
-    __device__ static void run(float (&v)[N], int li) { step<L / 2, N>(v, li); }
+    // lane: the lane index in the wave (its low log2 L bits are the index in the group)
+    __device__ static void run(float (&v)[N], int lane) { step<ilog2(L) - 1, N>(v, lane); }
 };
+
+// Sum of each value over the lanes of a wave that differ in bits B .. 5 (the
+// row groups of the wave), lanes below bit B kept apart.
+template <int B, int HC>
+__device__ __forceinline__ void rows_sum(f4 (&acc)[HC])
+{
+    if constexpr (B <= 5) {
+#pragma unroll
+        for (int j = 0; j < HC; ++j) {
+            acc[j].x = xor_sum<B>(acc[j].x);
+            acc[j].y = xor_sum<B>(acc[j].y);
+            acc[j].z = xor_sum<B>(acc[j].z);
+            acc[j].w = xor_sum<B>(acc[j].w);
+        }
+        rows_sum<B + 1>(acc);
+    }
+}
 
 __device__ __forceinline__ float dot4(f4 a, f4 b) { return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w; }
 
@@ -147,7 +266,7 @@ __device__ __forceinline__ void tok_near(const KParams& p, float* nearp, int nsp
     const int nkv = p.ns + p.W;
     float* SC = lds;                  // [H][64] scores, then weights
     float* ST = SC + H * TOK_KEYS;    // [16][2] max, mass
-    float* PS = ST + 32;              // [4][H][D] value sums of each wave
+    float* PS = ST + 32;              // [waves][4][D] value sums of each wave, for a chunk of 4 heads
     const f4 z4 = {0.f, 0.f, 0.f, 0.f};
     // every load is issued before the first use of any of them: clamped
     // (in-bounds) addresses, no condition on the loads
@@ -197,7 +316,7 @@ __device__ __forceinline__ void tok_near(const KParams& p, float* nearp, int nsp
         for (int u = 0; u < NL; ++u)
 #pragma unroll
             for (int j = 0; j < HC; ++j) s[u * HC + j] = dot4(kx[u], qc[j]);
-        LR::run(s, li);
+        LR::run(s, lane);
 #pragma unroll
         for (int i = 0; i < LR::slots; ++i) {
             const int idx = LR::index(i, li), u = idx / HC, h = hc + idx % HC, row = rb + u * RPP;
@@ -219,7 +338,10 @@ __device__ __forceinline__ void tok_near(const KParams& p, float* nearp, int nsp
         }
     }
     __syncthreads();
-    // value sums: registers, then over the row groups of the wave, then over the waves
+    // value sums: registers, then over the row groups of the wave, then over
+    // the waves through LDS, a chunk of HC heads at a time
+    constexpr int NWV = TOK_THREADS / 64;
+    float* base = nearp + (int64_t)g * nsplit * H * tok_rec(D);
     for (int hc = 0; hc < H; hc += HC) {
         f4 acc[HC];
 #pragma unroll
@@ -228,39 +350,28 @@ __device__ __forceinline__ void tok_near(const KParams& p, float* nearp, int nsp
         for (int u = 0; u < NL; ++u) {
             const int row = min(rb + u * RPP, TOK_KEYS - 1);   // rows past the block hold zero values
 #pragma unroll
-            for (int j = 0; j < HC; ++j) {
-                const float w = hc + j < H ? SC[min(hc + j, H - 1) * TOK_KEYS + row] : 0.f;
-                acc[j] += w * vx[u];
-            }
+            for (int j = 0; j < HC; ++j)   // heads past H repeat the last one; their sums are dropped
+                acc[j] += SC[min(hc + j, H - 1) * TOK_KEYS + row] * vx[u];
         }
-#pragma unroll
-        for (int k = ilog2(L); k < 6; ++k) {
-            const int s = 1 << k;
-#pragma unroll
-            for (int j = 0; j < HC; ++j) {
-                acc[j].x += __shfl_xor(acc[j].x, s, 64);
-                acc[j].y += __shfl_xor(acc[j].y, s, 64);
-                acc[j].z += __shfl_xor(acc[j].z, s, 64);
-                acc[j].w += __shfl_xor(acc[j].w, s, 64);
-            }
-        }
+        rows_sum<ilog2(L)>(acc);
+        if (hc > 0) __syncthreads();   // the previous chunk's sums have been read
         if (lane < L)
 #pragma unroll
-            for (int j = 0; j < HC; ++j)
-                if (hc + j < H) *reinterpret_cast<f4*>(PS + ((int64_t)wave * H + hc + j) * D + c4) = acc[j];
-    }
-    __syncthreads();
-    float* base = nearp + (int64_t)g * nsplit * H * tok_rec(D);
-    for (int e = tid; e < H * D; e += TOK_THREADS) {
-        const int h = e / D, t = e % D;
-        float a = 0.f;
+            for (int j = 0; j < HC; ++j) *reinterpret_cast<f4*>(PS + ((int64_t)wave * HC + j) * D + c4) = acc[j];
+        __syncthreads();
+        for (int e = tid; e < HC * (D / 4); e += TOK_THREADS) {
+            const int j = e / (D / 4), t = (e % (D / 4)) * 4, h = hc + j;
+            if (h < H) {
+                f4 a = *reinterpret_cast<const f4*>(PS + (int64_t)j * D + t);
 #pragma unroll
-        for (int w = 0; w < TOK_THREADS / 64; ++w) a += PS[((int64_t)w * H + h) * D + t];
-        float* rec = base + ((int64_t)sp * H + h) * tok_rec(D);
-        rec[2 + t] = a;
-        if (t == 0) {
-            rec[0] = ST[2 * h];
-            rec[1] = ST[2 * h + 1];
+                for (int w = 1; w < NWV; ++w) a += *reinterpret_cast<const f4*>(PS + ((int64_t)w * HC + j) * D + t);
+                float* rec = base + ((int64_t)sp * H + h) * tok_rec(D);
+                *reinterpret_cast<f4*>(rec + TOK_V0 + t) = a;
+                if (t == 0) {
+                    rec[0] = ST[2 * h];
+                    rec[1] = ST[2 * h + 1];
+                }
+            }
         }
     }
 }
@@ -359,7 +470,7 @@ __device__ __forceinline__ void tok_far(const KParams& p, float* farp, int fbk, 
         float s[NK];
 #pragma unroll
         for (int u = 0; u < NK; ++u) s[u] = dot4(kt[u], qh);
-        LRK::run(s, li);
+        LRK::run(s, lane);
 #pragma unroll
         for (int i = 0; i < LRK::slots; ++i) {
             const int a = rb + LRK::index(i, li) * RPP;
@@ -368,7 +479,7 @@ __device__ __forceinline__ void tok_far(const KParams& p, float* farp, int fbk, 
         float t[NQ];
 #pragma unroll
         for (int u = 0; u < NQ; ++u) t[u] = dot4(qt[u], ke);
-        LRQ::run(t, li);
+        LRQ::run(t, lane);
 #pragma unroll
         for (int i = 0; i < LRQ::slots; ++i) {
             const int j = rb + LRQ::index(i, li) * RPP;
@@ -413,7 +524,7 @@ __device__ __forceinline__ void tok_far(const KParams& p, float* farp, int fbk, 
         float u = 0.f;
         if (j < nb)
             for (int a = qq; a < m; a += 16) u += EA[a] * MU[a * TOK_BMAX + j];
-        u = group_sum(u, 16);
+        u = sum16(u);
         if (qq == 0 && j < nb) {
             if (p.rect) u = fmaxf(u, 0.f);
             GB[j] = u * exp2f(fmax + MB[j] * TOK_LOG2E - cl);
@@ -439,7 +550,7 @@ __device__ __forceinline__ void tok_far(const KParams& p, float* farp, int fbk, 
             }
             acc += GB[j] * x;
         }
-        rec[2 + t] = acc;
+        rec[TOK_V0 + t] = acc;
     }
 }
 
@@ -454,57 +565,88 @@ __global__ __launch_bounds__(TOK_THREADS) void k_tok_part(KParams p, float* part
         tok_far<D>(p, part + (int64_t)nnear * p.H * tok_rec(D), blockIdx.x - nnear, lds);
 }
 
-// One block per query head: the head's partials to one exponent, the far
-// part dropped when its total mass is not >= 0, out.  Thread (column, part)
-// folds records part, part + P, ... of the head with a running exponent (all
-// of its loads for up to TOK_MB records issued at once); the parts then meet
-// in LDS.  The first head of a group also pushes the row into the ring and
-// advances meta (no other block of this kernel reads them).
-constexpr int TOK_MT = 512;   // merge threads
-constexpr int TOK_MB = 16;    // records per thread per batch of loads
+// One block per query head: the head's partials to one exponent c = max of
+// all partial maxima (the pages' c = max(c_near, f_max + M'_b)), the far part
+// dropped when its total mass is not >= 0, out = (N + sum p v) / max(D + sum
+// p, 1e-30).  Thread (part, c4) folds records part, part + NPRT, ... with a
+// running exponent, reading each record's head and columns 4c4 .. 4c4+3 as
+// 16-byte loads; parts 0 .. 3 also take one far range each.  The parts meet
+// in LDS.  The first head of a group then pushes the row into the ring (slot
+// head when the ring is full, else head + len) and advances meta: no other
+// block of this kernel reads them, and every reader ran in the previous one.
+// Two partials (exponent m, mass l, value sums a) to one, against the larger
+// exponent; either may be empty (m = -inf).
+__device__ __forceinline__ void merge2(float& m, float& l, f4& a, float m2, float l2, f4 a2)
+{
+    const float mn = fmaxf(m, m2);
+    const float w1 = m == -INFINITY ? 0.f : exp2f(m - mn), w2 = m2 == -INFINITY ? 0.f : exp2f(m2 - mn);
+    l = l * w1 + l2 * w2;
+    a = a * w1 + a2 * w2;
+    m = mn;
+}
 
+// merge2 over the lanes of a wave that differ in bits B .. 5, lanes below bit
+// B kept apart; every lane of such a set ends with the same result
+template <int B>
+__device__ __forceinline__ void wave_merge(float& m, float& l, f4& a, int lane)
+{
+    if constexpr (B <= 5) {
+        f4 a2;
+        a2.x = xor_get<B>(a.x, lane);
+        a2.y = xor_get<B>(a.y, lane);
+        a2.z = xor_get<B>(a.z, lane);
+        a2.w = xor_get<B>(a.w, lane);
+        merge2(m, l, a, xor_get<B>(m, lane), xor_get<B>(l, lane), a2);
+        wave_merge<B + 1>(m, l, a, lane);
+    }
+}
+
+constexpr int TOK_MT = 512;   // merge threads
+constexpr int TOK_MB = 4;     // records per thread per batch of loads
+
+template <int D>
 __global__ __launch_bounds__(TOK_MT) void k_tok_merge(KParams p, const float* part, int nsplit)
 {
+    constexpr int C4 = D / 4;              // 16-byte columns
+    constexpr int NPRT = TOK_MT / C4;      // parts (>= 16 > TOK_FB)
     extern __shared__ float lds[];
-    const int gh = blockIdx.x, g = gh / p.H, h = gh % p.H;
-    const int tid = threadIdx.x;
-    const int H = p.H, dv = p.dv;
-    const int64_t rl = tok_rec(dv);
-    const float* nearp = part + (int64_t)g * nsplit * H * rl + (int64_t)h * rl;   // stride H*rl
+    const int gh = blockIdx.x, H = p.H, g = gh / H, h = gh % H;
+    const int tid = threadIdx.x, c4 = tid % C4, prt = tid / C4;
+    const int64_t rl = tok_rec(D);
+    const float* nearp = part + ((int64_t)g * nsplit * H + h) * rl;   // record k at k * H * rl
     const float* farp = part + (int64_t)p.G * nsplit * H * rl + (int64_t)gh * TOK_FB * rl;
-    const int P = TOK_MT / dv;                   // dv divides TOK_MT
-    const int col = tid % dv, prt = tid / dv;
-    float* SM = lds;                             // [P+1] exponent of each part; the far part last
-    float* SL = SM + P + 1;                      // [P+1] mass
-    float* SA = SL + P + 1;                      // [P+1][dv] value sums
-    // the far ranges: every thread reads them (their loads go out with the
-    // near records').  Their total mass is taken against their own largest
-    // exponent: its sign does not depend on the exponent.
-    float fmk[TOK_FB], flk[TOK_FB], fxk[TOK_FB];
-#pragma unroll
-    for (int j = 0; j < TOK_FB; ++j) {
-        fmk[j] = farp[j * rl];
-        flk[j] = farp[j * rl + 1];
-        fxk[j] = farp[j * rl + 2 + col];
-    }
-    float mrun = -INFINITY, lrun = 0.f, acc = 0.f;
-    // records k0, k0 + P, ..., k0 + (TOK_MB-1) P, folded in with a running exponent
+    constexpr int NW = TOK_MT / 64;        // waves
+    float* SM = lds;                       // [NW + TOK_FB] exponent of each wave, then of each far range
+    float* SL = SM + 16;                   // [NW + TOK_FB] mass
+    float* SA = SL + 16;                   // [NW + TOK_FB][D] value sums
+    // the commit's loads go out with the others (every block issues them;
+    // only the first head of a group stores)
+    const GMeta c = load_gmeta(p.meta, g, p.W);
+    const f4 kn = *reinterpret_cast<const f4*>(p.k + (int64_t)g * D + c4 * 4);
+    const f4 vn = *reinterpret_cast<const f4*>(p.v + (int64_t)g * D + c4 * 4);
+    // far range prt (parts 0 .. TOK_FB-1), loaded unconditionally
+    const float* fr = farp + (int64_t)min(prt, TOK_FB - 1) * rl;
+    const f4 fh = *reinterpret_cast<const f4*>(fr);
+    const f4 fx = *reinterpret_cast<const f4*>(fr + TOK_V0 + c4 * 4);
+    const f4 z4 = {0.f, 0.f, 0.f, 0.f};
+    float mrun = -INFINITY, lrun = 0.f;
+    f4 acc = z4;
+    // records k0, k0 + NPRT, ..., folded in with a running exponent
     auto fold = [&](int k0) {
-        float ms[TOK_MB], ls[TOK_MB], xs[TOK_MB];
+        f4 hd[TOK_MB], xs[TOK_MB];
 #pragma unroll
         for (int u = 0; u < TOK_MB; ++u) {
-            const int k = k0 + u * P;
-            const float* rc = nearp + (int64_t)min(k, nsplit - 1) * H * rl;   // clamped: no condition on the loads
-            ms[u] = rc[0];
-            ls[u] = rc[1];
-            xs[u] = rc[2 + col];
+            const float* rc = nearp + (int64_t)min(k0 + u * NPRT, nsplit - 1) * H * rl;   // clamped: no condition
+            hd[u] = *reinterpret_cast<const f4*>(rc);
+            xs[u] = *reinterpret_cast<const f4*>(rc + TOK_V0 + c4 * 4);
         }
-#pragma unroll
-        for (int u = 0; u < TOK_MB; ++u)
-            if (k0 + u * P >= nsplit) ms[u] = -INFINITY;
+        float ms[TOK_MB];
         float bm = mrun;
 #pragma unroll
-        for (int u = 0; u < TOK_MB; ++u) bm = fmaxf(bm, ms[u]);
+        for (int u = 0; u < TOK_MB; ++u) {
+            ms[u] = k0 + u * NPRT < nsplit ? hd[u].x : -INFINITY;
+            bm = fmaxf(bm, ms[u]);
+        }
         // no early exit when every record is empty: the loads stay unconditional
         const float bx = bm == -INFINITY ? 0.f : bm;
         const float sc = mrun == -INFINITY ? 0.f : exp2f(mrun - bx);
@@ -514,93 +656,105 @@ __global__ __launch_bounds__(TOK_MT) void k_tok_merge(KParams p, const float* pa
         for (int u = 0; u < TOK_MB; ++u) {
             const float w = ms[u] == -INFINITY ? 0.f : exp2f(ms[u] - bx);
             acc += w * xs[u];
-            lrun += w * ls[u];
+            lrun += w * hd[u].y;
         }
         mrun = bm;
     };
-    fold(prt);   // the first batch in straight-line code, so its loads go out with the far ones
-    for (int k0 = prt + TOK_MB * P; k0 < nsplit; k0 += TOK_MB * P) fold(k0);
-    SA[prt * dv + col] = acc;
-    if (col == 0) {
-        SM[prt] = mrun;
-        SL[prt] = lrun;
-    }
-    if (prt == 0) {
-        float fm = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < TOK_FB; ++j) fm = fmaxf(fm, fmk[j]);
-        float dfar = 0.f, xfar = 0.f;
-#pragma unroll
-        for (int j = 0; j < TOK_FB; ++j) {
-            const float w = fmk[j] == -INFINITY ? 0.f : exp2f(fmk[j] - fm);
-            dfar += w * flk[j];
-            xfar += w * fxk[j];
+    fold(prt);   // the first batch in straight-line code, so its loads go out with the rest
+    for (int k0 = prt + TOK_MB * NPRT; k0 < nsplit; k0 += TOK_MB * NPRT) fold(k0);
+    // the parts of a wave meet by lane exchanges (lanes that differ in the
+    // bits above the column bits), then the waves and the far ranges in LDS
+    wave_merge<ilog2(C4)>(mrun, lrun, acc, tid & 63);
+    const int wave = tid >> 6;
+    if ((tid & 63) < C4) {
+        *reinterpret_cast<f4*>(SA + (int64_t)wave * D + c4 * 4) = acc;
+        if (c4 == 0) {
+            SM[wave] = mrun;
+            SL[wave] = lrun;
         }
-        const bool have = fm != -INFINITY && dfar >= 0.f;   // else the far part is dropped
-        SA[P * dv + col] = have ? xfar : 0.f;
-        if (col == 0) {
-            SM[P] = have ? fm : -INFINITY;
-            SL[P] = have ? dfar : 0.f;
+    }
+    if (prt < TOK_FB) {
+        *reinterpret_cast<f4*>(SA + (int64_t)(NW + prt) * D + c4 * 4) = fx;
+        if (c4 == 0) {
+            SM[NW + prt] = fh.x;
+            SL[NW + prt] = fh.y;
         }
     }
     __syncthreads();
-    if (tid < dv) {
-        float c = -INFINITY;
-        for (int q = 0; q <= P; ++q) c = fmaxf(c, SM[q]);
-        float den = 0.f, num = 0.f;
-        for (int q = 0; q <= P; ++q) {
-            const float w = SM[q] == -INFINITY ? 0.f : exp2f(SM[q] - c);
-            den += w * SL[q];
-            num += w * SA[q * dv + tid];
+    if (tid < C4) {
+        float sm[NW + TOK_FB], sl[NW + TOK_FB];
+        f4 sa[NW + TOK_FB];
+#pragma unroll
+        for (int q = 0; q < NW + TOK_FB; ++q) {
+            sm[q] = SM[q];
+            sl[q] = SL[q];
+            sa[q] = *reinterpret_cast<const f4*>(SA + (int64_t)q * D + tid * 4);
         }
-        p.out[(int64_t)gh * dv + tid] = num / fmaxf(den, 1e-30f);
-    }
-    if (h == 0) {
-        // commit: ring push and meta (every reader of the ring and meta of
-        // this group ran in the previous kernel)
-        const GMeta c = load_gmeta(p.meta, g, p.W);
-        const TokRow r = tok_row(c);
-        __syncthreads();   // all threads have read meta before thread 0 writes it
-        float* kd = p.ring_k + ((int64_t)g * p.W + r.slot) * p.d;
-        float* vd = p.ring_v + ((int64_t)g * p.W + r.slot) * dv;
-        for (int e = tid; e < p.d; e += TOK_MT) kd[e] = p.k[(int64_t)g * p.d + e];
-        for (int e = tid; e < dv; e += TOK_MT) vd[e] = p.v[(int64_t)g * dv + e];
-        if (tid == 0) {
-            p.meta[4 * g + 0] = (uint32_t)r.len1;
-            p.meta[4 * g + 1] = (uint32_t)r.head1;
-            p.meta[4 * g + 2] = (uint32_t)r.nfar1;
+        // the far ranges' total mass against their own largest exponent: its
+        // sign does not depend on the exponent
+        float fm = -INFINITY;
+#pragma unroll
+        for (int j = NW; j < NW + TOK_FB; ++j) fm = fmaxf(fm, sm[j]);
+        float dfar = 0.f;
+#pragma unroll
+        for (int j = NW; j < NW + TOK_FB; ++j)
+            dfar += sm[j] == -INFINITY ? 0.f : sl[j] * exp2f(sm[j] - fm);
+        const bool have = fm != -INFINITY && dfar >= 0.f;   // else the far part is dropped
+#pragma unroll
+        for (int j = NW; j < NW + TOK_FB; ++j)
+            if (!have) sm[j] = -INFINITY;
+        float cm = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < NW + TOK_FB; ++q) cm = fmaxf(cm, sm[q]);
+        float den = 0.f;
+        f4 num = z4;
+#pragma unroll
+        for (int q = 0; q < NW + TOK_FB; ++q) {
+            const float w = sm[q] == -INFINITY ? 0.f : exp2f(sm[q] - cm);
+            den += w * sl[q];
+            num += w * sa[q];
+        }
+        *reinterpret_cast<f4*>(p.out + (int64_t)gh * D + tid * 4) = num * (1.f / fmaxf(den, 1e-30f));
+        if (h == 0) {
+            const TokRow r = tok_row(c);
+            *reinterpret_cast<f4*>(p.ring_k + ((int64_t)g * p.W + r.slot) * D + tid * 4) = kn;
+            *reinterpret_cast<f4*>(p.ring_v + ((int64_t)g * p.W + r.slot) * D + tid * 4) = vn;
+            if (tid == 0) {
+                p.meta[4 * g + 0] = (uint32_t)r.len1;
+                p.meta[4 * g + 1] = (uint32_t)r.head1;
+                p.meta[4 * g + 2] = (uint32_t)r.nfar1;
+            }
         }
     }
 }
 
+// the partial kernel, then the merge
 template <int D>
-static hipError_t launch_part(const KParams& p, float* part, int nsplit, hipStream_t st)
+static hipError_t launch_two(const KParams& p, float* part, int nsplit, hipStream_t st)
 {
-    const size_t lds_near = sizeof(float) * ((size_t)p.H * TOK_KEYS + 32 + (size_t)4 * p.H * D);
+    const size_t lds_near = sizeof(float) * ((size_t)p.H * TOK_KEYS + 32 + (size_t)(TOK_THREADS / 64) * 4 * D);
     const size_t lds_far = sizeof(float) * ((size_t)TOK_BMAX * D + 64 * TOK_BMAX + D + 64 + 6 * 16 + 4);
-    const size_t lds = lds_near > lds_far ? lds_near : lds_far;   // <= 37 KiB
+    const size_t lds = lds_near > lds_far ? lds_near : lds_far;   // <= 21 KiB
     hipLaunchKernelGGL(k_tok_part<D>, dim3(p.G * nsplit + p.nh * TOK_FB), dim3(TOK_THREADS), lds, st, p, part,
                        nsplit);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t lds_merge = sizeof(float) * (32 + (size_t)(TOK_MT / 64 + TOK_FB) * D);
+    hipLaunchKernelGGL(k_tok_merge<D>, dim3(p.nh), dim3(TOK_MT), lds_merge, st, p, (const float*)part, nsplit);
     return hipGetLastError();
 }
 
 hipError_t launch_token(const KParams& p, float* part, hipStream_t st)
 {
     const int nsplit = tok_splits(p.ns, p.W);
-    hipError_t e;
     switch (p.d) {
-    case 8: e = launch_part<8>(p, part, nsplit, st); break;
-    case 16: e = launch_part<16>(p, part, nsplit, st); break;
-    case 32: e = launch_part<32>(p, part, nsplit, st); break;
-    case 64: e = launch_part<64>(p, part, nsplit, st); break;
-    case 128: e = launch_part<128>(p, part, nsplit, st); break;
+    case 8: return launch_two<8>(p, part, nsplit, st);
+    case 16: return launch_two<16>(p, part, nsplit, st);
+    case 32: return launch_two<32>(p, part, nsplit, st);
+    case 64: return launch_two<64>(p, part, nsplit, st);
+    case 128: return launch_two<128>(p, part, nsplit, st);
     default: return hipErrorInvalidValue;
     }
-    if (e != hipSuccess) return e;
-    const size_t lds_merge = sizeof(float) * ((size_t)(TOK_MT / p.dv + 1) * (p.dv + 2));
-    hipLaunchKernelGGL(k_tok_merge, dim3(p.nh), dim3(TOK_MT), lds_merge, st, p,
-                       (const float*)part, nsplit);
-    return hipGetLastError();
 }
 
 }  // namespace swl
