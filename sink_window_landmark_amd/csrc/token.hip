@@ -242,6 +242,10 @@ __device__ __forceinline__ void rows_sum(f4 (&acc)[HC])
     }
 }
 
+// 2^x by the hardware instruction: arguments here are <= 0 (against a
+// maximum), and results below 2^-126 may flush to zero
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ float dot4(f4 a, f4 b) { return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w; }
 
 // Near partial of group g, keys k0 .. k0+63 taken by physical position (the
@@ -329,7 +333,7 @@ __device__ __forceinline__ void tok_near(const KParams& p, float* nearp, int nsp
     for (int h = wave; h < H; h += TOK_THREADS / 64) {
         const float sc = lane < TOK_KEYS ? SC[h * TOK_KEYS + lane] : -INFINITY;
         const float mx = wmax(sc);
-        const float pv = sc == -INFINITY ? 0.f : exp2f(sc - mx);
+        const float pv = sc == -INFINITY ? 0.f : ex2(sc - mx);
         const float l = wsum(pv);
         if (lane < TOK_KEYS) SC[h * TOK_KEYS + lane] = pv;
         if (lane == 0) {
@@ -409,10 +413,12 @@ __device__ __forceinline__ void tok_far(const KParams& p, float* farp, int fbk, 
         for (int t = tid; t < tok_rec(D); t += TOK_THREADS) rec[t] = t == 0 ? -INFINITY : 0.f;
         return;
     }
-    float* TH = lds;                  // [16][D]   this range's accumulators
-    float* MU = TH + TOK_BMAX * D;    // [64][16]  mu[a][b0 + j]
+    constexpr int C4 = D / 4;
+    static_assert(TOK_BMAX * C4 <= TOK_THREADS, "one accumulator piece per thread");
+    float* MU = lds;                  // [64][16]  mu[a][b0 + j]
     float* VE = MU + 64 * TOK_BMAX;   // [D]       evicted value
-    float* EA = VE + D;               // [64]      f_a, then e_a
+    float* NS = VE + D;               // [waves][D] value sums of each wave
+    float* EA = NS + (TOK_THREADS / 64) * D;   // [64] f_a, then e_a (0 past m)
     float* LB = EA + 64;              // [16]      evicted key's score per landmark
     float* MB = LB + 16;              // [16]      M'
     float* RB = MB + 16;              // [16]      R
@@ -453,12 +459,7 @@ __device__ __forceinline__ void tok_far(const KParams& p, float* farp, int fbk, 
     const float Mo = mz[bj], Zo = mz[m + bj];
     const f4 ke = *reinterpret_cast<const f4*>(p.ring_k + ((int64_t)g * p.W + c.head0) * D + c4);
     const float ve = p.ring_v[((int64_t)g * p.W + c.head0) * D + min(tid, D - 1)];
-    // LDS: accumulators, mu, evicted value
-#pragma unroll
-    for (int u = 0; u < NTH; ++u) {
-        const int e = tid + u * TOK_THREADS;
-        if (e < TOK_BMAX * (D / 4)) *reinterpret_cast<f4*>(TH + e * 4) = e < nb * (D / 4) ? tv[u] : z4;
-    }
+    // LDS: mu, evicted value (the accumulators stay in registers)
 #pragma unroll
     for (int u = 0; u < NMU; ++u) {
         const int e = tid + u * TOK_THREADS;
@@ -507,7 +508,7 @@ __device__ __forceinline__ void tok_far(const KParams& p, float* farp, int fbk, 
     if (wave == 1) {
         const float f = lane < m ? EA[lane] : -INFINITY;
         const float fmax = wmax(f);
-        if (lane < m) EA[lane] = exp2f(f - fmax);
+        EA[lane] = lane < m ? ex2(f - fmax) : 0.f;
         if (lane == 0) RED[0] = fmax;
     }
     __syncthreads();
@@ -522,12 +523,12 @@ __device__ __forceinline__ void tok_far(const KParams& p, float* farp, int fbk, 
     {
         const int j = tid >> 4, qq = tid & 15;
         float u = 0.f;
-        if (j < nb)
-            for (int a = qq; a < m; a += 16) u += EA[a] * MU[a * TOK_BMAX + j];
+#pragma unroll
+        for (int a = qq; a < 64; a += 16) u += EA[a] * MU[a * TOK_BMAX + min(j, TOK_BMAX - 1)];   // zeros past m
         u = sum16(u);
         if (qq == 0 && j < nb) {
             if (p.rect) u = fmaxf(u, 0.f);
-            GB[j] = u * exp2f(fmax + MB[j] * TOK_LOG2E - cl);
+            GB[j] = u * ex2(fmax + MB[j] * TOK_LOG2E - cl);
         }
     }
     __syncthreads();
@@ -538,19 +539,28 @@ __device__ __forceinline__ void tok_far(const KParams& p, float* farp, int fbk, 
             rec[1] = dd;
         }
     }
-    // Theta' = R Theta + x v_e (written back) and N = sum_b gain_b Theta'_b
-    float* th = p.theta + ((int64_t)gh * m + b0) * D;
-    for (int t = tid; t < D; t += TOK_THREADS) {
-        float acc = 0.f;
-        for (int j = 0; j < nb; ++j) {
-            float x = TH[j * D + t];
+    // Theta' = R Theta + x v_e (written back) and N = sum_b gain_b Theta'_b:
+    // thread (j, cc) holds columns 4cc .. 4cc+3 of accumulator b0 + j
+    {
+        const int j = tid / C4, cc = tid % C4;
+        f4 y[1] = {z4};
+        if (tid < TOK_BMAX * C4 && j < nb) {
+            f4 x = tv[0];
             if (r.full) {
-                x = x * RB[j] + XB[j] * VE[t];
-                th[(int64_t)j * D + t] = x;
+                x = x * RB[j] + XB[j] * *reinterpret_cast<const f4*>(VE + cc * 4);
+                *reinterpret_cast<f4*>(p.theta + ((int64_t)gh * m + b0 + j) * D + cc * 4) = x;
             }
-            acc += GB[j] * x;
+            y[0] = GB[j] * x;
         }
-        rec[TOK_V0 + t] = acc;
+        rows_sum<ilog2(C4)>(y);   // over the accumulators of the wave
+        if (lane < C4) *reinterpret_cast<f4*>(NS + (int64_t)wave * D + cc * 4) = y[0];
+        __syncthreads();
+        if (tid < C4) {
+            f4 a = *reinterpret_cast<const f4*>(NS + tid * 4);
+#pragma unroll
+            for (int w = 1; w < TOK_THREADS / 64; ++w) a += *reinterpret_cast<const f4*>(NS + (int64_t)w * D + tid * 4);
+            *reinterpret_cast<f4*>(rec + TOK_V0 + tid * 4) = a;
+        }
     }
 }
 
@@ -579,7 +589,7 @@ __global__ __launch_bounds__(TOK_THREADS) void k_tok_part(KParams p, float* part
 __device__ __forceinline__ void merge2(float& m, float& l, f4& a, float m2, float l2, f4 a2)
 {
     const float mn = fmaxf(m, m2);
-    const float w1 = m == -INFINITY ? 0.f : exp2f(m - mn), w2 = m2 == -INFINITY ? 0.f : exp2f(m2 - mn);
+    const float w1 = m == -INFINITY ? 0.f : ex2(m - mn), w2 = m2 == -INFINITY ? 0.f : ex2(m2 - mn);
     l = l * w1 + l2 * w2;
     a = a * w1 + a2 * w2;
     m = mn;
@@ -649,12 +659,12 @@ __global__ __launch_bounds__(TOK_MT) void k_tok_merge(KParams p, const float* pa
         }
         // no early exit when every record is empty: the loads stay unconditional
         const float bx = bm == -INFINITY ? 0.f : bm;
-        const float sc = mrun == -INFINITY ? 0.f : exp2f(mrun - bx);
+        const float sc = mrun == -INFINITY ? 0.f : ex2(mrun - bx);
         acc *= sc;
         lrun *= sc;
 #pragma unroll
         for (int u = 0; u < TOK_MB; ++u) {
-            const float w = ms[u] == -INFINITY ? 0.f : exp2f(ms[u] - bx);
+            const float w = ms[u] == -INFINITY ? 0.f : ex2(ms[u] - bx);
             acc += w * xs[u];
             lrun += w * hd[u].y;
         }
@@ -698,7 +708,7 @@ __global__ __launch_bounds__(TOK_MT) void k_tok_merge(KParams p, const float* pa
         float dfar = 0.f;
 #pragma unroll
         for (int j = NW; j < NW + TOK_FB; ++j)
-            dfar += sm[j] == -INFINITY ? 0.f : sl[j] * exp2f(sm[j] - fm);
+            dfar += sm[j] == -INFINITY ? 0.f : sl[j] * ex2(sm[j] - fm);
         const bool have = fm != -INFINITY && dfar >= 0.f;   // else the far part is dropped
 #pragma unroll
         for (int j = NW; j < NW + TOK_FB; ++j)
@@ -710,7 +720,7 @@ __global__ __launch_bounds__(TOK_MT) void k_tok_merge(KParams p, const float* pa
         f4 num = z4;
 #pragma unroll
         for (int q = 0; q < NW + TOK_FB; ++q) {
-            const float w = sm[q] == -INFINITY ? 0.f : exp2f(sm[q] - cm);
+            const float w = sm[q] == -INFINITY ? 0.f : ex2(sm[q] - cm);
             den += w * sl[q];
             num += w * sa[q];
         }
@@ -733,7 +743,7 @@ template <int D>
 static hipError_t launch_two(const KParams& p, float* part, int nsplit, hipStream_t st)
 {
     const size_t lds_near = sizeof(float) * ((size_t)p.H * TOK_KEYS + 32 + (size_t)(TOK_THREADS / 64) * 4 * D);
-    const size_t lds_far = sizeof(float) * ((size_t)TOK_BMAX * D + 64 * TOK_BMAX + D + 64 + 6 * 16 + 4);
+    const size_t lds_far = sizeof(float) * (64 * TOK_BMAX + D + (size_t)(TOK_THREADS / 64) * D + 64 + 6 * 16 + 4);
     const size_t lds = lds_near > lds_far ? lds_near : lds_far;   // <= 21 KiB
     hipLaunchKernelGGL(k_tok_part<D>, dim3(p.G * nsplit + p.nh * TOK_FB), dim3(TOK_THREADS), lds, st, p, part,
                        nsplit);
