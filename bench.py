@@ -72,6 +72,56 @@ def far_flops(cfg, T, len0=0, nfar0=0):
     return fe, fc, ro
 
 
+def attend_bytes(cfg, T, len0=0):
+    """Algorithmic HBM bytes of the near-attention + far-readout kernel over
+    T rows, each input counted once per 64-row sub-chunk: the sinks and the
+    ring rows it starts from, the chunk's own k and v, q in and out written,
+    and the far readout's inputs (Theta before the sub-chunk, the exp-mass
+    and prefix planes, and the per-landmark max, rescale and mass)."""
+    G, H, d, dv, m, ns = cfg.G, cfg.H, cfg.d, cfg.dv, cfg.m, cfg.ns
+    nh = G * H
+    f = 0
+    for g in range(G):
+        w = cfg.window(g)
+        ln = len0
+        for r0 in range(0, T, 64):
+            k = min(64, T - r0)
+            f += (ns + ln) * (d + dv) + k * (d + dv)
+            ln = min(w, ln + k)
+    for r0 in range(0, T, 64):
+        k = min(64, T - r0)
+        f += k * nh * (d + dv) + nh * m * (dv + 2 * k + 3)
+    return 4 * f
+
+
+def attend_counters(launch_bytes):
+    """HBM traffic of one attend launch from the committed counter summary,
+    or None when the kernel's source has changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "attend_maxwin_counters.md")
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    kv = {}
+    for line in text.splitlines():
+        if " = " in line:
+            k, v = line.split(" = ", 1)
+            kv[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in ("attend.hip", "swl_internal.h"):
+        with open(os.path.join(ROOT, "sink_window_landmark_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if kv.get("source_sha256") != h.hexdigest():
+        return None
+    read = float(kv["fetch_kib_per_launch"]) * float(kv["fetch_factor"]) * 1024
+    write = float(kv["write_kib_per_launch"]) * float(kv["write_factor"]) * 1024
+    return dict(bytes=read + write, read_bytes=read, write_bytes=write,
+                vs_algorithmic=(read + write) / launch_bytes,
+                source="profiles/attend_maxwin_counters.md (rocprofv3 FETCH_SIZE and WRITE_SIZE, "
+                       "scaled by a 256 MiB copy)")
+
+
 def decode_bytes(cfg):
     """Algorithmic HBM bytes of one decode token at a full window: the
     group's sinks and window K/V, the far skeleton (k~, q~, mu, M/Z, Theta
@@ -143,10 +193,12 @@ def run_gpu(args, cfg):
     near_ms = stages["attend"]
     near_launch_ms = float(np.mean(near_ms))
     near_step_flops = near_flops(cfg, T)
-    launches_per_step = len(near_ms) / args.steps
-    near_flops_per_launch = near_step_flops / launches_per_step
-    achieved = near_flops_per_launch / (near_launch_ms * 1e-3) / 1e12
     fe, fc, ro = far_flops(cfg, T)
+    launches_per_step = len(near_ms) / args.steps
+    # the attend kernel computes the near part and the far readout
+    near_flops_per_launch = (near_step_flops + ro) / launches_per_step
+    achieved = near_flops_per_launch / (near_launch_ms * 1e-3) / 1e12
+    near_bytes_per_launch = attend_bytes(cfg, T) / launches_per_step
     step_flops = near_step_flops + fe + fc + ro
 
     res = dict(
@@ -155,7 +207,8 @@ def run_gpu(args, cfg):
         wall_s=wall,
         stages_ms_per_step={n: float(np.sum(x)) / args.steps for n, x in stages.items()},
         near=dict(avg_launch_ms=near_launch_ms, launches_per_step=launches_per_step,
-                  flops_per_launch=near_flops_per_launch, achieved_tflops=achieved),
+                  flops_per_launch=near_flops_per_launch, achieved_tflops=achieved,
+                  bytes_per_launch=near_bytes_per_launch),
         step_flops=step_flops,
         step_tflops=step_flops / (ms_per_step * 1e-3) / 1e12,
     )
@@ -345,11 +398,16 @@ def main():
                      "unit": "TFLOP/s", "frac": near["achieved_tflops"] / MFMA_FP32_PEAK_TFLOPS,
                      "traffic": None,
                      "avg_launch_ms": near["avg_launch_ms"],
-                     "flops_per_launch": near["flops_per_launch"]},
+                     "flops_per_launch": near["flops_per_launch"],
+                     "algorithmic_bytes_per_launch": near["bytes_per_launch"]},
         "step": {"algorithmic_flops": res["step_flops"], "tflops": res["step_tflops"],
                  "frac_mfma_peak": res["step_tflops"] / MFMA_FP32_PEAK_TFLOPS,
                  "stages_ms": res["stages_ms_per_step"]},
     }
+    tr = attend_counters(near["bytes_per_launch"])
+    if tr is not None:
+        line["roofline"]["traffic"] = tr["bytes"]
+        line["roofline"]["traffic_detail"] = tr
     if "decode" in res:
         line["decode"] = res["decode"]
     if "chunk_api_rows_per_s" in res:
