@@ -17,7 +17,7 @@
  * Geometry (swl_geom): G KV groups, H query heads per group (nh = G*H,
  * query head gh = g*H + h), m landmarks, W ring stride (the widest group
  * window), ns sinks, d key width, dv value width, scale (usually 1/sqrt(d)),
- * rect (1: clamp u_b at 0).  Supported: d == dv in {8, 16, 32, 64, 128},
+ * rect (1: clamp u_b at 0).  Supported: d == dv in {8, 16, 32, 64, 128, 256},
  * 1 <= m <= 64, 1 <= H <= 16, 1 <= G <= 64, 0 <= ns <= 256, 1 <= W <= 65536.
  *
  * Device arrays (swl_state; all row-major, fp32 unless noted):

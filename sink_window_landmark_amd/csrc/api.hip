@@ -21,7 +21,7 @@ static bool geom_ok(const swl_geom* g)
     if (g->W < 1 || g->W > 65536) return false;
     if (g->ns < 0 || g->ns > 256) return false;
     if (g->d != g->dv) return false;
-    if (!(g->d == 8 || g->d == 16 || g->d == 32 || g->d == 64 || g->d == 128)) return false;
+    if (!(g->d == 8 || g->d == 16 || g->d == 32 || g->d == 64 || g->d == 128 || g->d == 256)) return false;
     if (!isfinite(g->scale)) return false;
     if (g->rect != 0 && g->rect != 1) return false;
     return true;

@@ -16,7 +16,8 @@
 //
 // The near part never depends on the far field, so every sub-chunk of a call
 // is computed in one launch: one block per (sub-chunk, KV group, group of up
-// to 4 query heads), two waves per head, each wave owning 32 query rows.
+// to 4 query heads; 2 at d = 256), two waves per head, each wave owning 32
+// query rows.
 // The block's keys (the sinks, then the band of positions its rows reach)
 // stream through LDS in tiles of 32 keys shared by all heads of the group
 // (the GQA reuse of the pages' Metal and Dory kernels).
@@ -39,8 +40,16 @@ namespace swl {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-constexpr int AT_THREADS = 512;
 constexpr int KT = 32;  // keys per tile
+
+// Block shape per head width: two waves per head, up to four heads per block
+// (two at d = 256, so that each wave may use a whole SIMD's registers:
+// Q^T and O^T alone take 256 of them).
+template <int D>
+struct AtCfg {
+    static constexpr int HPB = D > 128 ? 2 : 4;   // heads per block
+    static constexpr int THREADS = HPB * 2 * 64;
+};
 
 __device__ __forceinline__ floatx16 mfma32(float a, float b, floatx16 c)
 {
@@ -64,7 +73,18 @@ __device__ __forceinline__ void zero16(floatx16& x)
 template <int D, int NB>
 __device__ __forceinline__ void pv_step(floatx16 (&O)[NB], const float* row, int ln, float b)
 {
-    if constexpr (NB == 4) {
+    if constexpr (NB == 8) {
+        const float4 a = *reinterpret_cast<const float4*>(row + 8 * ln);
+        const float4 c = *reinterpret_cast<const float4*>(row + 8 * ln + 4);
+        O[0] = mfma32(a.x, b, O[0]);
+        O[1] = mfma32(a.y, b, O[1]);
+        O[2] = mfma32(a.z, b, O[2]);
+        O[3] = mfma32(a.w, b, O[3]);
+        O[4] = mfma32(c.x, b, O[4]);
+        O[5] = mfma32(c.y, b, O[5]);
+        O[6] = mfma32(c.z, b, O[6]);
+        O[7] = mfma32(c.w, b, O[7]);
+    } else if constexpr (NB == 4) {
         const float4 a = *reinterpret_cast<const float4*>(row + 4 * ln);
         O[0] = mfma32(a.x, b, O[0]);
         O[1] = mfma32(a.y, b, O[1]);
@@ -81,8 +101,10 @@ __device__ __forceinline__ void pv_step(floatx16 (&O)[NB], const float* row, int
 }
 
 template <int D, int MT>
-__global__ __launch_bounds__(AT_THREADS) void k_attend(KParams p)
+__global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
 {
+    constexpr int AT_THREADS = AtCfg<D>::THREADS;
+    constexpr int HPB = AtCfg<D>::HPB;
     constexpr int NB = D >= 32 ? D / 32 : 1;  // 32-column output blocks
     constexpr int LD = D + 4;                 // LDS row stride
     constexpr int F4 = KT * D / 4;            // float4 per tile matrix
@@ -95,12 +117,12 @@ __global__ __launch_bounds__(AT_THREADS) void k_attend(KParams p)
 
     // work item = (head group, group, sub-chunk), sub-chunk fastest, dealt
     // to XCDs in contiguous runs
-    const int hgroups = (p.H + 3) / 4;
+    const int hgroups = (p.H + HPB - 1) / HPB;
     const int w = xcd_work_item(blockIdx.x, p.S * p.G * hgroups);
     const int s = w % p.S, g = (w / p.S) % p.G, hgrp = w / (p.S * p.G);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int hf = lane >> 5, ln = lane & 31;
-    const int h = hgrp * 4 + (wave >> 1);
+    const int h = hgrp * HPB + (wave >> 1);
     const bool active = h < p.H;
     const int gh = g * p.H + h;
     const int r0 = s * SUB;
@@ -445,7 +467,12 @@ __global__ __launch_bounds__(AT_THREADS) void k_attend(KParams p)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int ii = kap(v, hf);
-            if constexpr (NB == 4) {
+            if constexpr (NB == 8) {
+                *reinterpret_cast<float4*>(orow + 8 * ii) =
+                    make_float4(O[0][v] * inv, O[1][v] * inv, O[2][v] * inv, O[3][v] * inv);
+                *reinterpret_cast<float4*>(orow + 8 * ii + 4) =
+                    make_float4(O[4][v] * inv, O[5][v] * inv, O[6][v] * inv, O[7][v] * inv);
+            } else if constexpr (NB == 4) {
                 *reinterpret_cast<float4*>(orow + 4 * ii) =
                     make_float4(O[0][v] * inv, O[1][v] * inv, O[2][v] * inv, O[3][v] * inv);
             } else if constexpr (NB == 2) {
@@ -460,9 +487,10 @@ __global__ __launch_bounds__(AT_THREADS) void k_attend(KParams p)
 template <int D>
 static hipError_t launch_d(const KParams& p, hipStream_t st)
 {
-    dim3 grid(p.S * p.G * ((p.H + 3) / 4));
-    if (p.m <= 32) hipLaunchKernelGGL((k_attend<D, 1>), grid, dim3(AT_THREADS), 0, st, p);
-    else hipLaunchKernelGGL((k_attend<D, 2>), grid, dim3(AT_THREADS), 0, st, p);
+    constexpr int HPB = AtCfg<D>::HPB;
+    dim3 grid(p.S * p.G * ((p.H + HPB - 1) / HPB));
+    if (p.m <= 32) hipLaunchKernelGGL((k_attend<D, 1>), grid, dim3(AtCfg<D>::THREADS), 0, st, p);
+    else hipLaunchKernelGGL((k_attend<D, 2>), grid, dim3(AtCfg<D>::THREADS), 0, st, p);
     return hipGetLastError();
 }
 
@@ -474,6 +502,7 @@ hipError_t launch_attend(const KParams& p, hipStream_t st)
     case 32: return launch_d<32>(p, st);
     case 64: return launch_d<64>(p, st);
     case 128: return launch_d<128>(p, st);
+    case 256: return launch_d<256>(p, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -330,6 +330,7 @@ hipError_t launch_far_score(const KParams& p, hipStream_t st)
     case 32: launch_fs<32>(p, st); break;
     case 64: launch_fs<64>(p, st); break;
     case 128: launch_fs<128>(p, st); break;
+    case 256: launch_fs<256>(p, st); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -356,6 +357,7 @@ hipError_t launch_dtheta(const KParams& p, hipStream_t st)
     case 32: launch_dt<32>(p, st); break;
     case 64: launch_dt<64>(p, st); break;
     case 128: launch_dt<128>(p, st); break;
+    case 256: launch_dt<256>(p, st); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -396,7 +396,7 @@ __device__ __forceinline__ void tok_far(const KParams& p, float* farp, int fbk, 
     constexpr int L = D / 4, RPP = TOK_THREADS / L;
     constexpr int NK = RPP >= 64 ? 1 : 64 / RPP;                 // landmark-key passes (m <= 64)
     constexpr int NQ = RPP >= TOK_BMAX ? 1 : TOK_BMAX / RPP;     // landmark-query passes
-    constexpr int NTH = TOK_BMAX * (D / 4) / TOK_THREADS > 0 ? TOK_BMAX * (D / 4) / TOK_THREADS : 1;
+    constexpr int NTH = (TOK_BMAX * (D / 4) + TOK_THREADS - 1) / TOK_THREADS;   // accumulator pieces per thread
     constexpr int NMU = 64 * TOK_BMAX / TOK_THREADS;
     using LRK = LaneReduce<NK, L>;
     using LRQ = LaneReduce<NQ, L>;
@@ -414,7 +414,7 @@ __device__ __forceinline__ void tok_far(const KParams& p, float* farp, int fbk, 
         return;
     }
     constexpr int C4 = D / 4;
-    static_assert(TOK_BMAX * C4 <= TOK_THREADS, "one accumulator piece per thread");
+    static_assert(TOK_THREADS % C4 == 0, "a thread's accumulator pieces share one column");
     float* MU = lds;                  // [64][16]  mu[a][b0 + j]
     float* VE = MU + 64 * TOK_BMAX;   // [D]       evicted value
     float* NS = VE + D;               // [waves][D] value sums of each wave
@@ -540,17 +540,22 @@ __device__ __forceinline__ void tok_far(const KParams& p, float* farp, int fbk, 
         }
     }
     // Theta' = R Theta + x v_e (written back) and N = sum_b gain_b Theta'_b:
-    // thread (j, cc) holds columns 4cc .. 4cc+3 of accumulator b0 + j
+    // thread (j, cc) holds columns 4cc .. 4cc+3 of accumulator b0 + j (two
+    // such pieces at d = 256)
     {
-        const int j = tid / C4, cc = tid % C4;
+        const int cc = tid % C4;   // the same column for every piece of this thread
         f4 y[1] = {z4};
-        if (tid < TOK_BMAX * C4 && j < nb) {
-            f4 x = tv[0];
-            if (r.full) {
-                x = x * RB[j] + XB[j] * *reinterpret_cast<const f4*>(VE + cc * 4);
-                *reinterpret_cast<f4*>(p.theta + ((int64_t)gh * m + b0 + j) * D + cc * 4) = x;
+#pragma unroll
+        for (int u = 0; u < NTH; ++u) {
+            const int e = tid + u * TOK_THREADS, j = e / C4;
+            if (e < TOK_BMAX * C4 && j < nb) {
+                f4 x = tv[u];
+                if (r.full) {
+                    x = x * RB[j] + XB[j] * *reinterpret_cast<const f4*>(VE + cc * 4);
+                    *reinterpret_cast<f4*>(p.theta + ((int64_t)gh * m + b0 + j) * D + cc * 4) = x;
+                }
+                y[0] += GB[j] * x;
             }
-            y[0] = GB[j] * x;
         }
         rows_sum<ilog2(C4)>(y);   // over the accumulators of the wave
         if (lane < C4) *reinterpret_cast<f4*>(NS + (int64_t)wave * D + cc * 4) = y[0];
@@ -763,6 +768,7 @@ hipError_t launch_token(const KParams& p, float* part, hipStream_t st)
     case 32: return launch_two<32>(p, part, nsplit, st);
     case 64: return launch_two<64>(p, part, nsplit, st);
     case 128: return launch_two<128>(p, part, nsplit, st);
+    case 256: return launch_two<256>(p, part, nsplit, st);
     default: return hipErrorInvalidValue;
     }
 }

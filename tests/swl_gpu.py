@@ -49,7 +49,8 @@ def excess(got, want, atol=ATOL, rtol=RTOL, scale=None):
     want = np.asarray(want, np.float64)
     ref = np.abs(want) if scale is None else scale
     both_inf = np.isinf(got) & np.isinf(want) & (np.sign(got) == np.sign(want))
-    d = np.where(both_inf, 0.0, np.abs(got - want))
+    with np.errstate(invalid="ignore"):   # inf - inf where both are -inf (masked below)
+        d = np.where(both_inf, 0.0, np.abs(got - want))
     return float(np.max(d - (atol + rtol * ref))) if d.size else -1.0
 
 

@@ -63,7 +63,7 @@ def test_scratch_bytes_grows_then_caps():
 
 @pytest.mark.parametrize("bad", [dict(G=0), dict(G=65), dict(H=0), dict(H=17), dict(m=0), dict(m=65),
                                  dict(W=0), dict(ns=-1), dict(ns=257), dict(d=24, dv=24),
-                                 dict(d=64, dv=128), dict(d=256, dv=256), dict(rect=2),
+                                 dict(d=64, dv=128), dict(d=512, dv=512), dict(rect=2),
                                  dict(scale=float("nan"))])
 def test_invalid_geometry_has_no_scratch(bad):
     assert swl.swl_scratch_bytes(_geom(**bad), 64) == 0

@@ -122,6 +122,31 @@ def test_reference_shapes(w, w2, chunks):
     check_state(read_state(st), orc)
 
 
+@pytest.mark.parametrize("w,w2,chunks,tokens", [(128, 512, [64, 64], 0), (128, 128, [5], 1)])
+def test_reference_production_head(w, w2, chunks, tokens):
+    """The pages' production head geometry (d = dv = 256, m = 32, 4 sinks, 6
+    query heads, a 300-row prompt), continued through attend_chunk + commit
+    and, in the second case, a token after a 5-row verify chunk."""
+    banner(f"production head d=256 w={w}/{w2} chunks={chunks} tokens={tokens}")
+    d, m, ns, H, t0 = 256, 32, 4, 6, 300
+    cfg = synth.Config("prod", G=2, H=H, d=d, dv=d, ns=ns, W=max(w, w2), m=m, rows=t0,
+                       windows=(w, w2))
+    host = synth.make_state(cfg)
+    n = t0 + sum(chunks) + tokens
+    q, k, v = synth.jit_rows(2, H, d, 0, n)
+    orc = oracle.from_config(cfg, host)
+    st = _state(cfg, host)
+    got0 = _prefill(cfg, st, q[:t0], k[:t0], v[:t0], poison=True)
+    check_out(got0, orc.step(q[:t0], k[:t0], v[:t0]), "prompt")
+    r0 = t0 + sum(chunks)
+    got1 = _chunks(cfg, st, q[t0:r0], k[t0:r0], v[t0:r0], chunks, poison=True)
+    check_out(got1, orc.step(q[t0:r0], k[t0:r0], v[t0:r0]), f"chunks {chunks}")
+    if tokens:
+        got2 = _tokens(cfg, st, q[r0:], k[r0:], v[r0:])
+        check_out(got2, orc.step(q[r0:], k[r0:], v[r0:]), "token")
+    check_state(read_state(st), orc)
+
+
 # -- the small layer, every row ------------------------------------------------------
 
 def test_small_full():
