@@ -152,6 +152,19 @@ int swl_prefill_traced(const swl_geom* geom, const swl_state* st,
                        float* out, void* scratch, size_t scratch_bytes, void* stream,
                        swl_stage_fn fn, void* user);
 
+/* The state after `rows` rows (rows >= 0; 0 is a no-op) whose keys and
+ * values are k [rows][G][d] and v [rows][G][dv], without their attention:
+ * far_e and the commit of every consecutive 64-row sub-chunk (o1c.rs
+ * spec_commit, which moves a layer over the accepted rows of a verify).
+ * A verify is a swl_attend_chunk over up to 64 speculative rows, which
+ * leaves the state as it was; committing the first r of them with this
+ * call gives the state of r serial steps, the far max taken over the
+ * accepted rows only.  The same state as swl_prefill over the rows, up to
+ * rounding.  scratch: swl_scratch_bytes(geom, rows) bytes. */
+int swl_commit_rows(const swl_geom* geom, const swl_state* st,
+                    const float* k, const float* v, int64_t rows,
+                    void* scratch, size_t scratch_bytes, void* stream);
+
 /* One row, attended and committed: a sub-chunk of one row (o1c.rs
  * encode_tok) in two launches.  The row's keys (sinks, then the window after
  * the push) are split over blocks of 64 keys per group, each writing a

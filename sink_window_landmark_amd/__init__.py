@@ -25,7 +25,8 @@ SUB = 64
 
 # Entry points declared by include/swl.h.
 EXPORTS = ("swl_scratch_bytes", "swl_init_state", "swl_attend_chunk", "swl_commit",
-           "swl_prefill", "swl_prefill_traced", "swl_attend_token", "swl_status_str")
+           "swl_prefill", "swl_prefill_traced", "swl_commit_rows", "swl_attend_token",
+           "swl_status_str")
 
 # Stage ids of swl_stage_fn (enum swl_stage).
 STAGES = ("far_score", "far_scan", "dtheta", "theta_scan", "attend", "ring", "meta")
@@ -76,6 +77,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.swl_prefill_traced.restype = ctypes.c_int
     lib.swl_prefill_traced.argtypes = [G, S, _P, _P, _P, ctypes.c_int64, _P, _P, ctypes.c_size_t,
                                        _P, STAGE_FN, _P]
+    lib.swl_commit_rows.restype = ctypes.c_int
+    lib.swl_commit_rows.argtypes = [G, S, _P, _P, ctypes.c_int64, _P, ctypes.c_size_t, _P]
     lib.swl_attend_token.restype = ctypes.c_int
     lib.swl_attend_token.argtypes = [G, S, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.swl_status_str.restype = ctypes.c_char_p
@@ -251,6 +254,17 @@ def swl_commit(state: LayerState, k, v, scratch, stream=None):
         ctypes.byref(state.geom.c()), ctypes.byref(state.c()), k.data_ptr(), v.data_ptr(), rows,
         scratch.data_ptr(), scratch.numel(), _stream(stream))
     _raise(rc, "swl_commit")
+
+
+def swl_commit_rows(state: LayerState, k, v, scratch, stream=None):
+    """The state after the rows of k, v without their attention (the accepted
+    rows of a verify)."""
+    rows = k.shape[0]
+    _rows_args(state, None, k, v, None, rows)
+    rc = load_library().swl_commit_rows(
+        ctypes.byref(state.geom.c()), ctypes.byref(state.c()), k.data_ptr(), v.data_ptr(), rows,
+        scratch.data_ptr(), scratch.numel(), _stream(stream))
+    _raise(rc, "swl_commit_rows")
 
 
 def swl_prefill(state: LayerState, q, k, v, out, scratch, stream=None):

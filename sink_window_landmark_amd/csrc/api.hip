@@ -172,14 +172,19 @@ int swl_commit(const swl_geom* geom, const swl_state* st, const float* k, const 
     return run_commit(p, static_cast<hipStream_t>(stream));
 }
 
-int swl_prefill_traced(const swl_geom* geom, const swl_state* st, const float* q,
-                       const float* k, const float* v, int64_t rows, float* out, void* scratch,
-                       size_t scratch_bytes, void* stream, swl_stage_fn fn, void* user)
+}  // extern "C"
+
+// Consecutive 64-row sub-chunks of `rows` rows, batched into passes of up
+// to PASS_SUBS sub-chunks: far_e, far commit, (attention,) ring commit and
+// meta of each pass.  Without `attend`, q and out are not used.
+static int run_rows(const swl_geom* geom, const swl_state* st, const float* q, const float* k,
+                    const float* v, int64_t rows, float* out, void* scratch, size_t scratch_bytes,
+                    void* stream, swl_stage_fn fn, void* user, bool attend)
 {
     if (!geom_ok(geom) || !state_ok(geom, st)) return SWL_EINVAL;
     if (rows < 0) return SWL_EINVAL;
     if (rows == 0) return SWL_OK;
-    if (!q || !k || !v || !out || !scratch) return SWL_EINVAL;
+    if (!k || !v || !scratch || (attend && (!q || !out))) return SWL_EINVAL;
     const int S_max = subs_for_rows(rows);
     if (scratch_bytes < carve(geom, S_max).total) return SWL_EINVAL;
     hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -195,10 +200,12 @@ int swl_prefill_traced(const swl_geom* geom, const swl_state* st, const float* q
     for (int64_t done = 0; done < rows;) {
         const int64_t T = rows - done < cap ? rows - done : cap;
         KParams p = make_params(geom, st);
-        p.q = q + done * nh * geom->d;
+        if (attend) {
+            p.q = q + done * nh * geom->d;
+            p.out = out + done * nh * geom->dv;
+        }
         p.k = k + done * geom->G * geom->d;
         p.v = v + done * geom->G * geom->dv;
-        p.out = out + done * nh * geom->dv;
         p.T = (int)T;
         p.S = (int)((T + SUB - 1) / SUB);
         set_scratch(p, geom, scratch, S_max);
@@ -208,7 +215,7 @@ int swl_prefill_traced(const swl_geom* geom, const swl_state* st, const float* q
         SWL_STAGE(SWL_STAGE_FAR_SCAN, launch_far_scan(p, hs));
         SWL_STAGE(SWL_STAGE_DTHETA, launch_dtheta(p, hs));
         SWL_STAGE(SWL_STAGE_THETA_SCAN, launch_theta_scan(p, true, hs));
-        SWL_STAGE(SWL_STAGE_ATTEND, launch_attend(p, hs));
+        if (attend) SWL_STAGE(SWL_STAGE_ATTEND, launch_attend(p, hs));
         SWL_STAGE(SWL_STAGE_RING, launch_ring_commit(p, hs));
         SWL_STAGE(SWL_STAGE_META, launch_meta(p, hs));
         done += T;
@@ -217,12 +224,28 @@ int swl_prefill_traced(const swl_geom* geom, const swl_state* st, const float* q
     return SWL_OK;
 }
 
+extern "C" {
+
+int swl_prefill_traced(const swl_geom* geom, const swl_state* st, const float* q,
+                       const float* k, const float* v, int64_t rows, float* out, void* scratch,
+                       size_t scratch_bytes, void* stream, swl_stage_fn fn, void* user)
+{
+    return run_rows(geom, st, q, k, v, rows, out, scratch, scratch_bytes, stream, fn, user, true);
+}
+
 int swl_prefill(const swl_geom* geom, const swl_state* st, const float* q, const float* k,
                 const float* v, int64_t rows, float* out, void* scratch, size_t scratch_bytes,
                 void* stream)
 {
-    return swl_prefill_traced(geom, st, q, k, v, rows, out, scratch, scratch_bytes, stream,
-                              nullptr, nullptr);
+    return run_rows(geom, st, q, k, v, rows, out, scratch, scratch_bytes, stream, nullptr,
+                    nullptr, true);
+}
+
+int swl_commit_rows(const swl_geom* geom, const swl_state* st, const float* k, const float* v,
+                    int64_t rows, void* scratch, size_t scratch_bytes, void* stream)
+{
+    return run_rows(geom, st, nullptr, k, v, rows, nullptr, scratch, scratch_bytes, stream,
+                    nullptr, nullptr, false);
 }
 
 int swl_attend_token(const swl_geom* geom, const swl_state* st, const float* q, const float* k,

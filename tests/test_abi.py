@@ -122,6 +122,14 @@ def test_calls_reject_small_scratch_and_null_pointers():
                                     FAKE, FAKE, n, None) == swl.SWL_EINVAL, f
     assert lib.swl_attend_token(ctypes.byref(g), ctypes.byref(st), FAKE, FAKE, FAKE, FAKE, FAKE,
                                 0, None) == swl.SWL_EINVAL
+    assert lib.swl_commit_rows(ctypes.byref(g), ctypes.byref(st), FAKE, FAKE, -1, FAKE, n_big,
+                               None) == swl.SWL_EINVAL
+    assert lib.swl_commit_rows(ctypes.byref(g), ctypes.byref(st), FAKE, FAKE, 1000, FAKE,
+                               n_big - 256, None) == swl.SWL_EINVAL
+    assert lib.swl_commit_rows(ctypes.byref(g), ctypes.byref(st), None, FAKE, 10, FAKE, n_big,
+                               None) == swl.SWL_EINVAL
+    assert lib.swl_commit_rows(ctypes.byref(g), ctypes.byref(st), None, None, 0, None, 0,
+                               None) == swl.SWL_OK
 
 
 @needs_no_gpu

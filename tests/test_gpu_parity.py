@@ -147,6 +147,67 @@ def test_reference_production_head(w, w2, chunks, tokens):
     check_state(read_state(st), orc)
 
 
+# -- verify: speculative rows, then a commit of the accepted ones --------------------
+
+@pytest.mark.parametrize("spec,accepted", [(64, 37), (64, 64), (20, 1)])
+def test_verify_then_commit_accepted_rows(spec, accepted):
+    """attend_chunk over speculative rows leaves the state as it was; the
+    accepted rows are then committed with swl_commit_rows (far_e over them
+    only), and the layer continues from that state."""
+    banner(f"verify spec={spec} accepted={accepted}")
+    cfg = synth.Config("verify", G=2, H=4, d=64, dv=64, ns=4, W=128, m=16, rows=300,
+                       windows=(96, 128), rope=True, landmark_scale=0.125)
+    host = synth.make_state(cfg)
+    t0, nxt = 300, 80
+    q, k, v = synth.rows(cfg, 0, t0 + spec + nxt)
+    st = _state(cfg, host)
+    _prefill(cfg, st, q[:t0], k[:t0], v[:t0])
+    before = read_state(st)
+    sp = slice(t0, t0 + spec)
+    t = torch()
+    out = t.empty((spec, cfg.nh, cfg.dv), dtype=t.float32, device="cuda")
+    scratch = swl.alloc_scratch(st.geom, 64)
+    kd, vd = dev(k[sp]), dev(v[sp])
+    swl.swl_attend_chunk(st, dev(q[sp]), kd, vd, out, scratch)
+    t.cuda.synchronize()
+    after = read_state(st)
+    for f in before:
+        assert np.array_equal(before[f], after[f], equal_nan=True), f"attend_chunk changed {f}"
+    spec_orc = oracle.from_config(cfg, host)
+    spec_orc.step(q[:t0], k[:t0], v[:t0], want=np.zeros(t0, bool))
+    check_out(out.cpu().numpy(), spec_orc.step(q[sp], k[sp], v[sp]), "speculative rows")
+    # accept the first rows: the state of that many serial steps
+    swl.swl_commit_rows(st, kd[:accepted].contiguous(), vd[:accepted].contiguous(),
+                        swl.alloc_scratch(st.geom, accepted))
+    orc = oracle.from_config(cfg, host)
+    orc.step(q[:t0], k[:t0], v[:t0], want=np.zeros(t0, bool))
+    orc.step(q[t0:t0 + accepted], k[t0:t0 + accepted], v[t0:t0 + accepted],
+             want=np.zeros(accepted, bool))
+    check_state(read_state(st), orc)
+    # the layer goes on with new rows
+    nx = slice(t0 + spec, t0 + spec + nxt)
+    got = _prefill(cfg, st, q[nx], k[nx], v[nx])
+    check_out(got, orc.step(q[nx], k[nx], v[nx]), "rows after the commit")
+    check_state(read_state(st), orc)
+
+
+def test_commit_rows_matches_prefill_state():
+    """swl_commit_rows over several sub-chunks gives prefill's state."""
+    banner("commit_rows over 150 rows vs prefill")
+    cfg = synth.SMALL.replace(rows=500, W=256, m=16)
+    host = synth.make_state(cfg)
+    q, k, v = synth.rows(cfg, 0, 500)
+    a = _state(cfg, host)
+    _prefill(cfg, a, q[:350], k[:350], v[:350])
+    b = a.clone()
+    swl.swl_commit_rows(a, dev(k[350:]), dev(v[350:]), swl.alloc_scratch(a.geom, 150))
+    _prefill(cfg, b, q[350:], k[350:], v[350:])
+    orc = oracle.from_config(cfg, host)
+    orc.step(q, k, v, want=np.zeros(500, bool))
+    check_state(read_state(a), orc)
+    check_state(read_state(b), orc)
+
+
 # -- the small layer, every row ------------------------------------------------------
 
 def test_small_full():
