@@ -165,6 +165,23 @@ int swl_commit_rows(const swl_geom* geom, const swl_state* st,
                     const float* k, const float* v, int64_t rows,
                     void* scratch, size_t scratch_bytes, void* stream);
 
+/* A layer sealed from `rows` exact rows (dory.rs seal, with the landmarks,
+ * mu and the sinks already in the state): the empty state (as
+ * swl_init_state, with the same `windows`), then swl_commit_rows over the
+ * rows, so the ring holds the last min(rows, w_g) of them and M, Z, Theta
+ * summarise the rows before those.  scratch: swl_scratch_bytes(geom, rows)
+ * bytes (none for rows == 0). */
+int swl_seal(const swl_geom* geom, const swl_state* st, const uint32_t* windows,
+             const float* k, const float* v, int64_t rows,
+             void* scratch, size_t scratch_bytes, void* stream);
+
+/* The bookkeeping of the last push undone in every group (dory.rs
+ * dory_o1_back, for models that run a layer several times per row): a full
+ * window moves its head back one slot and its far count down by one, a
+ * partial one loses its newest row; an empty window is left alone.  The
+ * ring's rows and M, Z, Theta are not restored. */
+int swl_rewind(const swl_geom* geom, const swl_state* st, void* stream);
+
 /* One row, attended and committed: a sub-chunk of one row (o1c.rs
  * encode_tok) in two launches.  The row's keys (sinks, then the window after
  * the push) are split over blocks of 64 keys per group, each writing a

@@ -172,6 +172,22 @@ class SerialOracle:
         return out
 
     # -- state in the GPU library's layouts ---------------------------------
+    def rewind(self) -> None:
+        """Undo the bookkeeping of the last push of every group, as the
+        pages' ``dory_o1_back`` (cortiq-engine 0.8.77 src/gpu_wgpu/dory.rs)
+        does: with a full window the head steps back one slot and the far
+        count drops by one, otherwise the window loses its newest row.  Ring
+        rows and M, Z, Theta stay as they are.  Reading for an empty window
+        (the page does not guard it): nothing changes."""
+        for p in self.parts:
+            wg = self.windows[p["g"]]
+            ln, hd, nf = (int(x) for x in p["meta"])
+            if ln == wg:
+                p["meta"][1] = (hd + wg - 1) % wg
+                p["meta"][2] = nf - 1
+            elif ln > 0:
+                p["meta"][0] = ln - 1
+
     def meta(self) -> np.ndarray:
         out = np.zeros((self.G, 4), np.uint32)
         for p in self.parts:

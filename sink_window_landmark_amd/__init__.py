@@ -25,8 +25,8 @@ SUB = 64
 
 # Entry points declared by include/swl.h.
 EXPORTS = ("swl_scratch_bytes", "swl_init_state", "swl_attend_chunk", "swl_commit",
-           "swl_prefill", "swl_prefill_traced", "swl_commit_rows", "swl_attend_token",
-           "swl_status_str")
+           "swl_prefill", "swl_prefill_traced", "swl_commit_rows", "swl_seal", "swl_rewind",
+           "swl_attend_token", "swl_status_str")
 
 # Stage ids of swl_stage_fn (enum swl_stage).
 STAGES = ("far_score", "far_scan", "dtheta", "theta_scan", "attend", "ring", "meta")
@@ -79,6 +79,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                        _P, STAGE_FN, _P]
     lib.swl_commit_rows.restype = ctypes.c_int
     lib.swl_commit_rows.argtypes = [G, S, _P, _P, ctypes.c_int64, _P, ctypes.c_size_t, _P]
+    lib.swl_seal.restype = ctypes.c_int
+    lib.swl_seal.argtypes = [G, S, _P, _P, _P, ctypes.c_int64, _P, ctypes.c_size_t, _P]
+    lib.swl_rewind.restype = ctypes.c_int
+    lib.swl_rewind.argtypes = [G, S, _P]
     lib.swl_attend_token.restype = ctypes.c_int
     lib.swl_attend_token.argtypes = [G, S, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.swl_status_str.restype = ctypes.c_char_p
@@ -215,14 +219,19 @@ def alloc_scratch(geom: Geom, rows: int, device="cuda"):
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def swl_init_state(state: LayerState, windows: Optional[Sequence[int]] = None, stream=None):
+def _windows_arg(state, windows):
+    """The u32 array of per-group window overrides, or None."""
+    if windows is None:
+        return None
     g = state.geom
-    arr = None
-    if windows is not None:
-        if len(windows) != g.G:
-            raise ValueError("one window override per group")
-        arr = (ctypes.c_uint32 * g.G)(*[int(w) for w in windows])
-    rc = load_library().swl_init_state(ctypes.byref(g.c()), ctypes.byref(state.c()),
+    if len(windows) != g.G:
+        raise ValueError("one window override per group")
+    return (ctypes.c_uint32 * g.G)(*[int(w) for w in windows])
+
+
+def swl_init_state(state: LayerState, windows: Optional[Sequence[int]] = None, stream=None):
+    arr = _windows_arg(state, windows)
+    rc = load_library().swl_init_state(ctypes.byref(state.geom.c()), ctypes.byref(state.c()),
                                        ctypes.cast(arr, _P) if arr is not None else None,
                                        _stream(stream))
     _raise(rc, "swl_init_state")
@@ -265,6 +274,27 @@ def swl_commit_rows(state: LayerState, k, v, scratch, stream=None):
         ctypes.byref(state.geom.c()), ctypes.byref(state.c()), k.data_ptr(), v.data_ptr(), rows,
         scratch.data_ptr(), scratch.numel(), _stream(stream))
     _raise(rc, "swl_commit_rows")
+
+
+def swl_seal(state: LayerState, k, v, scratch, windows: Optional[Sequence[int]] = None,
+             stream=None):
+    """The state sealed from the exact rows k, v (the landmarks, mu and sinks
+    already in ``state``)."""
+    rows = k.shape[0]
+    _rows_args(state, None, k, v, None, rows)
+    win = _windows_arg(state, windows)
+    rc = load_library().swl_seal(
+        ctypes.byref(state.geom.c()), ctypes.byref(state.c()),
+        ctypes.cast(win, ctypes.c_void_p) if win is not None else None,
+        k.data_ptr(), v.data_ptr(), rows, scratch.data_ptr(), scratch.numel(), _stream(stream))
+    _raise(rc, "swl_seal")
+
+
+def swl_rewind(state: LayerState, stream=None):
+    """Undo the bookkeeping of the last push in every group."""
+    rc = load_library().swl_rewind(ctypes.byref(state.geom.c()), ctypes.byref(state.c()),
+                                   _stream(stream))
+    _raise(rc, "swl_rewind")
 
 
 def swl_prefill(state: LayerState, q, k, v, out, scratch, stream=None):

@@ -248,6 +248,26 @@ int swl_commit_rows(const swl_geom* geom, const swl_state* st, const float* k, c
                     nullptr, nullptr, false);
 }
 
+int swl_seal(const swl_geom* geom, const swl_state* st, const uint32_t* windows, const float* k,
+             const float* v, int64_t rows, void* scratch, size_t scratch_bytes, void* stream)
+{
+    if (!geom_ok(geom) || !state_ok(geom, st)) return SWL_EINVAL;
+    if (rows < 0) return SWL_EINVAL;
+    if (rows > 0 && (!k || !v || !scratch || scratch_bytes < carve(geom, subs_for_rows(rows)).total))
+        return SWL_EINVAL;
+    const int rc = swl_init_state(geom, st, windows, stream);
+    if (rc != SWL_OK) return rc;
+    return swl_commit_rows(geom, st, k, v, rows, scratch, scratch_bytes, stream);
+}
+
+int swl_rewind(const swl_geom* geom, const swl_state* st, void* stream)
+{
+    if (!geom_ok(geom) || !state_ok(geom, st)) return SWL_EINVAL;
+    KParams p = make_params(geom, st);
+    SWL_TRY(launch_rewind(p, static_cast<hipStream_t>(stream)));
+    return SWL_OK;
+}
+
 int swl_attend_token(const swl_geom* geom, const swl_state* st, const float* q, const float* k,
                      const float* v, float* out, void* scratch, size_t scratch_bytes,
                      void* stream)

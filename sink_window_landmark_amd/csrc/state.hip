@@ -87,4 +87,27 @@ hipError_t launch_meta(const KParams& p, hipStream_t st)
     return hipGetLastError();
 }
 
+// The bookkeeping of one push undone, per group (dory.rs dory_o1_back): a
+// full window moves its head back one slot and gives back one far count;
+// otherwise the window is one row shorter.  The ring's rows and M, Z, Theta
+// stay as they are.  An empty window is left alone.
+__global__ void k_rewind(KParams p)
+{
+    const int g = blockIdx.x * blockDim.x + threadIdx.x;
+    if (g >= p.G) return;
+    const GMeta c = load_gmeta(p.meta, g, p.W);
+    if (c.len0 == c.wg) {
+        p.meta[4 * g + 1] = (uint32_t)((c.head0 + c.wg - 1) % c.wg);
+        p.meta[4 * g + 2] = (uint32_t)(c.nfar0 - 1);
+    } else if (c.len0 > 0) {
+        p.meta[4 * g + 0] = (uint32_t)(c.len0 - 1);
+    }
+}
+
+hipError_t launch_rewind(const KParams& p, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_rewind, dim3((p.G + 63) / 64), dim3(64), 0, st, p);
+    return hipGetLastError();
+}
+
 }  // namespace swl

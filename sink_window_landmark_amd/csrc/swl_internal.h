@@ -118,6 +118,7 @@ hipError_t launch_theta_scan(const KParams& p, bool commit, hipStream_t st);
 hipError_t launch_attend(const KParams& p, hipStream_t st);
 hipError_t launch_ring_commit(const KParams& p, hipStream_t st);
 hipError_t launch_meta(const KParams& p, hipStream_t st);
+hipError_t launch_rewind(const KParams& p, hipStream_t st);
 // one-row decode: partials, then merge + commit; `part` holds tok_part_floats()
 hipError_t launch_token(const KParams& p, float* part, hipStream_t st);
 size_t tok_part_floats(int G, int H, int dv, int ns, int W);

@@ -208,6 +208,62 @@ def test_commit_rows_matches_prefill_state():
     check_state(read_state(b), orc)
 
 
+# -- seal from exact rows, rewind one push ------------------------------------------
+
+def test_seal_from_exact_rows():
+    """swl_seal builds the state of the rows (ring = the last w_g of them,
+    M/Z/Theta over the rest) without attending them; the layer then goes on
+    as the oracle does."""
+    banner("seal 700 rows, then 100 more")
+    cfg = synth.Config("seal", G=2, H=4, d=64, dv=64, ns=4, W=256, m=16, rows=800,
+                       windows=(128, 256), rope=True, landmark_scale=0.125)
+    host = synth.make_state(cfg)
+    q, k, v = synth.rows(cfg, 0, 800)
+    st = _state(cfg, host)
+    swl.swl_seal(st, dev(k[:700]), dev(v[:700]), swl.alloc_scratch(st.geom, 700),
+                 windows=cfg.meta_windows())
+    orc = oracle.from_config(cfg, host)
+    orc.step(q[:700], k[:700], v[:700], want=np.zeros(700, bool))
+    check_state(read_state(st), orc)
+    got = _prefill(cfg, st, q[700:], k[700:], v[700:])
+    check_out(got, orc.step(q[700:], k[700:], v[700:]), "rows after the seal")
+    check_state(read_state(st), orc)
+
+
+@pytest.mark.parametrize("T", [30, 200])
+def test_rewind_one_push(T):
+    """swl_rewind moves meta back by one push in every group (a partial and a
+    full window here), as the oracle's rewind does; a token followed by a
+    rewind leaves meta where it was."""
+    banner(f"rewind after {T} rows")
+    cfg = synth.Config("rewind", G=2, H=2, d=32, dv=32, ns=2, W=64, m=8, rows=T,
+                       windows=(48, 64))
+    host = synth.make_state(cfg)
+    q, k, v = synth.rows(cfg, 0, T + 1)
+    st = _state(cfg, host)
+    _prefill(cfg, st, q[:T], k[:T], v[:T])
+    orc = oracle.from_config(cfg, host)
+    orc.step(q[:T], k[:T], v[:T], want=np.zeros(T, bool))
+    before = read_state(st)["meta"].copy()
+    swl.swl_rewind(st)
+    orc.rewind()
+    check_state(read_state(st), orc)
+    swl.swl_attend_token(st, dev(q[T:]), dev(k[T:]), dev(v[T:]),
+                         torch().empty((1, cfg.nh, cfg.dv), device="cuda"),
+                         swl.alloc_scratch(st.geom, 1))
+    swl.swl_rewind(st)
+    after = read_state(st)["meta"]
+    rewound = before.reshape(-1, 4).copy()
+    for g in range(cfg.G):
+        wg = cfg.window(g)
+        if rewound[g, 0] == wg:
+            rewound[g, 1] = (rewound[g, 1] + wg - 1) % wg
+            rewound[g, 2] -= 1
+        elif rewound[g, 0] > 0:
+            rewound[g, 0] -= 1
+    assert np.array_equal(after.reshape(-1, 4), rewound)
+
+
 # -- the small layer, every row ------------------------------------------------------
 
 def test_small_full():

@@ -224,6 +224,37 @@ def test_meta_and_ring_closed_form(wg, len0, head0, T):
         np.testing.assert_array_equal(rv[0, slot], V[len(V) - ln + x])
 
 
+@pytest.mark.parametrize("wg,len0,head0,T", [(8, 0, 0, 3), (8, 0, 0, 8), (8, 3, 5, 20), (5, 5, 4, 1)])
+def test_rewind_undoes_the_last_push(wg, len0, head0, T):
+    """A push followed by a rewind leaves len, head and nfar where they were
+    (the rewind is the inverse of one push's bookkeeping), in a window that
+    was partial or full before the push; repeated, it walks back through
+    every earlier meta of a partial window."""
+    cfg = _cfg(G=1, W=wg, len0=len0, head0=head0, rows=T + 1, m=2)
+    st = synth.make_state(cfg)
+    q, k, v = _rand_rows(cfg, T + 1, seed=9)
+    orc = oracle.from_config(cfg, st)
+    orc.step(q[:T], k[:T], v[:T], want=np.zeros(T, bool))
+    before = orc.meta()[0, :3].tolist()
+    orc.step(q[T:], k[T:], v[T:], want=np.zeros(1, bool))
+    assert orc.meta()[0, :3].tolist() != before
+    orc.rewind()
+    assert orc.meta()[0, :3].tolist() == before
+    # a partial window walks back to empty, then stays there
+    cfg2 = _cfg(G=1, W=wg, rows=3, m=2)
+    o2 = oracle.from_config(cfg2, synth.make_state(cfg2))
+    q2, k2, v2 = _rand_rows(cfg2, 3, seed=10)
+    seen = [o2.meta()[0, :3].tolist()]
+    for r in range(3):
+        o2.step(q2[r:r + 1], k2[r:r + 1], v2[r:r + 1], want=np.zeros(1, bool))
+        seen.append(o2.meta()[0, :3].tolist())
+    for r in range(3):
+        o2.rewind()
+        assert o2.meta()[0, :3].tolist() == seen[2 - r]
+    o2.rewind()
+    assert o2.meta()[0, :3].tolist() == [0, 0, 0]
+
+
 # -- rect and the negative-mass guard ----------------------------------------------
 
 def test_rect_clamps_negative_far_weights():
