@@ -236,8 +236,12 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
         zero16(sacc);
         const float* kr = &Ks[buf * KT + ln][hf * (D / 2)];
         // a wave in an MFMA stretch gets issue priority over its SIMD partner
-        // in its softmax stretch, so the two overlap
-        __builtin_amdgcn_s_setprio(1);
+        // in its softmax stretch, so the two overlap; in the score stretch
+        // waves 0-3 also rank above waves 4-7, so that waves sharing a SIMD
+        // tend to drift apart instead of reaching their softmax stretches
+        // together
+        if (wave < 4) __builtin_amdgcn_s_setprio(2);
+        else __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int st = 0; st < D / 2; st += 4) {
             const float4 a = *reinterpret_cast<const float4*>(kr + st);
@@ -251,7 +255,9 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
         // visible to row i when lo_q <= pos <= hi_q (every row of the wave
         // sees every key of a "full" tile)
         float tmax = -INFINITY;
-        if (!sink && tb >= lo_ib && tb + KT - 1 <= base + ia) {
+        // (the tile test is uniform over the wave: a scalar branch)
+        const int full_tile = __builtin_amdgcn_readfirstlane((int)(!sink && tb >= lo_ib && tb + KT - 1 <= base + ia));
+        if (full_tile) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sacc[v]);
         } else if (sink) {
