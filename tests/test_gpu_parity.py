@@ -387,6 +387,60 @@ def test_prefill_passes_match_one_long_call():
     check_state(read_state(st), orc)
 
 
+# -- limits of the geometry ------------------------------------------------------------
+
+def test_largest_heads_sinks_landmarks():
+    """H = 16 query heads, ns = 256 sinks, m = 64 landmarks, three groups with
+    windows 300 / 130 / 64 (not multiples of the tile sizes), a ragged
+    777-row prompt, then tokens."""
+    banner("limits: H=16 ns=256 m=64, windows 300/130/64")
+    cfg = synth.Config("limits", G=3, H=16, d=64, dv=64, ns=256, W=300, m=64, rows=777,
+                       windows=(300, 130, 64), rope=True, landmark_scale=0.125)
+    host = synth.make_state(cfg)
+    q, k, v = synth.rows(cfg, 0, 777 + 24)
+    st = _state(cfg, host)
+    got = _prefill(cfg, st, q[:777], k[:777], v[:777], poison=True)
+    orc = oracle.from_config(cfg, host, threads=oracle_threads())
+    check_out(got, orc.step(q[:777], k[:777], v[:777]))
+    check_state(read_state(st), orc)
+    got_t = _tokens(cfg, st, q[777:], k[777:], v[777:])
+    check_out(got_t, orc.step(q[777:], k[777:], v[777:]), "tokens")
+    check_state(read_state(st), orc)
+
+
+def test_many_groups():
+    """G = 64 KV groups (the limit) of two heads, a prompt and tokens."""
+    banner("limits: G=64")
+    cfg = synth.Config("groups", G=64, H=2, d=16, dv=16, ns=2, W=40, m=8, rows=150)
+    host = synth.make_state(cfg)
+    q, k, v = synth.rows(cfg, 0, 150 + 6)
+    st = _state(cfg, host)
+    got = _prefill(cfg, st, q[:150], k[:150], v[:150])
+    orc = oracle.from_config(cfg, host, threads=oracle_threads())
+    check_out(got, orc.step(q[:150], k[:150], v[:150]))
+    got_t = _tokens(cfg, st, q[150:], k[150:], v[150:])
+    check_out(got_t, orc.step(q[150:], k[150:], v[150:]), "tokens")
+    check_state(read_state(st), orc)
+
+
+@pytest.mark.parametrize("W,T", [(65536, 3000), (5000, 6000)])
+def test_tokens_over_many_splits(W, T):
+    """Decode with the window split into more than 64 partials per head (the
+    merge folds them in several batches): the widest ring stride with a
+    partial window, and a full 5000-key window."""
+    banner(f"tokens over many splits: W={W} after {T} rows")
+    cfg = synth.Config("splits", G=1, H=2, d=32, dv=32, ns=3, W=W, m=8, rows=T)
+    host = synth.make_state(cfg)
+    q, k, v = synth.rows(cfg, 0, T + 12)
+    st = _state(cfg, host)
+    _prefill(cfg, st, q[:T], k[:T], v[:T])
+    orc = oracle.from_config(cfg, host)
+    orc.step(q[:T], k[:T], v[:T], want=np.zeros(T, bool))
+    got = _tokens(cfg, st, q[T:], k[T:], v[T:])
+    check_out(got, orc.step(q[T:], k[T:], v[T:]), "tokens")
+    check_state(read_state(st), orc)
+
+
 def test_zero_rows_is_a_noop():
     cfg = synth.TINY
     host = synth.make_state(cfg)
