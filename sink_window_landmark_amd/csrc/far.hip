@@ -13,6 +13,7 @@
 //   E_sj = exp(l_j - M'_s);  P_sj = R_s Z_{s-1} + sum_{j'<=j} E_sj';
 //   Z_s = P_s,63;  Theta_s = R_s Theta_{s-1} + sum_j E_sj v_evicted(j).
 #include "swl_internal.h"
+#include "lanes.h"
 
 namespace swl {
 
@@ -24,6 +25,43 @@ __device__ __forceinline__ floatx16 fmfma(float a, float b, floatx16 c)
 }
 
 __device__ __forceinline__ int fkap(int v, int hf) { return (v >> 2) * 8 + hf * 4 + (v & 3); }
+
+// The rows the sub-chunk's rows evict (chunk rows jlo <= j < ks; zero rows
+// elsewhere) into LDS rows of W + 4 floats: the key or value at position
+// len0 + r0 + j - w_g, from the ring (positions before the call) or from the
+// call's own rows.  Every load takes a clamped address and no condition, so
+// they are all in flight at once (a load under a per-lane condition waits for
+// every earlier one); the row selection happens at the store.
+template <int W, int NT>
+__device__ __forceinline__ void stage_evicted(float* lds, const float* ring, const float* rows,
+                                              const KParams& p, const GMeta& c, int g, int r0,
+                                              int jlo, int ks)
+{
+    constexpr int N = SUB * (W / 4);                 // 16-byte pieces
+    constexpr int PT = (N + NT - 1) / NT;            // per thread
+    // a native 4-wide vector: an array of HIP's float4 struct would sit in scratch memory
+    typedef float v4 __attribute__((ext_vector_type(4)));
+    const int tid = threadIdx.x;
+    v4 x[PT];
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+        const int e = min(tid + u * NT, N - 1);
+        const int j = e / (W / 4), c4 = (e % (W / 4)) * 4;
+        const int pos = max(c.len0 + r0 + min(j, ks - 1) - c.wg, 0);
+        const float* ra = ring + ((int64_t)g * p.W + (c.head0 + min(pos, max(c.len0 - 1, 0))) % c.wg) * W;
+        const float* ia = rows + ((int64_t)max(pos - c.len0, 0) * p.G + g) * W;
+        x[u] = *reinterpret_cast<const v4*>((pos < c.len0 ? ra : ia) + c4);
+    }
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+        const int e = tid + u * NT;
+        if (e < N) {
+            const int j = e / (W / 4), c4 = (e % (W / 4)) * 4;
+            const v4 z = {0.f, 0.f, 0.f, 0.f};
+            *reinterpret_cast<v4*>(lds + j * (W + 4) + c4) = (j >= jlo && j < ks) ? x[u] : z;
+        }
+    }
+}
 
 // ---------------------------------------------------------------------------
 // far_score: L[s][gh*m+b][j] = scale <q~_{gh,b}, key evicted by row j>, -inf
@@ -50,13 +88,7 @@ __global__ __launch_bounds__(FS_THREADS) void k_far_score(KParams p)
     const int hm = p.H * p.m;
     const int64_t nhm = (int64_t)p.nh * p.m;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, ln = lane & 31;
-    for (int e = tid; e < SUB * (D / 4); e += FS_THREADS) {
-        const int j = e / (D / 4), c4 = (e % (D / 4)) * 4;
-        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (j >= jlo && j < ks)
-            x = *reinterpret_cast<const float4*>(key_row(p, c, g, c.len0 + r0 + j - c.wg) + c4);
-        *reinterpret_cast<float4*>(&ek[j][c4]) = x;
-    }
+    stage_evicted<D, FS_THREADS>(&ek[0][0], p.ring_k, p.k, p, c, g, r0, jlo, ks);
     __syncthreads();
     float* L = p.E + ((int64_t)s * nhm + (int64_t)g * hm) * SUB;
     float* MX = p.Ms + (int64_t)s * nhm + (int64_t)g * hm;   // local max (the scan overwrites)
@@ -100,9 +132,7 @@ __global__ __launch_bounds__(FS_THREADS) void k_far_score(KParams p)
                 acc[jt][v] = l;
                 m2 = fmaxf(m2, l);
             }
-#pragma unroll
-            for (int o = 16; o >= 1; o >>= 1) m2 = fmaxf(m2, __shfl_xor(m2, o, 64));
-            mx[v] = m2;
+            mx[v] = max32(m2);   // over the 32 evicting rows j of this lane half
         }
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -112,8 +142,7 @@ __global__ __launch_bounds__(FS_THREADS) void k_far_score(KParams p)
 #pragma unroll
                 for (int jt = 0; jt < 2; ++jt) z += expf(acc[jt][v] - mx[v]);
             }
-#pragma unroll
-            for (int o = 16; o >= 1; o >>= 1) z += __shfl_xor(z, o, 64);
+            z = sum32(z);
             if (hb < hm) {
 #pragma unroll
                 for (int jt = 0; jt < 2; ++jt) L[(int64_t)hb * SUB + jt * 32 + ln] = acc[jt][v];
@@ -195,13 +224,7 @@ __global__ __launch_bounds__(256) void k_dtheta(KParams p)
     const int hm = p.H * p.m;
     const int64_t nhm = (int64_t)p.nh * p.m;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, ln = lane & 31;
-    for (int e = tid; e < SUB * (DV / 4); e += 256) {
-        const int j = e / (DV / 4), c4 = (e % (DV / 4)) * 4;
-        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (j >= jlo && j < ks)
-            x = *reinterpret_cast<const float4*>(val_row(p, c, g, c.len0 + r0 + j - c.wg) + c4);
-        *reinterpret_cast<float4*>(&ve[j][c4]) = x;
-    }
+    stage_evicted<DV, 256>(&ve[0][0], p.ring_v, p.v, p, c, g, r0, jlo, ks);
     __syncthreads();
     const int64_t row0 = (int64_t)s * nhm + (int64_t)g * hm;   // landmark row (s, g*H*m)
     const int nht = (hm + 31) / 32;
