@@ -22,25 +22,50 @@
 // stream through LDS in tiles of 32 keys shared by all heads of the group
 // (the GQA reuse of the pages' Metal and Dory kernels).
 //
-// MFMA layout (v_mfma_f32_32x32x2f32; lane l, half hf = l/32, n = l%32;
-// kappa(v, hf) = (v/4)*8 + hf*4 + v%4):
-//   S^T = K Q^T     A = key rows (key n; the two d columns of step st are
-//                   hf*D/2 + st), B = Q^T held in registers (query n).  The
-//                   16 accumulators of lane l are keys kappa(v, hf) of query
-//                   n, so each lane owns one query's softmax state.
-//   O^T += V^T P^T  accumulator v of S^T is the B operand of step t = v;
-//                   A = V^T with value column NB*n + blk for block blk.
-//   The far products reuse the same shapes: landmarks (a or b) or in-chunk
-//   rows j take the place of keys, and a C-layout accumulator tile is always
-//   directly the B operand of the next product.
+// fp32 products on fp16 matrix cores (near part).  Each fp32 operand x is
+// split into fp16 halves, x = hi + lo * 2^-sc: hi is x rounded toward zero
+// and lo the exact remainder, scaled by 2^11 (sc = 11) for q and k so that
+// it stays a normal number.  A product is hi*hi + (hi*lo + lo*hi) * 2^-sc on
+// v_mfma_f32_32x32x16_f16 with fp32 accumulation (the hi*lo terms of the
+// scores in an accumulator of their own); the dropped lo*lo term and the
+// rounding of lo leave about 2^-20 relative error per product, at a fifth of
+// the fp32 MFMA's time for the three products.  Values split unscaled (an
+// absolute error floor of 2^-24), and the softmax weights are kept in
+// (0, 2^12] so that theirs stays far below that.  Range: |k| and
+// |scale * log2(e) * q| below 2^15, |v| below 65504.
+//
+// MFMA layout (32x32 tiles; lane l, half hf = l/32, n = l%32;
+// kappa(v, hf) = (v/4)*8 + hf*4 + v%4 is the row of accumulator v):
+//   S^T = K Q^T     A = key rows from LDS (key n; k-step st covers columns
+//                   16 st + 8 hf .. +7 of lane l), B = Q^T halves held in
+//                   registers (query n).  Lane l's accumulators are keys
+//                   kappa(v, hf) of query n, so each lane owns one query's
+//                   softmax state.
+//   O^T += V^T P^T  accumulators 8t .. 8t+7 of S^T are the B operand of
+//                   k-step t; V^T sits in LDS with one row per value column
+//                   and the keys of a tile permuted (bits 2 and 3 of the
+//                   key index swapped) so that the eight keys a lane needs
+//                   are one 16-byte read.  Row rho holds value column 2 rho
+//                   below D/2 and 2 (rho - D/2) + 1 above, which keeps the
+//                   staging writes free of bank conflicts.
+//   The far epilogue runs on v_mfma_f32_32x32x2f32 with the same shapes:
+//   landmarks (a or b) or in-chunk rows j take the place of keys, and a
+//   C-layout accumulator tile is always directly the B operand of the next
+//   product.
 // Softmax runs online in base 2 (q is pre-scaled by scale*log2 e).
 #include "swl_internal.h"
 
 namespace swl {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int KT = 32;  // keys per tile
+constexpr int KT = 32;                   // keys per tile
+constexpr float LO_UP = 2048.f;          // 2^11: scale of the lo halves of q and k
+constexpr float LO_DOWN = 1.f / 2048.f;
+constexpr float P_EXP = 12.f;            // softmax weights are 2^(s - max + 12)
 
 // Block shape per head width: two waves per head, up to four heads per block
 // (two at d = 256, so that each wave may use a whole SIMD's registers:
@@ -56,6 +81,12 @@ __device__ __forceinline__ floatx16 mfma32(float a, float b, floatx16 c)
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ floatx16 mfma16(u32x4 a, u32x4 b, floatx16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a),
+                                                  __builtin_bit_cast(half8, b), c, 0, 0, 0);
+}
+
 __device__ __forceinline__ int kap(int v, int hf) { return (v >> 2) * 8 + hf * 4 + (v & 3); }
 
 // 2^x as the bare v_exp_f32 (results below 2^-126 flush to 0, which only
@@ -68,35 +99,52 @@ __device__ __forceinline__ void zero16(floatx16& x)
     for (int v = 0; v < 16; ++v) x[v] = 0.f;
 }
 
-// O^T[blk] += A_row^T B for one MFMA step: `row` points at the value row of
-// this lane's k index (value column NB*n + blk is A for block blk).
+// (a, b) as an fp16 pair rounded toward zero, a in the low half
+__device__ __forceinline__ unsigned pk16(float a, float b)
+{
+    return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+__device__ __forceinline__ float half0(unsigned x)
+{
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(x & 0xffffu));
+}
+__device__ __forceinline__ float half1(unsigned x)
+{
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(x >> 16));
+}
+
+// hi/lo fp16 pairs of (a, b): a = hi + lo / 2^11 when SCALED, else hi + lo
+// (the remainder a - hi is exact in fp32)
+template <bool SCALED>
+struct Split {
+    unsigned hi, lo;
+    __device__ __forceinline__ Split(float a, float b)
+    {
+        hi = pk16(a, b);
+        const float ra = a - half0(hi), rb = b - half1(hi);
+        lo = SCALED ? pk16(ra * LO_UP, rb * LO_UP) : pk16(ra, rb);
+    }
+};
+
+// value column held by row rho of the V^T tiles (and by accumulator row rho
+// of O^T): the even columns first, then the odd ones
+template <int D>
+__device__ __forceinline__ int vcol(int rho) { return rho < D / 2 ? 2 * rho : 2 * rho - D + 1; }
+
+// Position of key bit 2 and bit 3 swapped: the order of a tile's keys in the
+// V^T rows.
+__device__ __forceinline__ int kperm(int k) { return (k & ~12) | ((k >> 1) & 4) | ((k << 1) & 8); }
+
+// O^T[blk] += A_row^T B for one fp32 MFMA step of the epilogue: `row` is the
+// value row of this lane's k index, and accumulator row rho of block blk is
+// value column vcol(32 blk + rho).
 template <int D, int NB>
 __device__ __forceinline__ void pv_step(floatx16 (&O)[NB], const float* row, int ln, float b)
 {
-    if constexpr (NB == 8) {
-        const float4 a = *reinterpret_cast<const float4*>(row + 8 * ln);
-        const float4 c = *reinterpret_cast<const float4*>(row + 8 * ln + 4);
-        O[0] = mfma32(a.x, b, O[0]);
-        O[1] = mfma32(a.y, b, O[1]);
-        O[2] = mfma32(a.z, b, O[2]);
-        O[3] = mfma32(a.w, b, O[3]);
-        O[4] = mfma32(c.x, b, O[4]);
-        O[5] = mfma32(c.y, b, O[5]);
-        O[6] = mfma32(c.z, b, O[6]);
-        O[7] = mfma32(c.w, b, O[7]);
-    } else if constexpr (NB == 4) {
-        const float4 a = *reinterpret_cast<const float4*>(row + 4 * ln);
-        O[0] = mfma32(a.x, b, O[0]);
-        O[1] = mfma32(a.y, b, O[1]);
-        O[2] = mfma32(a.z, b, O[2]);
-        O[3] = mfma32(a.w, b, O[3]);
-    } else if constexpr (NB == 2) {
-        const float2 a = *reinterpret_cast<const float2*>(row + 2 * ln);
-        O[0] = mfma32(a.x, b, O[0]);
-        O[1] = mfma32(a.y, b, O[1]);
-    } else {
-        const float a = ln < D ? row[ln] : 0.f;
-        O[0] = mfma32(a, b, O[0]);
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+        const int rho = min(blk * 32 + ln, D - 1);
+        O[blk] = mfma32(row[vcol<D>(rho)], b, O[blk]);
     }
 }
 
@@ -105,15 +153,27 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
 {
     constexpr int AT_THREADS = AtCfg<D>::THREADS;
     constexpr int HPB = AtCfg<D>::HPB;
-    constexpr int NB = D >= 32 ? D / 32 : 1;  // 32-column output blocks
-    constexpr int LD = D + 4;                 // LDS row stride
-    constexpr int F4 = KT * D / 4;            // float4 per tile matrix
-    constexpr int LPT = (F4 + AT_THREADS - 1) / AT_THREADS;
+    constexpr int NB = D >= 32 ? D / 32 : 1;  // 32-row blocks of O^T
+    constexpr int KD = D < 16 ? 16 : D;       // key width padded to whole k-steps
+    constexpr int NS = KD / 16;               // k-steps of a score tile
+    constexpr int LDK = KD + 8;               // fp16 row stride of a K tile
+    constexpr int LDV = KT + 8;               // fp16 row stride of a V^T tile
+    constexpr int KH = KT * LDK;              // fp16 elements of the hi (or lo) K tile
+    constexpr int VH = D * LDV;               // fp16 elements of the hi (or lo) V^T tile
+    constexpr int BUF = 2 * KH + 2 * VH;      // one buffer: K hi, K lo, V^T hi, V^T lo
+    constexpr int LDF = D + 4;                // fp32 row stride of the epilogue's tiles
+    constexpr int NEAR_BYTES = 2 * BUF * 2;
+    constexpr int FAR_BYTES = 2 * 2 * KT * LDF * 4;
+    constexpr int SMEM = NEAR_BYTES > FAR_BYTES ? NEAR_BYTES : FAR_BYTES;
+    constexpr int NU = 4 * D;                 // staging units of a tile: 4 keys x 2 columns
+    constexpr int LPU = (NU + AT_THREADS - 1) / AT_THREADS;
     constexpr float LOG2E = 1.4426950408889634f;
-    // two tile buffers of K and of V; the epilogue reuses Ks for the landmark
-    // keys (m <= 64 rows) and Vs for the sub-chunk's evicted values (64 rows)
-    __shared__ float Ks[2 * KT][LD];
-    __shared__ float Vs[2 * KT][LD];
+    __shared__ __align__(16) unsigned char smem[SMEM];
+    unsigned short* const tiles = reinterpret_cast<unsigned short*>(smem);
+    // the epilogue reuses the memory: landmark keys (m <= 64 rows) and the
+    // sub-chunk's evicted values (64 rows) in fp32
+    float(*const Ks)[LDF] = reinterpret_cast<float(*)[LDF]>(smem);
+    float(*const Vs)[LDF] = reinterpret_cast<float(*)[LDF]>(smem + 2 * KT * LDF * 4);
 
     // work item = (head group, group, sub-chunk), sub-chunk fastest, dealt
     // to XCDs in contiguous runs
@@ -141,19 +201,24 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
     const int w_hi = base + ib;                      // highest
     const int lo_ib = max(0, base + ib - c.wg + 1);  // every row of the wave sees [lo_ib, base+ia]
 
-    // Q^T fragment of this lane: q[r0+i][gh][hf*D/2 + st], pre-scaled.
-    float qf[D / 2];
+    // Q^T halves of this lane: q[r0+i][gh][16 st + 8 hf + e] * scale * log2 e
+    u32x4 qh[NS], ql[NS];
     {
         const float qs = p.scale * LOG2E;
         const bool ok = active && i < ks;
-        const float* qr = p.q + ((int64_t)(r0 + i) * p.nh + gh) * D + hf * (D / 2);
+        const float* qr = p.q + ((int64_t)(r0 + i) * p.nh + gh) * D;
 #pragma unroll
-        for (int st = 0; st < D / 2; st += 4) {
-            float4 x = ok ? *reinterpret_cast<const float4*>(qr + st) : make_float4(0.f, 0.f, 0.f, 0.f);
-            qf[st] = x.x * qs;
-            qf[st + 1] = x.y * qs;
-            qf[st + 2] = x.z * qs;
-            qf[st + 3] = x.w * qs;
+        for (int st = 0; st < NS; ++st) {
+            const int d0 = st * 16 + hf * 8;
+            float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = x;
+            if (ok & (d0 < D)) {
+                x = *reinterpret_cast<const float4*>(qr + d0);
+                y = *reinterpret_cast<const float4*>(qr + d0 + 4);
+            }
+            const Split<true> s0(x.x * qs, x.y * qs), s1(x.z * qs, x.w * qs);
+            const Split<true> s2(y.x * qs, y.y * qs), s3(y.z * qs, y.w * qs);
+            qh[st] = u32x4{s0.hi, s1.hi, s2.hi, s3.hi};
+            ql[st] = u32x4{s0.lo, s1.lo, s2.lo, s3.lo};
         }
     }
 
@@ -161,55 +226,75 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
     const int nwt = (hi_blk - lo_blk + KT) / KT;
     const int ntiles = nst + nwt;
 
-    float4 kreg[LPT], vreg[LPT];
+    if constexpr (KD > D) {
+        // zero columns D .. KD-1 of every K tile once: staging never writes them
+        for (int e = tid; e < 2 * 2 * KT; e += AT_THREADS) {
+            unsigned short* r = tiles + (e / (2 * KT)) * BUF + (e % (2 * KT)) * LDK;
+#pragma unroll
+            for (int x = D; x < KD; ++x) r[x] = 0;
+        }
+    }
+
+    // Key row x of tile tt: sinks clamp to the last sink and window positions
+    // to the block's last row, so every load reads real keys (the scores of
+    // the extra rows are masked).  Offsets fit 32 bits: a pass holds at most
+    // 16384 rows.
+    auto key_src = [&](int tt, int x, const float*& kp, const float*& vp) {
+        if (tt < nst) {
+            const uint32_t off = (uint32_t)(g * p.ns + min(tt * KT + x, p.ns - 1)) * D;
+            kp = p.sink_k + off;
+            vp = p.sink_v + off;
+        } else {
+            const int pos = min(lo_blk + (tt - nst) * KT + x, hi_blk);
+            const bool ring = pos < c.len0;
+            int slot = c.head0 + pos;
+            slot -= slot >= c.wg ? c.wg : 0;
+            const uint32_t off = ring ? (uint32_t)(g * p.W + slot) * D
+                                      : (uint32_t)(max(pos - c.len0, 0) * p.G + g) * D;
+            kp = (ring ? p.ring_k : p.k) + off;
+            vp = (ring ? p.ring_v : p.v) + off;
+        }
+    };
+
+    // staging unit e: keys 4 kg .. 4 kg + 3, columns c2, c2 + 1
+    float2 kreg[LPU][4], vreg[LPU][4];
     auto load_tile = [&](int tt) {
 #pragma unroll
-        for (int u = 0; u < LPT; ++u) {
-            const int e = tid + u * AT_THREADS;
-            float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
-            if (e < F4) {
-                const int row = e / (D / 4), c4 = (e % (D / 4)) * 4;
-                const float* kb = nullptr;
-                const float* vb = nullptr;
-                uint32_t off = 0;
-                if (tt < nst) {
-                    const int x = tt * KT + row;
-                    if (x < p.ns) {
-                        kb = p.sink_k;
-                        vb = p.sink_v;
-                        off = (uint32_t)(g * p.ns + x) * D;
-                    }
-                } else {
-                    const int pos = lo_blk + (tt - nst) * KT + row;
-                    if (pos <= hi_blk) {
-                        if (pos < c.len0) {
-                            kb = p.ring_k;
-                            vb = p.ring_v;
-                            off = (uint32_t)(g * p.W + (uint32_t)(c.head0 + pos) % (uint32_t)c.wg) * D;
-                        } else {
-                            kb = p.k;
-                            vb = p.v;
-                            off = (uint32_t)((pos - c.len0) * p.G + g) * D;
-                        }
-                    }
-                }
-                if (kb) {
-                    kx = *reinterpret_cast<const float4*>(kb + off + c4);
-                    vx = *reinterpret_cast<const float4*>(vb + off + c4);
-                }
+        for (int u = 0; u < LPU; ++u) {
+            const int e = min(tid + u * AT_THREADS, NU - 1);
+            const int kg = e / (D / 2), c2 = (e % (D / 2)) * 2;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float* kp;
+                const float* vp;
+                key_src(tt, kg * 4 + r, kp, vp);
+                kreg[u][r] = *reinterpret_cast<const float2*>(kp + c2);
+                vreg[u][r] = *reinterpret_cast<const float2*>(vp + c2);
             }
-            kreg[u] = kx;
-            vreg[u] = vx;
         }
     };
     auto store_tile = [&](int buf) {
+        unsigned short* kt = tiles + buf * BUF;
+        unsigned short* vt = kt + 2 * KH;
 #pragma unroll
-        for (int u = 0; u < LPT; ++u) {
+        for (int u = 0; u < LPU; ++u) {
             const int e = tid + u * AT_THREADS;
-            if (e < F4) {
-                const int row = e / (D / 4), c4 = (e % (D / 4)) * 4;
-                *reinterpret_cast<float4*>(&Ks[buf * KT + row][c4]) = kreg[u];
-                *reinterpret_cast<float4*>(&Vs[buf * KT + row][c4]) = vreg[u];
+            if ((NU % AT_THREADS == 0) || e < NU) {
+                const int kg = e / (D / 2), c2 = (e % (D / 2)) * 2;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const Split<true> sk(kreg[u][r].x, kreg[u][r].y);
+                    *reinterpret_cast<unsigned*>(kt + (kg * 4 + r) * LDK + c2) = sk.hi;
+                    *reinterpret_cast<unsigned*>(kt + KH + (kg * 4 + r) * LDK + c2) = sk.lo;
+                }
+                const int kc = kperm(kg * 4);
+                const Split<false> a0(vreg[u][0].x, vreg[u][1].x), a1(vreg[u][2].x, vreg[u][3].x);
+                const Split<false> b0(vreg[u][0].y, vreg[u][1].y), b1(vreg[u][2].y, vreg[u][3].y);
+                const int re = c2 / 2, ro = D / 2 + c2 / 2;   // rows of columns c2, c2 + 1
+                *reinterpret_cast<u32x2*>(vt + re * LDV + kc) = u32x2{a0.hi, a1.hi};
+                *reinterpret_cast<u32x2*>(vt + VH + re * LDV + kc) = u32x2{a0.lo, a1.lo};
+                *reinterpret_cast<u32x2*>(vt + ro * LDV + kc) = u32x2{b0.hi, b1.hi};
+                *reinterpret_cast<u32x2*>(vt + VH + ro * LDV + kc) = u32x2{b0.lo, b1.lo};
             }
         }
     };
@@ -232,9 +317,10 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
         const bool relevant = wave_rows && (sink || (tb <= w_hi && tb + KT - 1 >= w_lo));
         if (!relevant) continue;
 
-        floatx16 sacc;
-        zero16(sacc);
-        const float* kr = &Ks[buf * KT + ln][hf * (D / 2)];
+        floatx16 sh, sx;
+        zero16(sh);
+        zero16(sx);
+        const unsigned short* kr = tiles + buf * BUF + ln * LDK + hf * 8;
         // a wave in an MFMA stretch gets issue priority over its SIMD partner
         // in its softmax stretch, so the two overlap; in the score stretch
         // waves 0-3 also rank above waves 4-7, so that waves sharing a SIMD
@@ -243,14 +329,17 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
         if (wave < 4) __builtin_amdgcn_s_setprio(2);
         else __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int st = 0; st < D / 2; st += 4) {
-            const float4 a = *reinterpret_cast<const float4*>(kr + st);
-            sacc = mfma32(a.x, qf[st], sacc);
-            sacc = mfma32(a.y, qf[st + 1], sacc);
-            sacc = mfma32(a.z, qf[st + 2], sacc);
-            sacc = mfma32(a.w, qf[st + 3], sacc);
+        for (int st = 0; st < NS; ++st) {
+            const u32x4 ah = *reinterpret_cast<const u32x4*>(kr + st * 16);
+            const u32x4 al = *reinterpret_cast<const u32x4*>(kr + KH + st * 16);
+            sh = mfma16(ah, qh[st], sh);
+            sx = mfma16(ah, ql[st], sx);
+            sx = mfma16(al, qh[st], sx);
         }
         __builtin_amdgcn_s_setprio(0);
+        floatx16 sacc;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sacc[v] = fmaf(sx[v], LO_DOWN, sh[v]);
         // sinks are always visible; the window key at position tb + kappa is
         // visible to row i when lo_q <= pos <= hi_q (every row of the wave
         // sees every key of a "full" tile)
@@ -288,7 +377,7 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
                 for (int v = 0; v < 16; ++v) O[b][v] *= alpha;
             mrun = mnew;
         }
-        const float msub = mrun == -INFINITY ? 0.f : mrun;
+        const float msub = (mrun == -INFINITY ? 0.f : mrun) - P_EXP;
         float ts = 0.f;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -297,9 +386,28 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
             ts += pv;
         }
         lsum += ts;
+        u32x4 ph[2], pl[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const Split<false> s0(sacc[8 * t], sacc[8 * t + 1]), s1(sacc[8 * t + 2], sacc[8 * t + 3]);
+            const Split<false> s2(sacc[8 * t + 4], sacc[8 * t + 5]), s3(sacc[8 * t + 6], sacc[8 * t + 7]);
+            ph[t] = u32x4{s0.hi, s1.hi, s2.hi, s3.hi};
+            pl[t] = u32x4{s0.lo, s1.lo, s2.lo, s3.lo};
+        }
+        const unsigned short* vr = tiles + buf * BUF + 2 * KH + hf * 8;
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int t = 0; t < 16; ++t) pv_step<D, NB>(O, &Vs[buf * KT + kap(t, hf)][0], ln, sacc[t]);
+        for (int blk = 0; blk < NB; ++blk) {
+            const int rho = min(blk * 32 + ln, D - 1);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const u32x4 vh = *reinterpret_cast<const u32x4*>(vr + rho * LDV + t * 16);
+                const u32x4 vl = *reinterpret_cast<const u32x4*>(vr + VH + rho * LDV + t * 16);
+                O[blk] = mfma16(vh, ph[t], O[blk]);
+                O[blk] = mfma16(vh, pl[t], O[blk]);
+                O[blk] = mfma16(vl, ph[t], O[blk]);
+            }
+        }
         __builtin_amdgcn_s_setprio(0);
     }
     float den = lsum + __shfl_xor(lsum, 32, 64);   // near mass relative to mrun
@@ -336,6 +444,21 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
             const float* Pb = p.P + ghb0 * SUB;                         // [b][i]
             const float* Th = p.theta_prev + (int64_t)s * p.theta_prev_stride + (int64_t)gh * m * D;
 
+            // Q^T in fp32 for the epilogue's products: q[r0+i][gh][hf*D/2 + st]
+            float qf[D / 2];
+            {
+                const float qs = p.scale * LOG2E;
+                const bool ok = active && i < ks;
+                const float* qr = p.q + ((int64_t)(r0 + i) * p.nh + gh) * D + hf * (D / 2);
+#pragma unroll
+                for (int st = 0; st < D / 2; st += 4) {
+                    const float4 x = ok ? *reinterpret_cast<const float4*>(qr + st) : make_float4(0.f, 0.f, 0.f, 0.f);
+                    qf[st] = x.x * qs;
+                    qf[st + 1] = x.y * qs;
+                    qf[st + 2] = x.z * qs;
+                    qf[st + 3] = x.w * qs;
+                }
+            }
             // f^T = K~ Q^T (log2 units), e = exp2(f - fmax)
             floatx16 ef[MT];
 #pragma unroll
@@ -440,7 +563,7 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
                 }
             }
             // near part to the common exponent, then the far numerator
-            const float wn = ex2(mrun - cexp);
+            const float wn = ex2(mrun - cexp - P_EXP);   // the near weights carry 2^P_EXP
 #pragma unroll
             for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -470,22 +593,38 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
     if (active && i < ks) {
         const float inv = 1.f / fmaxf(den, 1e-30f);
         float* orow = p.out + ((int64_t)(r0 + i) * p.nh + gh) * D;
+        // accumulator row rho of block blk is value column vcol(32 blk + rho):
+        // rows rho and rho + D/2 are the adjacent columns 2 rho, 2 rho + 1
+        if constexpr (NB >= 2) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int ii = kap(v, hf);
-            if constexpr (NB == 8) {
-                *reinterpret_cast<float4*>(orow + 8 * ii) =
-                    make_float4(O[0][v] * inv, O[1][v] * inv, O[2][v] * inv, O[3][v] * inv);
-                *reinterpret_cast<float4*>(orow + 8 * ii + 4) =
-                    make_float4(O[4][v] * inv, O[5][v] * inv, O[6][v] * inv, O[7][v] * inv);
-            } else if constexpr (NB == 4) {
-                *reinterpret_cast<float4*>(orow + 4 * ii) =
-                    make_float4(O[0][v] * inv, O[1][v] * inv, O[2][v] * inv, O[3][v] * inv);
-            } else if constexpr (NB == 2) {
-                *reinterpret_cast<float2*>(orow + 2 * ii) = make_float2(O[0][v] * inv, O[1][v] * inv);
-            } else {
-                if (ii < D) orow[ii] = O[0][v] * inv;
+            for (int blk = 0; blk < NB / 2; ++blk)
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const floatx16& e = O[blk];
+                    const floatx16& o = O[blk + NB / 2];
+                    float* dst = orow + 2 * (blk * 32 + 8 * a + 4 * hf);
+                    *reinterpret_cast<float4*>(dst) =
+                        make_float4(e[4 * a] * inv, o[4 * a] * inv, e[4 * a + 1] * inv, o[4 * a + 1] * inv);
+                    *reinterpret_cast<float4*>(dst + 4) =
+                        make_float4(e[4 * a + 2] * inv, o[4 * a + 2] * inv, e[4 * a + 3] * inv, o[4 * a + 3] * inv);
+                }
+        } else if constexpr (D == 32 || D == 16) {
+            // D = 32: rows kappa(v) and kappa(v + 8) = kappa(v) + 16 for v < 8;
+            // D = 16: rows kappa(v) and kappa(v + 4) = kappa(v) + 8 for v < 4
+            constexpr int PAIR = D == 32 ? 8 : 4;
+#pragma unroll
+            for (int a = 0; a < PAIR / 4; ++a) {
+                const floatx16& e = O[0];
+                float* dst = orow + 2 * (8 * a + 4 * hf);
+                *reinterpret_cast<float4*>(dst) = make_float4(e[4 * a] * inv, e[4 * a + PAIR] * inv,
+                                                              e[4 * a + 1] * inv, e[4 * a + 1 + PAIR] * inv);
+                *reinterpret_cast<float4*>(dst + 4) = make_float4(e[4 * a + 2] * inv, e[4 * a + 2 + PAIR] * inv,
+                                                                  e[4 * a + 3] * inv, e[4 * a + 3 + PAIR] * inv);
             }
+        } else {
+            // D = 8: rows kappa(v, hf) = 4 hf + v for v < 4
+#pragma unroll
+            for (int v = 0; v < 4; ++v) orow[vcol<D>(4 * hf + v)] = O[0][v] * inv;
         }
     }
 }
