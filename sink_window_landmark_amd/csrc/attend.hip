@@ -31,7 +31,7 @@
 // rounding of lo leave about 2^-20 relative error per product, at a fifth of
 // the fp32 MFMA's time for the three products.  Values split unscaled (an
 // absolute error floor of 2^-24), and the softmax weights are kept in
-// (0, 2^12] so that theirs stays far below that.  Range: |k| and
+// (0, 2^15] with a sum of at least 2^8 so that theirs stays far below that.  Range: |k| and
 // |scale * log2(e) * q| below 2^15, |v| below 65504.
 //
 // MFMA layout (32x32 tiles; lane l, half hf = l/32, n = l%32;
@@ -65,7 +65,14 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int KT = 32;                   // keys per tile
 constexpr float LO_UP = 2048.f;          // 2^11: scale of the lo halves of q and k
 constexpr float LO_DOWN = 1.f / 2048.f;
-constexpr float P_EXP = 12.f;            // softmax weights are 2^(s - max + 12)
+// Softmax weights are 2^(s - m + P_EXP) against a reference m that is only
+// raised when a score exceeds it by more than TAU (log2 units), so they stay
+// in (0, 2^(P_EXP + TAU)] = (0, 2^15], inside fp16 range, while the running
+// sum, which holds the weight 2^P_EXP of the key that set m, stays at least
+// 2^8: the fp16 remainders' absolute floor (2^-24) is then far below fp32
+// rounding of the result.
+constexpr float P_EXP = 8.f;
+constexpr float TAU = 7.f;
 
 // Block shape per head width: two waves per head, up to four heads per block
 // (two at d = 256, so that each wave may use a whole SIMD's registers:
@@ -165,7 +172,7 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
     constexpr int NEAR_BYTES = 2 * BUF * 2;
     constexpr int FAR_BYTES = 2 * 2 * KT * LDF * 4;
     constexpr int SMEM = NEAR_BYTES > FAR_BYTES ? NEAR_BYTES : FAR_BYTES;
-    constexpr int NU = 4 * D;                 // staging units of a tile: 4 keys x 2 columns
+    constexpr int NU = 4 * D;                 // staging units of a tile: 2 keys x 4 columns
     constexpr int LPU = (NU + AT_THREADS - 1) / AT_THREADS;
     constexpr float LOG2E = 1.4426950408889634f;
     __shared__ __align__(16) unsigned char smem[SMEM];
@@ -239,37 +246,40 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
     // to the block's last row, so every load reads real keys (the scores of
     // the extra rows are masked).  Offsets fit 32 bits: a pass holds at most
     // 16384 rows.
-    auto key_src = [&](int tt, int x, const float*& kp, const float*& vp) {
-        if (tt < nst) {
-            const uint32_t off = (uint32_t)(g * p.ns + min(tt * KT + x, p.ns - 1)) * D;
-            kp = p.sink_k + off;
-            vp = p.sink_v + off;
-        } else {
-            const int pos = min(lo_blk + (tt - nst) * KT + x, hi_blk);
-            const bool ring = pos < c.len0;
-            int slot = c.head0 + pos;
-            slot -= slot >= c.wg ? c.wg : 0;
-            const uint32_t off = ring ? (uint32_t)(g * p.W + slot) * D
-                                      : (uint32_t)(max(pos - c.len0, 0) * p.G + g) * D;
-            kp = (ring ? p.ring_k : p.k) + off;
-            vp = (ring ? p.ring_v : p.v) + off;
-        }
+    auto sink_src = [&](int tt, int x, const float*& kp, const float*& vp) {
+        const uint32_t off = (uint32_t)(g * p.ns + min(tt * KT + x, p.ns - 1)) * D;
+        kp = p.sink_k + off;
+        vp = p.sink_v + off;
+    };
+    auto win_src = [&](int tt, int x, const float*& kp, const float*& vp) {
+        const int pos = min(lo_blk + (tt - nst) * KT + x, hi_blk);
+        const bool ring = pos < c.len0;
+        int slot = c.head0 + pos;
+        slot -= slot >= c.wg ? c.wg : 0;
+        const uint32_t off = ring ? (uint32_t)(g * p.W + slot) * D
+                                  : (uint32_t)(max(pos - c.len0, 0) * p.G + g) * D;
+        kp = (ring ? p.ring_k : p.k) + off;
+        vp = (ring ? p.ring_v : p.v) + off;
     };
 
-    // staging unit e: keys 4 kg .. 4 kg + 3, columns c2, c2 + 1
-    float2 kreg[LPU][4], vreg[LPU][4];
+    // Staging unit e: keys 2 kp, 2 kp + 1 (kp = e % 16, fastest over lanes
+    // so that the V^T writes of a wave spread over the banks) and columns
+    // c4 .. c4 + 3.
+    float4 kreg[LPU][2], vreg[LPU][2];
     auto load_tile = [&](int tt) {
+        const bool sink = tt < nst;   // uniform: a scalar branch per row
 #pragma unroll
         for (int u = 0; u < LPU; ++u) {
             const int e = min(tid + u * AT_THREADS, NU - 1);
-            const int kg = e / (D / 2), c2 = (e % (D / 2)) * 2;
+            const int kp = e & 15, c4 = (e >> 4) * 4;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float* kp;
-                const float* vp;
-                key_src(tt, kg * 4 + r, kp, vp);
-                kreg[u][r] = *reinterpret_cast<const float2*>(kp + c2);
-                vreg[u][r] = *reinterpret_cast<const float2*>(vp + c2);
+            for (int r = 0; r < 2; ++r) {
+                const float* ka;
+                const float* va;
+                if (sink) sink_src(tt, 2 * kp + r, ka, va);
+                else win_src(tt, 2 * kp + r, ka, va);
+                kreg[u][r] = *reinterpret_cast<const float4*>(ka + c4);
+                vreg[u][r] = *reinterpret_cast<const float4*>(va + c4);
             }
         }
     };
@@ -280,21 +290,28 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
         for (int u = 0; u < LPU; ++u) {
             const int e = tid + u * AT_THREADS;
             if ((NU % AT_THREADS == 0) || e < NU) {
-                const int kg = e / (D / 2), c2 = (e % (D / 2)) * 2;
+                const int kp = e & 15, c4 = (e >> 4) * 4;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const Split<true> sk(kreg[u][r].x, kreg[u][r].y);
-                    *reinterpret_cast<unsigned*>(kt + (kg * 4 + r) * LDK + c2) = sk.hi;
-                    *reinterpret_cast<unsigned*>(kt + KH + (kg * 4 + r) * LDK + c2) = sk.lo;
+                for (int r = 0; r < 2; ++r) {
+                    const float4 x = kreg[u][r];
+                    const Split<true> s0(x.x, x.y), s1(x.z, x.w);
+                    *reinterpret_cast<u32x2*>(kt + (2 * kp + r) * LDK + c4) = u32x2{s0.hi, s1.hi};
+                    *reinterpret_cast<u32x2*>(kt + KH + (2 * kp + r) * LDK + c4) = u32x2{s0.lo, s1.lo};
                 }
-                const int kc = kperm(kg * 4);
-                const Split<false> a0(vreg[u][0].x, vreg[u][1].x), a1(vreg[u][2].x, vreg[u][3].x);
-                const Split<false> b0(vreg[u][0].y, vreg[u][1].y), b1(vreg[u][2].y, vreg[u][3].y);
-                const int re = c2 / 2, ro = D / 2 + c2 / 2;   // rows of columns c2, c2 + 1
-                *reinterpret_cast<u32x2*>(vt + re * LDV + kc) = u32x2{a0.hi, a1.hi};
-                *reinterpret_cast<u32x2*>(vt + VH + re * LDV + kc) = u32x2{a0.lo, a1.lo};
-                *reinterpret_cast<u32x2*>(vt + ro * LDV + kc) = u32x2{b0.hi, b1.hi};
-                *reinterpret_cast<u32x2*>(vt + VH + ro * LDV + kc) = u32x2{b0.lo, b1.lo};
+                // columns c4 + j of the two keys: rows c4/2, c4/2 + 1 (even
+                // columns) and D/2 + c4/2, D/2 + c4/2 + 1 (odd columns)
+                const int kc = kperm(2 * kp);
+                const float4 a = vreg[u][0], b = vreg[u][1];
+                const Split<false> v0(a.x, b.x), v1(a.y, b.y), v2(a.z, b.z), v3(a.w, b.w);
+                const int re = c4 / 2, ro = D / 2 + c4 / 2;
+                *reinterpret_cast<unsigned*>(vt + re * LDV + kc) = v0.hi;
+                *reinterpret_cast<unsigned*>(vt + (re + 1) * LDV + kc) = v2.hi;
+                *reinterpret_cast<unsigned*>(vt + ro * LDV + kc) = v1.hi;
+                *reinterpret_cast<unsigned*>(vt + (ro + 1) * LDV + kc) = v3.hi;
+                *reinterpret_cast<unsigned*>(vt + VH + re * LDV + kc) = v0.lo;
+                *reinterpret_cast<unsigned*>(vt + VH + (re + 1) * LDV + kc) = v2.lo;
+                *reinterpret_cast<unsigned*>(vt + VH + ro * LDV + kc) = v1.lo;
+                *reinterpret_cast<unsigned*>(vt + VH + (ro + 1) * LDV + kc) = v3.lo;
             }
         }
     };
@@ -366,8 +383,9 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
             }
         }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        // rescale the running sums only when some query's maximum rises
-        if (__any(tmax > mrun)) {
+        // raise the reference (and rescale the running sums) only when some
+        // query's score exceeds it by more than TAU
+        if (__any(tmax > mrun + TAU)) {
             const float mnew = fmaxf(mrun, tmax);
             const float alpha = mnew == -INFINITY ? 1.f : ex2(mrun - mnew);
             lsum *= alpha;
