@@ -29,7 +29,7 @@ EXPORTS = ("swl_scratch_bytes", "swl_init_state", "swl_attend_chunk", "swl_commi
            "swl_attend_token", "swl_status_str")
 
 # Stage ids of swl_stage_fn (enum swl_stage).
-STAGES = ("far_score", "far_scan", "dtheta", "theta_scan", "attend", "ring", "meta")
+STAGES = ("far_score", "far_scan", "dtheta", "theta_scan", "attend", "ring", "meta", "kv_split")
 STAGE_FN = ctypes.CFUNCTYPE(None, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p)
 
 

@@ -40,7 +40,7 @@ static bool state_ok(const swl_geom* g, const swl_state* st)
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Carve {
-    size_t tok, e, p, ms, rs, tz, th, total;
+    size_t tok, e, p, ms, rs, tz, th, kv, total;
 };
 
 static Carve carve(const swl_geom* g, int S)
@@ -56,6 +56,7 @@ static Carve carve(const swl_geom* g, int S)
     c.rs = off; off += align256(sizeof(float) * (size_t)S * nhm);
     c.tz = off; off += align256(sizeof(float) * (size_t)(S + 1) * nhm);
     c.th = off; off += align256(sizeof(float) * (size_t)S * nhm * g->dv);
+    c.kv = off; off += align256((size_t)g->G * kv_tiles(g->ns, g->W, S) * kv_tile_bytes(g->d));
     c.total = off;
     return c;
 }
@@ -91,6 +92,8 @@ static void set_scratch(KParams& p, const swl_geom* g, void* scratch, int S)
     p.Rs = reinterpret_cast<float*>(b + c.rs);
     p.TZ = reinterpret_cast<float*>(b + c.tz);
     p.TH = reinterpret_cast<float*>(b + c.th);
+    p.kvs = reinterpret_cast<unsigned short*>(b + c.kv);
+    p.kv_tiles = kv_tiles(g->ns, g->W, S);
 }
 
 #define SWL_TRY(x)                          \
@@ -105,6 +108,7 @@ static int run_attend(const KParams& p, hipStream_t st)
     SWL_TRY(launch_far_score(p, st));
     SWL_TRY(launch_far_scan(p, st));
     SWL_TRY(launch_dtheta(p, st));
+    SWL_TRY(launch_kv_split(p, st));
     SWL_TRY(launch_attend(p, st));
     return SWL_OK;
 }
@@ -215,7 +219,10 @@ static int run_rows(const swl_geom* geom, const swl_state* st, const float* q, c
         SWL_STAGE(SWL_STAGE_FAR_SCAN, launch_far_scan(p, hs));
         SWL_STAGE(SWL_STAGE_DTHETA, launch_dtheta(p, hs));
         SWL_STAGE(SWL_STAGE_THETA_SCAN, launch_theta_scan(p, true, hs));
-        if (attend) SWL_STAGE(SWL_STAGE_ATTEND, launch_attend(p, hs));
+        if (attend) {
+            SWL_STAGE(SWL_STAGE_KV_SPLIT, launch_kv_split(p, hs));
+            SWL_STAGE(SWL_STAGE_ATTEND, launch_attend(p, hs));
+        }
         SWL_STAGE(SWL_STAGE_RING, launch_ring_commit(p, hs));
         SWL_STAGE(SWL_STAGE_META, launch_meta(p, hs));
         done += T;

@@ -45,9 +45,13 @@
 //                   k-step t; V^T sits in LDS with one row per value column
 //                   and the keys of a tile permuted (bits 2 and 3 of the
 //                   key index swapped) so that the eight keys a lane needs
-//                   are one 16-byte read.  Row rho holds value column 2 rho
-//                   below D/2 and 2 (rho - D/2) + 1 above, which keeps the
-//                   staging writes free of bank conflicts.
+//                   are one 16-byte read.
+// Key tiles: k_kv_split writes every key of a pass once as fp16 hi/lo tiles
+// (32 positions each, aligned to multiples of 32, sinks first) in the exact
+// byte layout attention wants in LDS, with the 16-byte chunks of each row
+// XOR-swizzled so that the MFMA operand reads are free of bank conflicts;
+// attention then stages a tile with plain global-to-LDS copies
+// (global_load_lds_dwordx4), with no arithmetic and no registers.
 //   The far epilogue runs on v_mfma_f32_32x32x2f32 with the same shapes:
 //   landmarks (a or b) or in-chunk rows j take the place of keys, and a
 //   C-layout accumulator tile is always directly the B operand of the next
@@ -63,6 +67,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int KT = 32;                   // keys per tile
+
 constexpr float LO_UP = 2048.f;          // 2^11: scale of the lo halves of q and k
 constexpr float LO_DOWN = 1.f / 2048.f;
 // Softmax weights are 2^(s - m + P_EXP) against a reference m that is only
@@ -133,25 +138,115 @@ struct Split {
     }
 };
 
-// value column held by row rho of the V^T tiles (and by accumulator row rho
-// of O^T): the even columns first, then the odd ones
-template <int D>
-__device__ __forceinline__ int vcol(int rho) { return rho < D / 2 ? 2 * rho : 2 * rho - D + 1; }
-
 // Position of key bit 2 and bit 3 swapped: the order of a tile's keys in the
-// V^T rows.
+// V^T rows (an involution).
 __device__ __forceinline__ int kperm(int k) { return (k & ~12) | ((k >> 1) & 4) | ((k << 1) & 8); }
 
+// One key tile in fp16 halves: K hi [KT][KD], K lo [KT][KD] (lo scaled by
+// 2^11), V^T hi [D][KT], V^T lo [D][KT] (keys in kperm order), 128 (KD + D)
+// bytes, a whole number of 1 KB wave copies.  Logical 16-byte chunk c of K
+// row r sits at chunk kchunk(r, c) and chunk c of V^T row rho at
+// vchunk(rho, c): the rows that one read instruction touches then start in
+// different banks.
+template <int D>
+struct KvTile {
+    static constexpr int KD = D < 16 ? 16 : D;   // key width padded to whole k-steps
+    static constexpr int KH = KT * KD;
+    static constexpr int VH = D * KT;
+    static constexpr int HALVES = 2 * KH + 2 * VH;
+    static constexpr int BYTES = 2 * HALVES;
+    static constexpr int CPR = KD / 8;                     // chunks of a K row
+    static constexpr int RPB = KD >= 128 ? 1 : 128 / KD;   // K rows per 256 bytes
+    static constexpr int CMASK = (CPR < 16 ? CPR : 16) - 1;
+};
+template <int D>
+__device__ __forceinline__ int kchunk(int r, int c) { return c ^ ((r / KvTile<D>::RPB) & KvTile<D>::CMASK); }
+__device__ __forceinline__ int vchunk(int rho, int c) { return c ^ ((rho >> 2) & 3); }
+
+// 16 bytes from global memory into LDS at lds_base + 16 * lane (M0 holds the
+// wave's LDS base).  Inline assembly, so that the compiler does not order
+// later LDS reads of the other tile buffer behind it: the kernel waits for
+// these copies itself (s_waitcnt, then a barrier) before a tile is read.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds_base)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+
 // O^T[blk] += A_row^T B for one fp32 MFMA step of the epilogue: `row` is the
-// value row of this lane's k index, and accumulator row rho of block blk is
-// value column vcol(32 blk + rho).
+// value row of this lane's k index (value column 32 blk + n is A for block
+// blk).
 template <int D, int NB>
 __device__ __forceinline__ void pv_step(floatx16 (&O)[NB], const float* row, int ln, float b)
 {
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk) {
-        const int rho = min(blk * 32 + ln, D - 1);
-        O[blk] = mfma32(row[vcol<D>(rho)], b, O[blk]);
+    for (int blk = 0; blk < NB; ++blk) O[blk] = mfma32(row[min(blk * 32 + ln, D - 1)], b, O[blk]);
+}
+
+// ---------------------------------------------------------------------------
+// k_kv_split: the key tiles of a pass.  One block per (group, tile): tiles
+// 0 .. nst-1 hold the sinks, tile nst + j the window positions 32 j ..
+// 32 j + 31 (ring positions, then the pass's rows), up to the last position
+// of the pass; rows past the end repeat the last real key (attention masks
+// them).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void k_kv_split(KParams p)
+{
+    using L = KvTile<D>;
+    __shared__ float kf[KT][D + 1];
+    __shared__ float vf[KT][D + 1];
+    const int t = blockIdx.x % p.kv_tiles, g = blockIdx.x / p.kv_tiles;
+    const int nst = (p.ns + KT - 1) / KT;
+    const GMeta c = load_gmeta(p.meta, g, p.W);
+    const int last = c.len0 + p.T - 1;   // last window position of the pass
+    if (t >= nst && (t - nst) * KT > last) return;
+    for (int e = threadIdx.x; e < KT * (D / 4); e += 256) {
+        const int r = e / (D / 4), c4 = (e % (D / 4)) * 4;
+        const float* kp;
+        const float* vp;
+        if (t < nst) {
+            const int64_t off = ((int64_t)g * p.ns + min(t * KT + r, p.ns - 1)) * D;
+            kp = p.sink_k + off;
+            vp = p.sink_v + off;
+        } else {
+            const int pos = min((t - nst) * KT + r, last);
+            kp = key_row(p, c, g, pos);
+            vp = val_row(p, c, g, pos);
+        }
+        const float4 kx = *reinterpret_cast<const float4*>(kp + c4);
+        const float4 vx = *reinterpret_cast<const float4*>(vp + c4);
+        kf[r][c4] = kx.x; kf[r][c4 + 1] = kx.y; kf[r][c4 + 2] = kx.z; kf[r][c4 + 3] = kx.w;
+        vf[r][c4] = vx.x; vf[r][c4 + 1] = vx.y; vf[r][c4 + 2] = vx.z; vf[r][c4 + 3] = vx.w;
+    }
+    __syncthreads();
+    unsigned short* out = p.kvs + ((int64_t)g * p.kv_tiles + t) * L::HALVES;
+    // K: row r, logical chunk cc = columns 8 cc .. 8 cc + 7 (zero past D)
+    for (int e = threadIdx.x; e < KT * L::CPR; e += 256) {
+        const int r = e / L::CPR, cc = e % L::CPR;
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = cc * 8 + j < D ? kf[r][min(cc * 8 + j, D - 1)] : 0.f;
+        const Split<true> s0(x[0], x[1]), s1(x[2], x[3]), s2(x[4], x[5]), s3(x[6], x[7]);
+        const int dst = r * L::KD + kchunk<D>(r, cc) * 8;
+        *reinterpret_cast<u32x4*>(out + dst) = u32x4{s0.hi, s1.hi, s2.hi, s3.hi};
+        *reinterpret_cast<u32x4*>(out + L::KH + dst) = u32x4{s0.lo, s1.lo, s2.lo, s3.lo};
+    }
+    // V^T: value column rho, logical chunk cc = key slots 8 cc .. 8 cc + 7
+    unsigned short* vo = out + 2 * L::KH;
+    for (int e = threadIdx.x; e < D * 4; e += 256) {
+        const int rho = e >> 2, cc = e & 3;
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = vf[kperm(cc * 8 + j)][rho];
+        const Split<false> s0(x[0], x[1]), s1(x[2], x[3]), s2(x[4], x[5]), s3(x[6], x[7]);
+        const int dst = rho * KT + vchunk(rho, cc) * 8;
+        *reinterpret_cast<u32x4*>(vo + dst) = u32x4{s0.hi, s1.hi, s2.hi, s3.hi};
+        *reinterpret_cast<u32x4*>(vo + L::VH + dst) = u32x4{s0.lo, s1.lo, s2.lo, s3.lo};
     }
 }
 
@@ -161,19 +256,16 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
     constexpr int AT_THREADS = AtCfg<D>::THREADS;
     constexpr int HPB = AtCfg<D>::HPB;
     constexpr int NB = D >= 32 ? D / 32 : 1;  // 32-row blocks of O^T
-    constexpr int KD = D < 16 ? 16 : D;       // key width padded to whole k-steps
+    using L = KvTile<D>;
+    constexpr int KD = L::KD;
     constexpr int NS = KD / 16;               // k-steps of a score tile
-    constexpr int LDK = KD + 8;               // fp16 row stride of a K tile
-    constexpr int LDV = KT + 8;               // fp16 row stride of a V^T tile
-    constexpr int KH = KT * LDK;              // fp16 elements of the hi (or lo) K tile
-    constexpr int VH = D * LDV;               // fp16 elements of the hi (or lo) V^T tile
-    constexpr int BUF = 2 * KH + 2 * VH;      // one buffer: K hi, K lo, V^T hi, V^T lo
+    constexpr int BUF = L::HALVES;            // one tile buffer (fp16 halves)
+    constexpr int NCH = L::BYTES / 1024;      // 1 KB wave copies of a tile
+    constexpr int NW = AT_THREADS / 64;
     constexpr int LDF = D + 4;                // fp32 row stride of the epilogue's tiles
-    constexpr int NEAR_BYTES = 2 * BUF * 2;
+    constexpr int NEAR_BYTES = 2 * L::BYTES;
     constexpr int FAR_BYTES = 2 * 2 * KT * LDF * 4;
     constexpr int SMEM = NEAR_BYTES > FAR_BYTES ? NEAR_BYTES : FAR_BYTES;
-    constexpr int NU = 4 * D;                 // staging units of a tile: 2 keys x 4 columns
-    constexpr int LPU = (NU + AT_THREADS - 1) / AT_THREADS;
     constexpr float LOG2E = 1.4426950408889634f;
     __shared__ __align__(16) unsigned char smem[SMEM];
     unsigned short* const tiles = reinterpret_cast<unsigned short*>(smem);
@@ -229,91 +321,17 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
         }
     }
 
+    // tiles: the sinks, then the aligned window tiles j0 .. j1 that meet the
+    // block's positions lo_blk .. hi_blk
     const int nst = (p.ns + KT - 1) / KT;
-    const int nwt = (hi_blk - lo_blk + KT) / KT;
-    const int ntiles = nst + nwt;
-
-    if constexpr (KD > D) {
-        // zero columns D .. KD-1 of every K tile once: staging never writes them
-        for (int e = tid; e < 2 * 2 * KT; e += AT_THREADS) {
-            unsigned short* r = tiles + (e / (2 * KT)) * BUF + (e % (2 * KT)) * LDK;
+    const int j0 = lo_blk / KT;
+    const int ntiles = nst + hi_blk / KT - j0 + 1;
+    const unsigned short* kvg = p.kvs + (int64_t)g * p.kv_tiles * BUF + lane * 8;
+    auto issue = [&](int tt, int buf) {
+        const unsigned short* src = kvg + (int64_t)(tt < nst ? tt : tt + j0) * BUF;
 #pragma unroll
-            for (int x = D; x < KD; ++x) r[x] = 0;
-        }
-    }
-
-    // Key row x of tile tt: sinks clamp to the last sink and window positions
-    // to the block's last row, so every load reads real keys (the scores of
-    // the extra rows are masked).  Offsets fit 32 bits: a pass holds at most
-    // 16384 rows.
-    auto sink_src = [&](int tt, int x, const float*& kp, const float*& vp) {
-        const uint32_t off = (uint32_t)(g * p.ns + min(tt * KT + x, p.ns - 1)) * D;
-        kp = p.sink_k + off;
-        vp = p.sink_v + off;
-    };
-    auto win_src = [&](int tt, int x, const float*& kp, const float*& vp) {
-        const int pos = min(lo_blk + (tt - nst) * KT + x, hi_blk);
-        const bool ring = pos < c.len0;
-        int slot = c.head0 + pos;
-        slot -= slot >= c.wg ? c.wg : 0;
-        const uint32_t off = ring ? (uint32_t)(g * p.W + slot) * D
-                                  : (uint32_t)(max(pos - c.len0, 0) * p.G + g) * D;
-        kp = (ring ? p.ring_k : p.k) + off;
-        vp = (ring ? p.ring_v : p.v) + off;
-    };
-
-    // Staging unit e: keys 2 kp, 2 kp + 1 (kp = e % 16, fastest over lanes
-    // so that the V^T writes of a wave spread over the banks) and columns
-    // c4 .. c4 + 3.
-    float4 kreg[LPU][2], vreg[LPU][2];
-    auto load_tile = [&](int tt) {
-        const bool sink = tt < nst;   // uniform: a scalar branch per row
-#pragma unroll
-        for (int u = 0; u < LPU; ++u) {
-            const int e = min(tid + u * AT_THREADS, NU - 1);
-            const int kp = e & 15, c4 = (e >> 4) * 4;
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const float* ka;
-                const float* va;
-                if (sink) sink_src(tt, 2 * kp + r, ka, va);
-                else win_src(tt, 2 * kp + r, ka, va);
-                kreg[u][r] = *reinterpret_cast<const float4*>(ka + c4);
-                vreg[u][r] = *reinterpret_cast<const float4*>(va + c4);
-            }
-        }
-    };
-    auto store_tile = [&](int buf) {
-        unsigned short* kt = tiles + buf * BUF;
-        unsigned short* vt = kt + 2 * KH;
-#pragma unroll
-        for (int u = 0; u < LPU; ++u) {
-            const int e = tid + u * AT_THREADS;
-            if ((NU % AT_THREADS == 0) || e < NU) {
-                const int kp = e & 15, c4 = (e >> 4) * 4;
-#pragma unroll
-                for (int r = 0; r < 2; ++r) {
-                    const float4 x = kreg[u][r];
-                    const Split<true> s0(x.x, x.y), s1(x.z, x.w);
-                    *reinterpret_cast<u32x2*>(kt + (2 * kp + r) * LDK + c4) = u32x2{s0.hi, s1.hi};
-                    *reinterpret_cast<u32x2*>(kt + KH + (2 * kp + r) * LDK + c4) = u32x2{s0.lo, s1.lo};
-                }
-                // columns c4 + j of the two keys: rows c4/2, c4/2 + 1 (even
-                // columns) and D/2 + c4/2, D/2 + c4/2 + 1 (odd columns)
-                const int kc = kperm(2 * kp);
-                const float4 a = vreg[u][0], b = vreg[u][1];
-                const Split<false> v0(a.x, b.x), v1(a.y, b.y), v2(a.z, b.z), v3(a.w, b.w);
-                const int re = c4 / 2, ro = D / 2 + c4 / 2;
-                *reinterpret_cast<unsigned*>(vt + re * LDV + kc) = v0.hi;
-                *reinterpret_cast<unsigned*>(vt + (re + 1) * LDV + kc) = v2.hi;
-                *reinterpret_cast<unsigned*>(vt + ro * LDV + kc) = v1.hi;
-                *reinterpret_cast<unsigned*>(vt + (ro + 1) * LDV + kc) = v3.hi;
-                *reinterpret_cast<unsigned*>(vt + VH + re * LDV + kc) = v0.lo;
-                *reinterpret_cast<unsigned*>(vt + VH + (re + 1) * LDV + kc) = v2.lo;
-                *reinterpret_cast<unsigned*>(vt + VH + ro * LDV + kc) = v1.lo;
-                *reinterpret_cast<unsigned*>(vt + VH + (ro + 1) * LDV + kc) = v3.lo;
-            }
-        }
+        for (int ch = wave; ch < NCH; ch += NW)
+            dma16(src + ch * 512, __builtin_amdgcn_readfirstlane(lds_addr(tiles + buf * BUF + ch * 512)));
     };
 
     floatx16 O[NB];
@@ -322,22 +340,23 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
     float mrun = -INFINITY, lsum = 0.f;
 
     // ---- near part: online softmax over the key tiles ----
-    load_tile(0);
+    issue(0, 0);
+#pragma unroll 1
     for (int tt = 0; tt < ntiles; ++tt) {
         const int buf = tt & 1;
-        store_tile(buf);
-        __syncthreads();
-        if (tt + 1 < ntiles) load_tile(tt + 1);
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of tile tt have landed
+        __syncthreads();                 // ... and every wave's; tile tt-1 is no longer read
+        if (tt + 1 < ntiles) issue(tt + 1, buf ^ 1);
 
         const bool sink = tt < nst;
-        const int tb = sink ? tt * KT : lo_blk + (tt - nst) * KT;
+        const int tb = sink ? tt * KT : (j0 + tt - nst) * KT;
         const bool relevant = wave_rows && (sink || (tb <= w_hi && tb + KT - 1 >= w_lo));
         if (!relevant) continue;
 
         floatx16 sh, sx;
         zero16(sh);
         zero16(sx);
-        const unsigned short* kr = tiles + buf * BUF + ln * LDK + hf * 8;
+        const unsigned short* kr = tiles + buf * BUF + ln * KD;
         // a wave in an MFMA stretch gets issue priority over its SIMD partner
         // in its softmax stretch, so the two overlap; in the score stretch
         // waves 0-3 also rank above waves 4-7, so that waves sharing a SIMD
@@ -347,8 +366,9 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
         else __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
-            const u32x4 ah = *reinterpret_cast<const u32x4*>(kr + st * 16);
-            const u32x4 al = *reinterpret_cast<const u32x4*>(kr + KH + st * 16);
+            const int ck = kchunk<D>(ln, 2 * st + hf) * 8;
+            const u32x4 ah = *reinterpret_cast<const u32x4*>(kr + ck);
+            const u32x4 al = *reinterpret_cast<const u32x4*>(kr + L::KH + ck);
             sh = mfma16(ah, qh[st], sh);
             sx = mfma16(ah, ql[st], sx);
             sx = mfma16(al, qh[st], sx);
@@ -412,15 +432,16 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
             ph[t] = u32x4{s0.hi, s1.hi, s2.hi, s3.hi};
             pl[t] = u32x4{s0.lo, s1.lo, s2.lo, s3.lo};
         }
-        const unsigned short* vr = tiles + buf * BUF + 2 * KH + hf * 8;
+        const unsigned short* vr = tiles + buf * BUF + 2 * L::KH;
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) {
             const int rho = min(blk * 32 + ln, D - 1);
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const u32x4 vh = *reinterpret_cast<const u32x4*>(vr + rho * LDV + t * 16);
-                const u32x4 vl = *reinterpret_cast<const u32x4*>(vr + VH + rho * LDV + t * 16);
+                const int cv = rho * KT + vchunk(rho, 2 * t + hf) * 8;
+                const u32x4 vh = *reinterpret_cast<const u32x4*>(vr + cv);
+                const u32x4 vl = *reinterpret_cast<const u32x4*>(vr + L::VH + cv);
                 O[blk] = mfma16(vh, ph[t], O[blk]);
                 O[blk] = mfma16(vh, pl[t], O[blk]);
                 O[blk] = mfma16(vl, ph[t], O[blk]);
@@ -611,39 +632,15 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
     if (active && i < ks) {
         const float inv = 1.f / fmaxf(den, 1e-30f);
         float* orow = p.out + ((int64_t)(r0 + i) * p.nh + gh) * D;
-        // accumulator row rho of block blk is value column vcol(32 blk + rho):
-        // rows rho and rho + D/2 are the adjacent columns 2 rho, 2 rho + 1
-        if constexpr (NB >= 2) {
+        // accumulator row rho of block blk is value column 32 blk + rho; rows
+        // kappa(4a .. 4a+3, hf) are the adjacent columns 8a + 4hf .. +3
 #pragma unroll
-            for (int blk = 0; blk < NB / 2; ++blk)
+        for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    const floatx16& e = O[blk];
-                    const floatx16& o = O[blk + NB / 2];
-                    float* dst = orow + 2 * (blk * 32 + 8 * a + 4 * hf);
-                    *reinterpret_cast<float4*>(dst) =
-                        make_float4(e[4 * a] * inv, o[4 * a] * inv, e[4 * a + 1] * inv, o[4 * a + 1] * inv);
-                    *reinterpret_cast<float4*>(dst + 4) =
-                        make_float4(e[4 * a + 2] * inv, o[4 * a + 2] * inv, e[4 * a + 3] * inv, o[4 * a + 3] * inv);
-                }
-        } else if constexpr (D == 32 || D == 16) {
-            // D = 32: rows kappa(v) and kappa(v + 8) = kappa(v) + 16 for v < 8;
-            // D = 16: rows kappa(v) and kappa(v + 4) = kappa(v) + 8 for v < 4
-            constexpr int PAIR = D == 32 ? 8 : 4;
-#pragma unroll
-            for (int a = 0; a < PAIR / 4; ++a) {
-                const floatx16& e = O[0];
-                float* dst = orow + 2 * (8 * a + 4 * hf);
-                *reinterpret_cast<float4*>(dst) = make_float4(e[4 * a] * inv, e[4 * a + PAIR] * inv,
-                                                              e[4 * a + 1] * inv, e[4 * a + 1 + PAIR] * inv);
-                *reinterpret_cast<float4*>(dst + 4) = make_float4(e[4 * a + 2] * inv, e[4 * a + 2 + PAIR] * inv,
-                                                                  e[4 * a + 3] * inv, e[4 * a + 3 + PAIR] * inv);
-            }
-        } else {
-            // D = 8: rows kappa(v, hf) = 4 hf + v for v < 4
-#pragma unroll
-            for (int v = 0; v < 4; ++v) orow[vcol<D>(4 * hf + v)] = O[0][v] * inv;
-        }
+            for (int a = 0; a < (D >= 32 ? 4 : D / 8); ++a)
+                *reinterpret_cast<float4*>(orow + blk * 32 + 8 * a + 4 * hf) =
+                    make_float4(O[blk][4 * a] * inv, O[blk][4 * a + 1] * inv, O[blk][4 * a + 2] * inv,
+                                O[blk][4 * a + 3] * inv);
     }
 }
 
@@ -655,6 +652,34 @@ static hipError_t launch_d(const KParams& p, hipStream_t st)
     if (p.m <= 32) hipLaunchKernelGGL((k_attend<D, 1>), grid, dim3(AtCfg<D>::THREADS), 0, st, p);
     else hipLaunchKernelGGL((k_attend<D, 2>), grid, dim3(AtCfg<D>::THREADS), 0, st, p);
     return hipGetLastError();
+}
+
+int kv_tiles(int ns, int W, int S)
+{
+    // positions of a pass: at most W ring keys, then S sub-chunks of rows
+    return (ns + KT - 1) / KT + (W + S * SUB + KT - 1) / KT;
+}
+
+size_t kv_tile_bytes(int d) { return (size_t)128 * ((d < 16 ? 16 : d) + d); }
+
+template <int D>
+static hipError_t launch_split_d(const KParams& p, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_kv_split<D>, dim3(p.G * p.kv_tiles), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_split(const KParams& p, hipStream_t st)
+{
+    switch (p.d) {
+    case 8: return launch_split_d<8>(p, st);
+    case 16: return launch_split_d<16>(p, st);
+    case 32: return launch_split_d<32>(p, st);
+    case 64: return launch_split_d<64>(p, st);
+    case 128: return launch_split_d<128>(p, st);
+    case 256: return launch_split_d<256>(p, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_attend(const KParams& p, hipStream_t st)

@@ -44,6 +44,8 @@ struct KParams {
     float* TH;   // [S][nh*m][dv]   Theta increments, then Theta before each sub-chunk
     const float* theta_prev;  // Theta before sub-chunk s at theta_prev + s*theta_prev_stride
     int64_t theta_prev_stride;
+    unsigned short* kvs;      // [G][kv_tiles] fp16 key tiles of the pass (k_kv_split)
+    int kv_tiles;             // tiles per group: the sinks, then the aligned window tiles
 };
 
 // Ring bookkeeping of group g at the start of a call.
@@ -115,7 +117,11 @@ hipError_t launch_far_score(const KParams& p, hipStream_t st);
 hipError_t launch_far_scan(const KParams& p, hipStream_t st);
 hipError_t launch_dtheta(const KParams& p, hipStream_t st);
 hipError_t launch_theta_scan(const KParams& p, bool commit, hipStream_t st);
+hipError_t launch_kv_split(const KParams& p, hipStream_t st);
 hipError_t launch_attend(const KParams& p, hipStream_t st);
+// tiles per group and bytes per tile of the fp16 key tiles
+int kv_tiles(int ns, int W, int S);
+size_t kv_tile_bytes(int d);
 hipError_t launch_ring_commit(const KParams& p, hipStream_t st);
 hipError_t launch_meta(const KParams& p, hipStream_t st);
 hipError_t launch_rewind(const KParams& p, hipStream_t st);
