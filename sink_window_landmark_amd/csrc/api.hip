@@ -51,7 +51,7 @@ static Carve carve(const swl_geom* g, int S)
     // the decode plane comes first, at an offset that does not depend on S
     c.tok = off; off += align256(sizeof(float) * tok_part_floats(g->G, g->H, g->dv, g->ns, g->W));
     c.e = off;  off += align256(sizeof(float) * (size_t)S * nhm * SUB);
-    c.p = off;  off += align256(sizeof(float) * (size_t)S * nhm * SUB);
+    c.p = off;  off += align256(sizeof(float) * (size_t)S * g->G * g->H * SUB * 64);
     c.ms = off; off += align256(sizeof(float) * (size_t)S * nhm);
     c.rs = off; off += align256(sizeof(float) * (size_t)S * nhm);
     c.tz = off; off += align256(sizeof(float) * (size_t)(S + 1) * nhm);

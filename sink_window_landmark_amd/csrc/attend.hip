@@ -264,7 +264,7 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
     constexpr int NW = AT_THREADS / 64;
     constexpr int LDF = D + 4;                // fp32 row stride of the epilogue's tiles
     constexpr int NEAR_BYTES = 2 * L::BYTES;
-    constexpr int FAR_BYTES = 2 * 2 * KT * LDF * 4;
+    constexpr int FAR_BYTES = 2 * 2 * KT * LDF * 4 + HPB * 2 * 64 * 4;
     constexpr int SMEM = NEAR_BYTES > FAR_BYTES ? NEAR_BYTES : FAR_BYTES;
     constexpr float LOG2E = 1.4426950408889634f;
     __shared__ __align__(16) unsigned char smem[SMEM];
@@ -273,6 +273,8 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
     // sub-chunk's evicted values (64 rows) in fp32
     float(*const Ks)[LDF] = reinterpret_cast<float(*)[LDF]>(smem);
     float(*const Vs)[LDF] = reinterpret_cast<float(*)[LDF]>(smem + 2 * KT * LDF * 4);
+    // and the post-sub-chunk max M' and rescale R of each head's landmarks
+    float(*const MR)[2][64] = reinterpret_cast<float(*)[2][64]>(smem + 4 * KT * LDF * 4);
 
     // work item = (head group, group, sub-chunk), sub-chunk fastest, dealt
     // to XCDs in contiguous runs
@@ -470,6 +472,12 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
             *reinterpret_cast<float4*>(&Ks[row][c4]) = kx;
             *reinterpret_cast<float4*>(&Vs[row][c4]) = vx;
         }
+        for (int e = tid; e < HPB * 2 * 64; e += AT_THREADS) {
+            const int hh = e >> 7, which = (e >> 6) & 1, b = e & 63;
+            const int ghh = g * p.H + min(hgrp * HPB + hh, p.H - 1);
+            const float* src = which ? p.Rs : p.Ms;
+            MR[hh][which][b] = src[((int64_t)s * p.nh + ghh) * m + min(b, m - 1)];
+        }
         __syncthreads();
 
         const int farl = sm.nfar0 + (i >= sm.j0 ? i - sm.j0 + 1 : 0);
@@ -477,10 +485,10 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
         if (wave_rows) {
             const int64_t nhm = (int64_t)p.nh * m;
             const int64_t ghb0 = (int64_t)s * nhm + (int64_t)gh * m;   // (s, gh, b = 0)
-            const float* Ms = p.Ms + ghb0;
-            const float* Rs = p.Rs + ghb0;
+            const float* Ms = MR[wave >> 1][0];   // (b < 64: entries past m are not used)
+            const float* Rs = MR[wave >> 1][1];
             const float* Eb = p.E + ghb0 * SUB;                         // [b][j]
-            const float* Pb = p.P + ghb0 * SUB;                         // [b][i]
+            const float* Pt = p.P + (((int64_t)s * p.nh + gh) * SUB + i) * 64 + hf * 4;   // [b] of row i
             const float* Th = p.theta_prev + (int64_t)s * p.theta_prev_stride + (int64_t)gh * m * D;
 
             // Q^T in fp32 for the epilogue's products: q[r0+i][gh][hf*D/2 + st]
@@ -563,13 +571,19 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
 #pragma unroll
             for (int bt = 0; bt < MT; ++bt)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int b = bt * 32 + kap(v, hf);
-                    float u = gn[bt][v];
-                    if (p.rect) u = fmaxf(u, 0.f);
-                    const float gain = (lane_far && b < m) ? u * ex2(fmax + mb[bt][v] - cexp) : 0.f;
-                    gn[bt][v] = gain;
-                    if (b < m && lane_far) dfar += gain * Pb[(int64_t)b * SUB + i];
+                for (int a = 0; a < 4; ++a) {
+                    // landmarks kappa(4a .. 4a+3, hf) = 32 bt + 8a + 4hf .. +3
+                    const float4 pq = *reinterpret_cast<const float4*>(Pt + bt * 32 + 8 * a);
+                    const float pb[4] = {pq.x, pq.y, pq.z, pq.w};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int v = 4 * a + r, b = bt * 32 + kap(v, hf);
+                        float u = gn[bt][v];
+                        if (p.rect) u = fmaxf(u, 0.f);
+                        const float gain = lane_far & (b < m) ? u * ex2(fmax + mb[bt][v] - cexp) : 0.f;
+                        gn[bt][v] = gain;
+                        dfar += lane_far & (b < m) ? gain * pb[r] : 0.f;
+                    }
                 }
             dfar += __shfl_xor(dfar, 32, 64);
             const bool have = lane_far && dfar >= 0.f;

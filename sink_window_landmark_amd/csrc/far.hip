@@ -234,7 +234,10 @@ __global__ __launch_bounds__(256) void k_dtheta(KParams p)
         float e[32];
         {
             float* Lr = p.E + (row0 + min(hb, hm - 1)) * SUB + hf * 32;
-            float* Pr = p.P + (row0 + min(hb, hm - 1)) * SUB + hf * 32;
+            // P is stored per (sub-chunk, head, row j) with the landmarks
+            // contiguous: PT[s][gh][j][64], b < m
+            const int hbc = min(hb, hm - 1);
+            float* Pt = p.P + (((int64_t)s * p.nh + g * p.H + hbc / p.m) * SUB + hf * 32) * 64 + hbc % p.m;
             const float Mn = p.Ms[row0 + min(hb, hm - 1)];
             const float base = p.Rs[row0 + min(hb, hm - 1)] * p.TZ[row0 + min(hb, hm - 1)];
 #pragma unroll
@@ -261,7 +264,10 @@ __global__ __launch_bounds__(256) void k_dtheta(KParams p)
                     pre += e[k + 2]; pp.z = pre;
                     pre += e[k + 3]; pp.w = pre;
                     *reinterpret_cast<float4*>(Lr + k) = pe;
-                    *reinterpret_cast<float4*>(Pr + k) = pp;
+                    Pt[(k + 0) * 64] = pp.x;
+                    Pt[(k + 1) * 64] = pp.y;
+                    Pt[(k + 2) * 64] = pp.z;
+                    Pt[(k + 3) * 64] = pp.w;
                 }
             }
         }

@@ -37,7 +37,7 @@ struct KParams {
     int S;   // sub-chunks, ceil(T / SUB)
     // scratch planes (see scratch_layout)
     float* E;    // [S][nh*m][SUB]  scores, then exp mass against the post-sub-chunk max
-    float* P;    // [S][nh*m][SUB]  far mass prefix R*Z + sum_{j'<=j} E
+    float* P;    // [S][nh][SUB][64] far mass prefix R*Z + sum_{j'<=j} E of row j, landmark b < m
     float* Ms;   // [S][nh*m]       local max of the scores, then the post-sub-chunk max
     float* Rs;   // [S][nh*m]       local mass of the scores, then the rescale of the old mass
     float* TZ;   // [S+1][nh*m]     mass before each sub-chunk, then after the last
