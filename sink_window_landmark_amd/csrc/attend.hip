@@ -366,14 +366,31 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
         // together
         if (wave < 4) __builtin_amdgcn_s_setprio(2);
         else __builtin_amdgcn_s_setprio(1);
+        // (the operands of step st+1 are read before the products of step st
+        // are issued, so the LDS latency hides behind them)
+        u32x4 ah = *reinterpret_cast<const u32x4*>(kr + kchunk<D>(ln, hf) * 8);
+        u32x4 al = *reinterpret_cast<const u32x4*>(kr + L::KH + kchunk<D>(ln, hf) * 8);
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
-            const int ck = kchunk<D>(ln, 2 * st + hf) * 8;
-            const u32x4 ah = *reinterpret_cast<const u32x4*>(kr + ck);
-            const u32x4 al = *reinterpret_cast<const u32x4*>(kr + L::KH + ck);
+            u32x4 ahn = ah, aln = al;
+            if (st + 1 < NS) {
+                const int ck = kchunk<D>(ln, 2 * st + 2 + hf) * 8;
+                ahn = *reinterpret_cast<const u32x4*>(kr + ck);
+                aln = *reinterpret_cast<const u32x4*>(kr + L::KH + ck);
+            }
             sh = mfma16(ah, qh[st], sh);
             sx = mfma16(ah, ql[st], sx);
             sx = mfma16(al, qh[st], sx);
+            ah = ahn;
+            al = aln;
+        }
+        // issue order: the first two steps' reads, then per step its three
+        // products and the reads of the step after next
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+            if (st + 2 < NS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
         __builtin_amdgcn_s_setprio(0);
         floatx16 sacc;
@@ -436,18 +453,34 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
         }
         const unsigned short* vr = tiles + buf * BUF + 2 * L::KH;
         __builtin_amdgcn_s_setprio(1);
+        // step (blk, t) = step k = 2 blk + t; operands of step k+1 are read
+        // before the products of step k, and the products of a step go to one
+        // accumulator while the next step's go to another
+        auto vaddr = [&](int k) {
+            const int rho = min((k >> 1) * 32 + ln, D - 1);
+            return rho * KT + vchunk(rho, 2 * (k & 1) + hf) * 8;
+        };
+        u32x4 vh = *reinterpret_cast<const u32x4*>(vr + vaddr(0));
+        u32x4 vl = *reinterpret_cast<const u32x4*>(vr + L::VH + vaddr(0));
 #pragma unroll
-        for (int blk = 0; blk < NB; ++blk) {
-            const int rho = min(blk * 32 + ln, D - 1);
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int cv = rho * KT + vchunk(rho, 2 * t + hf) * 8;
-                const u32x4 vh = *reinterpret_cast<const u32x4*>(vr + cv);
-                const u32x4 vl = *reinterpret_cast<const u32x4*>(vr + L::VH + cv);
-                O[blk] = mfma16(vh, ph[t], O[blk]);
-                O[blk] = mfma16(vh, pl[t], O[blk]);
-                O[blk] = mfma16(vl, ph[t], O[blk]);
+        for (int k = 0; k < 2 * NB; ++k) {
+            u32x4 vhn = vh, vln = vl;
+            if (k + 1 < 2 * NB) {
+                vhn = *reinterpret_cast<const u32x4*>(vr + vaddr(k + 1));
+                vln = *reinterpret_cast<const u32x4*>(vr + L::VH + vaddr(k + 1));
             }
+            const int blk = k >> 1, t = k & 1;
+            O[blk] = mfma16(vh, ph[t], O[blk]);
+            O[blk] = mfma16(vh, pl[t], O[blk]);
+            O[blk] = mfma16(vl, ph[t], O[blk]);
+            vh = vhn;
+            vl = vln;
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int k = 0; k < 2 * NB; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+            if (k + 2 < 2 * NB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
         __builtin_amdgcn_s_setprio(0);
     }
