@@ -162,42 +162,73 @@ __global__ __launch_bounds__(FS_THREADS) void k_far_score(KParams p)
 // P_{s,63}, up to rounding), and the final mass into TZ[S].  Reads the local
 // (mx, zl) that far_score left in Ms/Rs and replaces them with M'_s and R_s.
 // ---------------------------------------------------------------------------
-constexpr int SCAN_AHEAD = 8;
+constexpr int SCAN_AHEAD = 8;   // theta_scan's prefetch depth
 
+// (M, Z) of a run of sub-chunks: the max and the mass against it; a run
+// with no evictions is (-inf, 0).  Runs a then b combine to the pair of the
+// concatenation: the online-softmax merge, an associative operation.
+struct MZ {
+    float M, Z;
+};
+__device__ __forceinline__ MZ mz_merge(MZ a, MZ b)
+{
+    const float M = fmaxf(a.M, b.M);
+    const float za = a.M == -INFINITY ? 0.f : a.Z * expf(a.M - M);
+    const float zb = b.M == -INFINITY ? 0.f : b.Z * expf(b.M - M);
+    return {M, za + zb};
+}
+
+// One wave per landmark row; lane l takes sub-chunks 4l .. 4l+3 (S <= 256):
+// the merge of each lane's run, an exclusive scan of the runs over the wave,
+// then every lane applies the recurrence above to its own sub-chunks from
+// the state before them (so M'_s and R_s are exactly the serial ones and Z
+// differs from the serial sum only in rounding order).
 __global__ __launch_bounds__(256) void k_mz_scan(KParams p)
 {
     const int64_t nhm = (int64_t)p.nh * p.m;
-    const int64_t ghb = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (ghb >= nhm) return;
+    const int lane = threadIdx.x & 63;
+    const int64_t ghb = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (ghb >= nhm) return;   // (uniform over the wave)
     const int64_t gh = ghb / p.m, b = ghb % p.m;
-    float M = p.mz[gh * 2 * p.m + b];
-    float Z = p.mz[gh * 2 * p.m + p.m + b];
-    for (int s0 = 0; s0 < p.S; s0 += SCAN_AHEAD) {
-        float mx[SCAN_AHEAD], zl[SCAN_AHEAD];
+    float mx[4], zl[4];
 #pragma unroll
-        for (int k = 0; k < SCAN_AHEAD; ++k) {
-            const int s = min(s0 + k, p.S - 1);
-            mx[k] = p.Ms[(int64_t)s * nhm + ghb];
-            zl[k] = p.Rs[(int64_t)s * nhm + ghb];
-        }
+    for (int k = 0; k < 4; ++k) {
+        const int s = min(4 * lane + k, p.S - 1);
+        mx[k] = p.Ms[(int64_t)s * nhm + ghb];
+        zl[k] = p.Rs[(int64_t)s * nhm + ghb];
+        if (4 * lane + k >= p.S) mx[k] = -INFINITY;   // past the last sub-chunk: empty
+    }
+    MZ run = {-INFINITY, 0.f};
 #pragma unroll
-        for (int k = 0; k < SCAN_AHEAD; ++k) {
-            const int s = s0 + k;
-            if (s < p.S) {
-                const float Mn = fmaxf(M, mx[k]);
-                const float R = (Mn == M) ? 1.0f : expf(M - Mn);
-                const int64_t at = (int64_t)s * nhm + ghb;
-                p.Ms[at] = Mn;
-                p.Rs[at] = R;
-                p.TZ[at] = Z;
-                Z = R * Z + (mx[k] == -INFINITY ? 0.f : zl[k] * expf(mx[k] - Mn));
-                M = Mn;
-            }
+    for (int k = 0; k < 4; ++k) run = mz_merge(run, MZ{mx[k], zl[k]});
+    // inclusive scan over the lanes, then shift to the exclusive prefix
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const MZ o = {__shfl_up(run.M, d, 64), __shfl_up(run.Z, d, 64)};
+        if (lane >= d) run = mz_merge(o, run);
+    }
+    MZ pre = {__shfl_up(run.M, 1, 64), __shfl_up(run.Z, 1, 64)};
+    if (lane == 0) pre = {-INFINITY, 0.f};
+    // the committed state before the call, then this lane's sub-chunks
+    MZ st = mz_merge(MZ{p.mz[gh * 2 * p.m + b], p.mz[gh * 2 * p.m + p.m + b]}, pre);
+    float M = st.M, Z = st.Z;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int s = 4 * lane + k;
+        if (s < p.S) {
+            const float Mn = fmaxf(M, mx[k]);
+            const float R = (Mn == M) ? 1.0f : expf(M - Mn);
+            const int64_t at = (int64_t)s * nhm + ghb;
+            p.Ms[at] = Mn;
+            p.Rs[at] = R;
+            p.TZ[at] = Z;
+            Z = R * Z + (mx[k] == -INFINITY ? 0.f : zl[k] * expf(mx[k] - Mn));
+            M = Mn;
+            // the mass after the last sub-chunk, which a commit stores: a call
+            // that resumes from the committed state then carries this value
+            if (s == p.S - 1) p.TZ[(int64_t)p.S * nhm + ghb] = Z;
         }
     }
-    // the mass after the last sub-chunk, which a commit stores: a call that
-    // resumes from the committed state then carries exactly this value
-    p.TZ[(int64_t)p.S * nhm + ghb] = Z;
 }
 
 // ---------------------------------------------------------------------------
@@ -368,7 +399,7 @@ hipError_t launch_far_score(const KParams& p, hipStream_t st)
 hipError_t launch_far_scan(const KParams& p, hipStream_t st)
 {
     const int64_t nhm = (int64_t)p.nh * p.m;
-    hipLaunchKernelGGL(k_mz_scan, dim3((unsigned)((nhm + 255) / 256)), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(k_mz_scan, dim3((unsigned)((nhm + 3) / 4)), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 

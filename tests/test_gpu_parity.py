@@ -363,10 +363,21 @@ def test_resume_from_copied_state():
     saved = {f: getattr(b, f).cpu() for f in swl.LayerState.FIELDS}
     c = swl.LayerState(b.geom, **{f: x.to("cuda") for f, x in saved.items()})
     rest = _prefill(cfg, c, q[cut:], k[cut:], v[cut:])
-    np.testing.assert_array_equal(np.concatenate([first, rest]), full)
+    # The far mass Z is a scan over the call's sub-chunks whose association
+    # order depends on where the call starts, so Z (and through it the
+    # outputs) agree up to rounding; the max M, the rescale R, Theta (an
+    # elementwise recurrence in sub-chunk order), the ring and meta are exact.
+    np.testing.assert_allclose(np.concatenate([first, rest]), full, rtol=1e-6, atol=1e-7)
     sa, sc = read_state(a), read_state(c)
     for f in sa:
-        np.testing.assert_array_equal(sa[f], sc[f])
+        if f == "mz":
+            m = cfg.m
+            za = sa[f].reshape(-1, 2, m)
+            zc = sc[f].reshape(-1, 2, m)
+            np.testing.assert_array_equal(za[:, 0], zc[:, 0])
+            np.testing.assert_allclose(za[:, 1], zc[:, 1], rtol=1e-6, atol=0)
+        else:
+            np.testing.assert_array_equal(sa[f], sc[f])
 
 
 def test_prefill_passes_match_one_long_call():
