@@ -2,8 +2,9 @@
 // value accumulator.  cortiq-engine 0.8.51 src/gpu_wgpu/o1_batch.rs,
 // o1b_far_e and o1b_far_commit, generalised from one sub-chunk to the S
 // sub-chunks of a call: the score and value products of every sub-chunk run
-// in parallel on fp32 MFMA, and only the per-landmark recurrences (M and Z
-// as scalars, Theta elementwise) walk the sub-chunks in order.
+// in parallel on MFMA (fp16 hi/lo splits, fp32 accuracy), and only the
+// per-landmark recurrences (M and Z as scalars, Theta elementwise) walk the
+// sub-chunks in order.
 //
 // Per sub-chunk s and landmark row (gh, b), with l_j the score of the key
 // evicted by chunk row j (rows j0 <= j < k_s evict):
@@ -19,65 +20,64 @@ namespace swl {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-__device__ __forceinline__ floatx16 fmfma(float a, float b, floatx16 c)
-{
-    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
-}
-
 __device__ __forceinline__ int fkap(int v, int hf) { return (v >> 2) * 8 + hf * 4 + (v & 3); }
 
-// The rows the sub-chunk's rows evict (chunk rows jlo <= j < ks; zero rows
-// elsewhere) into LDS rows of W + 4 floats: the key or value at position
-// len0 + r0 + j - w_g, from the ring (positions before the call) or from the
-// call's own rows.  Every load takes a clamped address and no condition, so
-// they are all in flight at once (a load under a per-lane condition waits for
-// every earlier one); the row selection happens at the store.
-template <int W, int NT>
-__device__ __forceinline__ void stage_evicted(float* lds, const float* ring, const float* rows,
-                                              const KParams& p, const GMeta& c, int g, int r0,
-                                              int jlo, int ks)
+// fp32-accurate products on fp16 matrix cores, as in the attention kernel:
+// x = hi + lo * 2^-11 (hi rounded toward zero, lo the scaled remainder), a
+// product is hi*hi + (hi*lo + lo*hi) * 2^-11 with fp32 accumulation.
+typedef _Float16 fhalf8 __attribute__((ext_vector_type(8)));
+typedef unsigned int fu32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int fu32x2 __attribute__((ext_vector_type(2)));
+constexpr float F_LO_UP = 2048.f;
+constexpr float F_LO_DOWN = 1.f / 2048.f;
+
+__device__ __forceinline__ floatx16 fmfma16(fu32x4 a, fu32x4 b, floatx16 c)
 {
-    constexpr int N = SUB * (W / 4);                 // 16-byte pieces
-    constexpr int PT = (N + NT - 1) / NT;            // per thread
-    // a native 4-wide vector: an array of HIP's float4 struct would sit in scratch memory
-    typedef float v4 __attribute__((ext_vector_type(4)));
-    const int tid = threadIdx.x;
-    v4 x[PT];
-#pragma unroll
-    for (int u = 0; u < PT; ++u) {
-        const int e = min(tid + u * NT, N - 1);
-        const int j = e / (W / 4), c4 = (e % (W / 4)) * 4;
-        const int pos = max(c.len0 + r0 + min(j, ks - 1) - c.wg, 0);
-        const float* ra = ring + ((int64_t)g * p.W + (c.head0 + min(pos, max(c.len0 - 1, 0))) % c.wg) * W;
-        const float* ia = rows + ((int64_t)max(pos - c.len0, 0) * p.G + g) * W;
-        x[u] = *reinterpret_cast<const v4*>((pos < c.len0 ? ra : ia) + c4);
-    }
-#pragma unroll
-    for (int u = 0; u < PT; ++u) {
-        const int e = tid + u * NT;
-        if (e < N) {
-            const int j = e / (W / 4), c4 = (e % (W / 4)) * 4;
-            const v4 z = {0.f, 0.f, 0.f, 0.f};
-            *reinterpret_cast<v4*>(lds + j * (W + 4) + c4) = (j >= jlo && j < ks) ? x[u] : z;
-        }
-    }
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(fhalf8, a),
+                                                  __builtin_bit_cast(fhalf8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ unsigned fpk16(float a, float b)
+{
+    return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+// hi/lo fp16 pairs of (a, b); lo scaled by 2^11 when SCALED
+template <bool SCALED>
+__device__ __forceinline__ void fsplit(float a, float b, unsigned& hi, unsigned& lo)
+{
+    hi = fpk16(a, b);
+    const float ra = a - (float)__builtin_bit_cast(_Float16, (unsigned short)(hi & 0xffffu));
+    const float rb = b - (float)__builtin_bit_cast(_Float16, (unsigned short)(hi >> 16));
+    lo = SCALED ? fpk16(ra * F_LO_UP, rb * F_LO_UP) : fpk16(ra, rb);
+}
+// 16-byte chunk c of row r of a [32][KD] fp16 tile sits at kswz(r, c): rows
+// that one read touches start in different banks
+template <int KD>
+__device__ __forceinline__ int kswz(int r, int c)
+{
+    constexpr int CPR = KD / 8, RPB = KD >= 128 ? 1 : 128 / KD, M = (CPR < 16 ? CPR : 16) - 1;
+    return c ^ ((r / RPB) & M);
 }
 
 // ---------------------------------------------------------------------------
 // far_score: L[s][gh*m+b][j] = scale <q~_{gh,b}, key evicted by row j>, -inf
 // for rows that do not evict, and per landmark row the local max mx and mass
 // zl = sum_j exp(l_j - mx) of the sub-chunk.  One block per (sub-chunk,
-// group); the evicted keys are staged in LDS.  MFMA C[hb][j] = Q~ K_e^T with
-// the d index of step st split over the two lane halves (hf*D/2 + st), so
-// both operands are row-contiguous per lane.
+// group); the evicted keys are staged in LDS as fp16 hi/lo.  MFMA
+// C[hb][j] = Q~ K_e^T on v_mfma_f32_32x32x16_f16 (three split products per
+// k-step; lane (row, hf) holds columns 16 st + 8 hf .. +7 of its row).
 // ---------------------------------------------------------------------------
 constexpr int FS_THREADS = 256;
 
 template <int D>
 __global__ __launch_bounds__(FS_THREADS) void k_far_score(KParams p)
 {
-    constexpr int LD = D + 4;
-    __shared__ float ek[SUB][LD];
+    constexpr int KD = D < 16 ? 16 : D;    // key width padded to whole k-steps
+    constexpr int NS = KD / 16;
+    constexpr int KH = 32 * KD;            // halves of one [32][KD] tile
+    // evicted keys of the sub-chunk as fp16 hi/lo: rows j = 32 jt + r in
+    // tile jt (hi at ek + jt * 2 KH, lo KH further), zero for rows that do
+    // not evict and for the columns past D
+    __shared__ __align__(16) unsigned short ek[2 * 2 * KH];
     const int w = xcd_work_item(blockIdx.x, p.S * p.G);
     const int s = w % p.S, g = w / p.S;
     const int r0 = s * SUB;
@@ -88,7 +88,38 @@ __global__ __launch_bounds__(FS_THREADS) void k_far_score(KParams p)
     const int hm = p.H * p.m;
     const int64_t nhm = (int64_t)p.nh * p.m;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, ln = lane & 31;
-    stage_evicted<D, FS_THREADS>(&ek[0][0], p.ring_k, p.k, p, c, g, r0, jlo, ks);
+    {
+        // 4-column pieces of the 64 rows: clamped unconditional loads (all in
+        // flight at once), the row and column selection at the store
+        typedef float v4 __attribute__((ext_vector_type(4)));
+        constexpr int N = SUB * (KD / 4);
+        constexpr int PT = (N + FS_THREADS - 1) / FS_THREADS;
+        v4 x[PT];
+#pragma unroll
+        for (int u = 0; u < PT; ++u) {
+            const int e = min(tid + u * FS_THREADS, N - 1);
+            const int j = e / (KD / 4), c4 = min((e % (KD / 4)) * 4, D - 4);
+            const int pos = max(c.len0 + r0 + min(j, ks - 1) - c.wg, 0);
+            const float* ra = p.ring_k + ((int64_t)g * p.W + (c.head0 + min(pos, max(c.len0 - 1, 0))) % c.wg) * D;
+            const float* ia = p.k + ((int64_t)max(pos - c.len0, 0) * p.G + g) * D;
+            x[u] = *reinterpret_cast<const v4*>((pos < c.len0 ? ra : ia) + c4);
+        }
+#pragma unroll
+        for (int u = 0; u < PT; ++u) {
+            const int e = tid + u * FS_THREADS;
+            if (e < N) {
+                const int j = e / (KD / 4), c4 = (e % (KD / 4)) * 4;
+                const bool live = (j >= jlo) & (j < ks) & (c4 < D);
+                unsigned h0, l0, h1, l1;
+                fsplit<true>(live ? x[u].x : 0.f, live ? x[u].y : 0.f, h0, l0);
+                fsplit<true>(live ? x[u].z : 0.f, live ? x[u].w : 0.f, h1, l1);
+                const int jt = j >> 5, r = j & 31;
+                unsigned short* t = ek + jt * 2 * KH + r * KD + kswz<KD>(r, c4 >> 3) * 8 + (c4 & 4);
+                *reinterpret_cast<fu32x2*>(t) = fu32x2{h0, h1};
+                *reinterpret_cast<fu32x2*>(t + KH) = fu32x2{l0, l1};
+            }
+        }
+    }
     __syncthreads();
     float* L = p.E + ((int64_t)s * nhm + (int64_t)g * hm) * SUB;
     float* MX = p.Ms + (int64_t)s * nhm + (int64_t)g * hm;   // local max (the scan overwrites)
@@ -96,29 +127,48 @@ __global__ __launch_bounds__(FS_THREADS) void k_far_score(KParams p)
     const int nht = (hm + 31) / 32;
     for (int ht = wave; ht < nht; ht += FS_THREADS / 64) {
         const int hb_a = ht * 32 + ln;   // A row of this lane
-        float qa[D / 2];
+        // landmark query halves: q~[hb][16 st + 8 hf + e]
+        fu32x4 qah[NS], qal[NS];
         {
-            const float* qr = p.q_tilde + ((int64_t)g * hm + min(hb_a, hm - 1)) * D + hf * (D / 2);
+            const float* qr = p.q_tilde + ((int64_t)g * hm + min(hb_a, hm - 1)) * D;
 #pragma unroll
-            for (int st = 0; st < D / 2; st += 4) {
-                const float4 x = *reinterpret_cast<const float4*>(qr + st);
-                qa[st] = x.x; qa[st + 1] = x.y; qa[st + 2] = x.z; qa[st + 3] = x.w;
+            for (int st = 0; st < NS; ++st) {
+                const int d0 = 16 * st + 8 * hf;
+                float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = x;
+                if (d0 < D) {
+                    x = *reinterpret_cast<const float4*>(qr + d0);
+                    y = *reinterpret_cast<const float4*>(qr + d0 + 4);
+                }
+                unsigned h[4], l[4];
+                fsplit<true>(x.x, x.y, h[0], l[0]);
+                fsplit<true>(x.z, x.w, h[1], l[1]);
+                fsplit<true>(y.x, y.y, h[2], l[2]);
+                fsplit<true>(y.z, y.w, h[3], l[3]);
+                qah[st] = fu32x4{h[0], h[1], h[2], h[3]};
+                qal[st] = fu32x4{l[0], l[1], l[2], l[3]};
             }
         }
         floatx16 acc[2];
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt) {
+            floatx16 sh, sx;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[jt][v] = 0.f;
-            const float* kr = &ek[jt * 32 + ln][hf * (D / 2)];
-#pragma unroll
-            for (int st = 0; st < D / 2; st += 4) {
-                const float4 b = *reinterpret_cast<const float4*>(kr + st);
-                acc[jt] = fmfma(qa[st], b.x, acc[jt]);
-                acc[jt] = fmfma(qa[st + 1], b.y, acc[jt]);
-                acc[jt] = fmfma(qa[st + 2], b.z, acc[jt]);
-                acc[jt] = fmfma(qa[st + 3], b.w, acc[jt]);
+            for (int v = 0; v < 16; ++v) {
+                sh[v] = 0.f;
+                sx[v] = 0.f;
             }
+            const unsigned short* kr = ek + jt * 2 * KH + ln * KD;
+#pragma unroll
+            for (int st = 0; st < NS; ++st) {
+                const int ck = kswz<KD>(ln, 2 * st + hf) * 8;
+                const fu32x4 bh = *reinterpret_cast<const fu32x4*>(kr + ck);
+                const fu32x4 bl = *reinterpret_cast<const fu32x4*>(kr + KH + ck);
+                sh = fmfma16(qah[st], bh, sh);
+                sx = fmfma16(qah[st], bl, sx);
+                sx = fmfma16(qal[st], bh, sx);
+            }
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[jt][v] = fmaf(sx[v], F_LO_DOWN, sh[v]);
         }
         // lane holds rows hb = ht*32 + kappa(v, hf), columns j = jt*32 + ln
         float mx[16];
@@ -162,7 +212,7 @@ __global__ __launch_bounds__(FS_THREADS) void k_far_score(KParams p)
 // P_{s,63}, up to rounding), and the final mass into TZ[S].  Reads the local
 // (mx, zl) that far_score left in Ms/Rs and replaces them with M'_s and R_s.
 // ---------------------------------------------------------------------------
-constexpr int SCAN_AHEAD = 8;   // theta_scan's prefetch depth
+constexpr int SCAN_AHEAD = 32;  // theta_scan's prefetch depth
 
 // (M, Z) of a run of sub-chunks: the max and the mass against it; a run
 // with no evictions is (-inf, 0).  Runs a then b combine to the pair of the
@@ -234,17 +284,23 @@ __global__ __launch_bounds__(256) void k_mz_scan(KParams p)
 // ---------------------------------------------------------------------------
 // dtheta: per (sub-chunk, group): E = exp(l - M'_s) and P = R_s Z_{s-1} +
 // prefix_j E for every landmark row (written for the attention epilogue and
-// the commit), and TH[s][gh*m+b][t] = sum_j E_bj v_evicted(j)[t] on MFMA
-// (C[b][t], step st pairs rows hf*32 + st of E and of the evicted values,
-// so each lane's E row is 32 contiguous values whose prefix is a register
-// loop).  The evicted values are staged in LDS.
+// the commit), and TH[s][gh*m+b][t] = sum_j E_bj v_evicted(j)[t] on fp16
+// MFMA with hi/lo splits (C[b][t]; each lane holds rows hf*32 .. +31 of its
+// E row, so its prefix is a register loop, and k-step st takes rows
+// 32 hf + 8 st .. +7).  E is scaled by 2^12 before the split so that the
+// fp16 remainders of its small values stay far above their absolute floor;
+// the result is scaled back exactly.  The evicted values are staged in LDS
+// transposed.
 // ---------------------------------------------------------------------------
 template <int DV>
 __global__ __launch_bounds__(256) void k_dtheta(KParams p)
 {
     constexpr int NT = DV >= 32 ? DV / 32 : 1;   // 32-column output tiles
-    constexpr int LD = DV + 4;
-    __shared__ float ve[SUB][LD];
+    // the evicted values transposed, fp16 hi/lo: row t holds the 64 rows j
+    // (chunk c = rows 8c .. 8c+7 at chunk c ^ ((t >> 1) & 7)), zero for rows
+    // that do not evict
+    constexpr int VH = DV * SUB;
+    __shared__ __align__(16) unsigned short vt[2 * VH];
     const int w = xcd_work_item(blockIdx.x, p.S * p.G);
     const int s = w % p.S, g = w / p.S;
     const int r0 = s * SUB;
@@ -255,7 +311,44 @@ __global__ __launch_bounds__(256) void k_dtheta(KParams p)
     const int hm = p.H * p.m;
     const int64_t nhm = (int64_t)p.nh * p.m;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, ln = lane & 31;
-    stage_evicted<DV, 256>(&ve[0][0], p.ring_v, p.v, p, c, g, r0, jlo, ks);
+    {
+        // units of two rows (2 jp, 2 jp + 1) x four columns: clamped
+        // unconditional loads, then per column one fp16 pair of each half
+        typedef float v4 __attribute__((ext_vector_type(4)));
+        constexpr int N = (SUB / 2) * (DV / 4);
+        constexpr int PT = (N + 255) / 256;
+        v4 x[PT][2];
+#pragma unroll
+        for (int u = 0; u < PT; ++u) {
+            const int e = min(tid + u * 256, N - 1);
+            const int jp = e / (DV / 4), c4 = (e % (DV / 4)) * 4;
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int j = 2 * jp + r;
+                const int pos = max(c.len0 + r0 + min(j, ks - 1) - c.wg, 0);
+                const float* ra = p.ring_v + ((int64_t)g * p.W + (c.head0 + min(pos, max(c.len0 - 1, 0))) % c.wg) * DV;
+                const float* ia = p.v + ((int64_t)max(pos - c.len0, 0) * p.G + g) * DV;
+                x[u][r] = *reinterpret_cast<const v4*>((pos < c.len0 ? ra : ia) + c4);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < PT; ++u) {
+            const int e = tid + u * 256;
+            if (e < N) {
+                const int jp = e / (DV / 4), c4 = (e % (DV / 4)) * 4;
+                const bool l0 = (2 * jp >= jlo) & (2 * jp < ks), l1 = (2 * jp + 1 >= jlo) & (2 * jp + 1 < ks);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int t = c4 + q;
+                    unsigned hi, lo;
+                    fsplit<false>(l0 ? x[u][0][q] : 0.f, l1 ? x[u][1][q] : 0.f, hi, lo);
+                    const int at = t * SUB + (((jp >> 2) ^ ((t >> 1) & 7)) << 3) + ((2 * jp) & 7);
+                    *reinterpret_cast<unsigned*>(vt + at) = hi;
+                    *reinterpret_cast<unsigned*>(vt + VH + at) = lo;
+                }
+            }
+        }
+    }
     __syncthreads();
     const int64_t row0 = (int64_t)s * nhm + (int64_t)g * hm;   // landmark row (s, g*H*m)
     const int nht = (hm + 31) / 32;
@@ -302,20 +395,35 @@ __global__ __launch_bounds__(256) void k_dtheta(KParams p)
                 }
             }
         }
+        // E * 2^12 as fp16 halves: k-step st takes rows j = 32 hf + 8 st + e
+        // of this lane's landmark row (its own e[8 st + e])
+        fu32x4 eh[4], el[4];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            unsigned h[4], l[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                fsplit<false>(e[8 * st + 2 * q] * 4096.f, e[8 * st + 2 * q + 1] * 4096.f, h[q], l[q]);
+            eh[st] = fu32x4{h[0], h[1], h[2], h[3]};
+            el[st] = fu32x4{l[0], l[1], l[2], l[3]};
+        }
         floatx16 acc[NT];
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt)
+        for (int tt = 0; tt < NT; ++tt) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[tt][v] = 0.f;
+            const int t = min(tt * 32 + ln, DV - 1);
 #pragma unroll
-        for (int st = 0; st < 32; ++st) {
-            const float* vr = &ve[hf * 32 + st][0];
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt) {
-                const int t = tt * 32 + ln;
-                const float b = t < DV ? vr[t] : 0.f;
-                acc[tt] = fmfma(e[st], b, acc[tt]);
+            for (int st = 0; st < 4; ++st) {
+                const int at = t * SUB + (((4 * hf + st) ^ ((t >> 1) & 7)) << 3);
+                const fu32x4 vh = *reinterpret_cast<const fu32x4*>(vt + at);
+                const fu32x4 vl = *reinterpret_cast<const fu32x4*>(vt + VH + at);
+                acc[tt] = fmfma16(eh[st], vh, acc[tt]);
+                acc[tt] = fmfma16(eh[st], vl, acc[tt]);
+                acc[tt] = fmfma16(el[st], vh, acc[tt]);
             }
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[tt][v] *= 1.f / 4096.f;
         }
         // lane holds rows hb = ht*32 + kappa(v, hf), columns t = tt*32 + ln
 #pragma unroll
