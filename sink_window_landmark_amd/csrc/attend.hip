@@ -264,17 +264,18 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
     constexpr int NW = AT_THREADS / 64;
     constexpr int LDF = D + 4;                // fp32 row stride of the epilogue's tiles
     constexpr int NEAR_BYTES = 2 * L::BYTES;
-    constexpr int FAR_BYTES = 2 * 2 * KT * LDF * 4 + HPB * 2 * 64 * 4;
+    constexpr int KTB = 2 * 2 * L::KH * 2;     // landmark keys as two fp16 hi/lo K tiles
+    constexpr int FAR_BYTES = KTB + 2 * KT * LDF * 4 + HPB * 2 * 64 * 4;
     constexpr int SMEM = NEAR_BYTES > FAR_BYTES ? NEAR_BYTES : FAR_BYTES;
     constexpr float LOG2E = 1.4426950408889634f;
     __shared__ __align__(16) unsigned char smem[SMEM];
     unsigned short* const tiles = reinterpret_cast<unsigned short*>(smem);
-    // the epilogue reuses the memory: landmark keys (m <= 64 rows) and the
-    // sub-chunk's evicted values (64 rows) in fp32
-    float(*const Ks)[LDF] = reinterpret_cast<float(*)[LDF]>(smem);
-    float(*const Vs)[LDF] = reinterpret_cast<float(*)[LDF]>(smem + 2 * KT * LDF * 4);
+    // the epilogue reuses the memory: landmark keys (m <= 64 rows) as fp16
+    // hi/lo K tiles and the sub-chunk's evicted values (64 rows) in fp32
+    unsigned short* const Kt = reinterpret_cast<unsigned short*>(smem);
+    float(*const Vs)[LDF] = reinterpret_cast<float(*)[LDF]>(smem + KTB);
     // and the post-sub-chunk max M' and rescale R of each head's landmarks
-    float(*const MR)[2][64] = reinterpret_cast<float(*)[2][64]>(smem + 4 * KT * LDF * 4);
+    float(*const MR)[2][64] = reinterpret_cast<float(*)[2][64]>(smem + KTB + 2 * KT * LDF * 4);
 
     // work item = (head group, group, sub-chunk), sub-chunk fastest, dealt
     // to XCDs in contiguous runs
@@ -497,13 +498,21 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
         // evicted values of the sub-chunk -> Vs rows 0..63 (zero where none)
         for (int e = tid; e < 2 * KT * (D / 4); e += AT_THREADS) {
             const int row = e / (D / 4), c4 = (e % (D / 4)) * 4;
-            float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
-            if (row < m)
-                kx = *reinterpret_cast<const float4*>(p.k_tilde + ((int64_t)g * m + row) * D + c4);
+            float4 vx = make_float4(0.f, 0.f, 0.f, 0.f);
             if (row >= jlo && row < ks)
                 vx = *reinterpret_cast<const float4*>(val_row(p, c, g, c.len0 + r0 + row - c.wg) + c4);
-            *reinterpret_cast<float4*>(&Ks[row][c4]) = kx;
             *reinterpret_cast<float4*>(&Vs[row][c4]) = vx;
+        }
+        // landmark row a = 32 at + r of K tile at, columns past D zero
+        for (int e = tid; e < 2 * KT * (KD / 4); e += AT_THREADS) {
+            const int row = e / (KD / 4), c4 = (e % (KD / 4)) * 4;
+            const float4 kx = *reinterpret_cast<const float4*>(p.k_tilde + ((int64_t)g * m + min(row, m - 1)) * D + min(c4, D - 4));
+            const bool live = (row < m) & (c4 < D);
+            const Split<true> s0(live ? kx.x : 0.f, live ? kx.y : 0.f), s1(live ? kx.z : 0.f, live ? kx.w : 0.f);
+            const int r = row & 31;
+            unsigned short* t = Kt + (row >> 5) * 2 * L::KH + r * KD + kchunk<D>(r, c4 >> 3) * 8 + (c4 & 4);
+            *reinterpret_cast<u32x2*>(t) = u32x2{s0.hi, s1.hi};
+            *reinterpret_cast<u32x2*>(t + L::KH) = u32x2{s0.lo, s1.lo};
         }
         for (int e = tid; e < HPB * 2 * 64; e += AT_THREADS) {
             const int hh = e >> 7, which = (e >> 6) & 1, b = e & 63;
@@ -524,35 +533,26 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
             const float* Pt = p.P + (((int64_t)s * p.nh + gh) * SUB + i) * 64 + hf * 4;   // [b] of row i
             const float* Th = p.theta_prev + (int64_t)s * p.theta_prev_stride + (int64_t)gh * m * D;
 
-            // Q^T in fp32 for the epilogue's products: q[r0+i][gh][hf*D/2 + st]
-            float qf[D / 2];
-            {
-                const float qs = p.scale * LOG2E;
-                const bool ok = active && i < ks;
-                const float* qr = p.q + ((int64_t)(r0 + i) * p.nh + gh) * D + hf * (D / 2);
-#pragma unroll
-                for (int st = 0; st < D / 2; st += 4) {
-                    const float4 x = ok ? *reinterpret_cast<const float4*>(qr + st) : make_float4(0.f, 0.f, 0.f, 0.f);
-                    qf[st] = x.x * qs;
-                    qf[st + 1] = x.y * qs;
-                    qf[st + 2] = x.z * qs;
-                    qf[st + 3] = x.w * qs;
-                }
-            }
-            // f^T = K~ Q^T (log2 units), e = exp2(f - fmax)
+            // f^T = K~ Q^T (log2 units) from the near part's Q^T halves, three
+            // split products per k-step; e = exp2(f - fmax)
             floatx16 ef[MT];
 #pragma unroll
             for (int at = 0; at < MT; ++at) {
-                zero16(ef[at]);
-                const float* kr = &Ks[at * 32 + ln][hf * (D / 2)];
+                floatx16 fh, fx;
+                zero16(fh);
+                zero16(fx);
+                const unsigned short* kr = Kt + at * 2 * L::KH + ln * KD;
 #pragma unroll
-                for (int st = 0; st < D / 2; st += 4) {
-                    const float4 a = *reinterpret_cast<const float4*>(kr + st);
-                    ef[at] = mfma32(a.x, qf[st], ef[at]);
-                    ef[at] = mfma32(a.y, qf[st + 1], ef[at]);
-                    ef[at] = mfma32(a.z, qf[st + 2], ef[at]);
-                    ef[at] = mfma32(a.w, qf[st + 3], ef[at]);
+                for (int st = 0; st < NS; ++st) {
+                    const int ck = kchunk<D>(ln, 2 * st + hf) * 8;
+                    const u32x4 ah = *reinterpret_cast<const u32x4*>(kr + ck);
+                    const u32x4 al = *reinterpret_cast<const u32x4*>(kr + L::KH + ck);
+                    fh = mfma16(ah, qh[st], fh);
+                    fx = mfma16(ah, ql[st], fx);
+                    fx = mfma16(al, qh[st], fx);
                 }
+#pragma unroll
+                for (int v = 0; v < 16; ++v) ef[at][v] = fmaf(fx[v], LO_DOWN, fh[v]);
             }
             float fmax = -INFINITY;
 #pragma unroll
