@@ -138,6 +138,21 @@ struct Split {
     }
 };
 
+// hi/lo fp16 pairs of (a, b) with a = hi + lo, the remainders taken by
+// v_fma_mix_f32 straight from the packed fp16 halves (one instruction per
+// element instead of a conversion and a subtraction; exact, as a - hi is)
+struct SplitMix {
+    unsigned hi, lo;
+    __device__ __forceinline__ SplitMix(float a, float b)
+    {
+        hi = pk16(a, b);
+        float ra, rb;
+        asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(ra) : "v"(hi), "v"(a));
+        asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(rb) : "v"(hi), "v"(b));
+        lo = pk16(ra, rb);
+    }
+};
+
 // Position of key bit 2 and bit 3 swapped: the order of a tile's keys in the
 // V^T rows (an involution).
 __device__ __forceinline__ int kperm(int k) { return (k & ~12) | ((k >> 1) & 4) | ((k << 1) & 8); }
@@ -447,8 +462,8 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
         u32x4 ph[2], pl[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const Split<false> s0(sacc[8 * t], sacc[8 * t + 1]), s1(sacc[8 * t + 2], sacc[8 * t + 3]);
-            const Split<false> s2(sacc[8 * t + 4], sacc[8 * t + 5]), s3(sacc[8 * t + 6], sacc[8 * t + 7]);
+            const SplitMix s0(sacc[8 * t], sacc[8 * t + 1]), s1(sacc[8 * t + 2], sacc[8 * t + 3]);
+            const SplitMix s2(sacc[8 * t + 4], sacc[8 * t + 5]), s3(sacc[8 * t + 6], sacc[8 * t + 7]);
             ph[t] = u32x4{s0.hi, s1.hi, s2.hi, s3.hi};
             pl[t] = u32x4{s0.lo, s1.lo, s2.lo, s3.lo};
         }
