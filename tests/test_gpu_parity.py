@@ -350,6 +350,23 @@ def test_negative_mu_guard_and_rect(rect):
     check_state(read_state(st), orc)
 
 
+def test_no_sinks():
+    """A layer without sinks: no sink tiles, the window tiles start the key
+    tiles, and the decode path runs on from the prefilled state."""
+    banner("no sinks")
+    cfg = synth.Config("nosink", G=2, H=2, d=32, dv=32, ns=0, W=96, m=8, rows=400,
+                       windows=(70, 96))
+    host = synth.make_state(cfg)
+    T = 360
+    q, k, v = synth.rows(cfg, 0, cfg.rows)
+    st = _state(cfg, host)
+    got = _prefill(cfg, st, q[:T], k[:T], v[:T])
+    orc = oracle.from_config(cfg, host)
+    check_out(got, orc.step(q[:T], k[:T], v[:T]), "prefill")
+    check_out(_tokens(cfg, st, q[T:], k[T:], v[T:]), orc.step(q[T:], k[T:], v[T:]), "tokens")
+    check_state(read_state(st), orc)
+
+
 def test_resume_from_copied_state():
     banner("resume from a copied state")
     cfg = synth.SMALL.replace(rows=1500, W=256, m=16)
