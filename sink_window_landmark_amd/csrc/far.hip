@@ -148,28 +148,41 @@ __global__ __launch_bounds__(FS_THREADS) void k_far_score(KParams p)
                 qal[st] = fu32x4{l[0], l[1], l[2], l[3]};
             }
         }
-        floatx16 acc[2];
+        // both 32-row tiles of evicted keys in one k-step loop: each step's
+        // query halves feed six products on four accumulators, and the LDS
+        // reads run two steps ahead of their products
+        floatx16 sh[2], sx[2];
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-            floatx16 sh, sx;
+        for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                sh[v] = 0.f;
-                sx[v] = 0.f;
-            }
-            const unsigned short* kr = ek + jt * 2 * KH + ln * KD;
-#pragma unroll
-            for (int st = 0; st < NS; ++st) {
-                const int ck = kswz<KD>(ln, 2 * st + hf) * 8;
-                const fu32x4 bh = *reinterpret_cast<const fu32x4*>(kr + ck);
-                const fu32x4 bl = *reinterpret_cast<const fu32x4*>(kr + KH + ck);
-                sh = fmfma16(qah[st], bh, sh);
-                sx = fmfma16(qah[st], bl, sx);
-                sx = fmfma16(qal[st], bh, sx);
+                sh[jt][v] = 0.f;
+                sx[jt][v] = 0.f;
             }
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[jt][v] = fmaf(sx[v], F_LO_DOWN, sh[v]);
+        for (int st = 0; st < NS; ++st) {
+            const int ck = kswz<KD>(ln, 2 * st + hf) * 8;
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt) {
+                const unsigned short* kr = ek + jt * 2 * KH + ln * KD + ck;
+                const fu32x4 bh = *reinterpret_cast<const fu32x4*>(kr);
+                const fu32x4 bl = *reinterpret_cast<const fu32x4*>(kr + KH);
+                sh[jt] = fmfma16(qah[st], bh, sh[jt]);
+                sx[jt] = fmfma16(qah[st], bl, sx[jt]);
+                sx[jt] = fmfma16(qal[st], bh, sx[jt]);
+            }
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+            if (st + 2 < NS) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        }
+        floatx16 acc[2];
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[jt][v] = fmaf(sx[jt][v], F_LO_DOWN, sh[jt][v]);
         // lane holds rows hb = ht*32 + kappa(v, hf), columns j = jt*32 + ln
         float mx[16];
 #pragma unroll
@@ -407,14 +420,18 @@ __global__ __launch_bounds__(256) void k_dtheta(KParams p)
             eh[st] = fu32x4{h[0], h[1], h[2], h[3]};
             el[st] = fu32x4{l[0], l[1], l[2], l[3]};
         }
+        // k-step outer, column tiles inner: consecutive products go to
+        // different accumulators, and the LDS reads run two steps ahead
         floatx16 acc[NT];
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
+        for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[tt][v] = 0.f;
-            const int t = min(tt * 32 + ln, DV - 1);
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {
+        for (int st = 0; st < 4; ++st) {
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                const int t = min(tt * 32 + ln, DV - 1);
                 const int at = t * SUB + (((4 * hf + st) ^ ((t >> 1) & 7)) << 3);
                 const fu32x4 vh = *reinterpret_cast<const fu32x4*>(vt + at);
                 const fu32x4 vl = *reinterpret_cast<const fu32x4*>(vt + VH + at);
@@ -422,9 +439,17 @@ __global__ __launch_bounds__(256) void k_dtheta(KParams p)
                 acc[tt] = fmfma16(eh[st], vl, acc[tt]);
                 acc[tt] = fmfma16(el[st], vh, acc[tt]);
             }
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int k = 0; k < 4 * NT; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+            if (k + 2 < 4 * NT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[tt][v] *= 1.f / 4096.f;
-        }
         // lane holds rows hb = ht*32 + kappa(v, hf), columns t = tt*32 + ln
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
