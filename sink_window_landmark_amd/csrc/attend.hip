@@ -23,12 +23,13 @@
 // (the GQA reuse of the pages' Metal and Dory kernels).
 //
 // fp32 products on fp16 matrix cores (near part).  Each fp32 operand x is
-// split into fp16 halves, x = hi + lo * 2^-sc: hi is x rounded toward zero
-// and lo the exact remainder, scaled by 2^11 (sc = 11) for q and k so that
-// it stays a normal number.  A product is hi*hi + (hi*lo + lo*hi) * 2^-sc on
-// v_mfma_f32_32x32x16_f16 with fp32 accumulation (the hi*lo terms of the
-// scores in an accumulator of their own); the dropped lo*lo term and the
-// rounding of lo leave about 2^-20 relative error per product, at a fifth of
+// split into fp16 halves, x = hi + lo * 2^-sc: hi is x rounded to nearest
+// and lo the remainder rounded to nearest, scaled by 2^11 (sc = 11) for q
+// and k so that it stays a normal number.  A product is
+// hi*hi + (hi*lo + lo*hi) * 2^-sc on v_mfma_f32_32x32x16_f16 with fp32
+// accumulation (the hi*lo terms of the scores in an accumulator of their
+// own); the dropped lo*lo term and the rounding of lo leave at most
+// 3 * 2^-22 of |a*b| per product a*b, at a fifth of
 // the fp32 MFMA's time for the three products.  Values split unscaled (an
 // absolute error floor of 2^-24), and the softmax weights are kept in
 // (0, 2^15] with a sum of at least 2^8 so that theirs stays far below that.  Range: |k| and
@@ -111,11 +112,6 @@ __device__ __forceinline__ void zero16(floatx16& x)
     for (int v = 0; v < 16; ++v) x[v] = 0.f;
 }
 
-// (a, b) as an fp16 pair rounded toward zero, a in the low half
-__device__ __forceinline__ unsigned pk16(float a, float b)
-{
-    return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a, b));
-}
 __device__ __forceinline__ float half0(unsigned x)
 {
     return (float)__builtin_bit_cast(_Float16, (unsigned short)(x & 0xffffu));
@@ -125,16 +121,31 @@ __device__ __forceinline__ float half1(unsigned x)
     return (float)__builtin_bit_cast(_Float16, (unsigned short)(x >> 16));
 }
 
+// (a, b) as an fp16 pair rounded to nearest, a in the low half
+__device__ __forceinline__ unsigned pk16n(float a, float b)
+{
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 h = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(unsigned, h);
+}
+
 // hi/lo fp16 pairs of (a, b): a = hi + lo / 2^11 when SCALED, else hi + lo
-// (the remainder a - hi is exact in fp32)
+// (the remainder a - hi is exact in fp32).  Both halves round to nearest:
+// the split's relative error is at most 2^-22, a fourth of what rounding
+// toward zero leaves, and it is what scores of large magnitude carry into
+// the weights.  The empty asm pins a and b as rounded fp32 values: without
+// it the compiler may contract a caller's product into one use (the fused
+// conversion v_fma_mixlo_f16 of the unrounded product) but not the other,
+// and the two roundings of hi then differ by an fp16 ulp now and then.
 template <bool SCALED>
 struct Split {
     unsigned hi, lo;
     __device__ __forceinline__ Split(float a, float b)
     {
-        hi = pk16(a, b);
+        asm("" : "+v"(a), "+v"(b));
+        hi = pk16n(a, b);
         const float ra = a - half0(hi), rb = b - half1(hi);
-        lo = SCALED ? pk16(ra * LO_UP, rb * LO_UP) : pk16(ra, rb);
+        lo = SCALED ? pk16n(ra * LO_UP, rb * LO_UP) : pk16n(ra, rb);
     }
 };
 
@@ -145,11 +156,11 @@ struct SplitMix {
     unsigned hi, lo;
     __device__ __forceinline__ SplitMix(float a, float b)
     {
-        hi = pk16(a, b);
+        hi = pk16n(a, b);
         float ra, rb;
         asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(ra) : "v"(hi), "v"(a));
         asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(rb) : "v"(hi), "v"(b));
-        lo = pk16(ra, rb);
+        lo = pk16n(ra, rb);
     }
 };
 

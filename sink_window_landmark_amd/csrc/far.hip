@@ -23,7 +23,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ int fkap(int v, int hf) { return (v >> 2) * 8 + hf * 4 + (v & 3); }
 
 // fp32-accurate products on fp16 matrix cores, as in the attention kernel:
-// x = hi + lo * 2^-11 (hi rounded toward zero, lo the scaled remainder), a
+// x = hi + lo * 2^-11 (hi and the scaled remainder lo rounded to nearest), a
 // product is hi*hi + (hi*lo + lo*hi) * 2^-11 with fp32 accumulation.
 typedef _Float16 fhalf8 __attribute__((ext_vector_type(8)));
 typedef unsigned int fu32x4 __attribute__((ext_vector_type(4)));
@@ -36,18 +36,25 @@ __device__ __forceinline__ floatx16 fmfma16(fu32x4 a, fu32x4 b, floatx16 c)
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(fhalf8, a),
                                                   __builtin_bit_cast(fhalf8, b), c, 0, 0, 0);
 }
-__device__ __forceinline__ unsigned fpk16(float a, float b)
+// (a, b) as an fp16 pair rounded to nearest, a in the low half
+__device__ __forceinline__ unsigned fpk16n(float a, float b)
 {
-    return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a, b));
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 h = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(unsigned, h);
 }
-// hi/lo fp16 pairs of (a, b); lo scaled by 2^11 when SCALED
+// hi/lo fp16 pairs of (a, b), both rounded to nearest (about 2^-22 error
+// per product); lo scaled by 2^11 when SCALED.  a and b are pinned as
+// rounded fp32 values first, so that a product in the caller cannot be
+// contracted into one rounding of hi and not into the other.
 template <bool SCALED>
 __device__ __forceinline__ void fsplit(float a, float b, unsigned& hi, unsigned& lo)
 {
-    hi = fpk16(a, b);
+    asm("" : "+v"(a), "+v"(b));
+    hi = fpk16n(a, b);
     const float ra = a - (float)__builtin_bit_cast(_Float16, (unsigned short)(hi & 0xffffu));
     const float rb = b - (float)__builtin_bit_cast(_Float16, (unsigned short)(hi >> 16));
-    lo = SCALED ? fpk16(ra * F_LO_UP, rb * F_LO_UP) : fpk16(ra, rb);
+    lo = SCALED ? fpk16n(ra * F_LO_UP, rb * F_LO_UP) : fpk16n(ra, rb);
 }
 // 16-byte chunk c of row r of a [32][KD] fp16 tile sits at kswz(r, c): rows
 // that one read touches start in different banks

@@ -60,7 +60,12 @@ def check_out(got, want, what="out"):
     e = excess(got, want)
     md = float(np.max(np.abs(got.astype(np.float64) - want))) if got.size else 0.0
     print(f"  {what}: max|d| {md:.3e}  excess {e:.3e}", flush=True)
-    assert e <= 0, f"{what}: beyond tolerance by {e:.3e} (max|d| {md:.3e})"
+    if e > 0:
+        w = np.asarray(want, np.float64)
+        at = np.unravel_index(np.argmax(np.abs(got - w) - (ATOL + RTOL * np.abs(w))), w.shape)
+        raise AssertionError(f"{what}: beyond tolerance by {e:.3e} (max|d| {md:.3e}); worst at "
+                             f"{tuple(int(i) for i in at)}: got {float(got[at]):.8g}, "
+                             f"want {float(w[at]):.8g}, max|want| {float(np.max(np.abs(w))):.4g}")
 
 
 def check_state(gpu, orc, ring=True):

@@ -13,8 +13,8 @@ import oracle
 import synth
 import sink_window_landmark_amd as swl
 
-from swl_gpu import (banner, check_out, check_state, dev, geom_of, oracle_threads, read_state,
-                     torch)
+from swl_gpu import (ATOL, banner, check_out, check_state, dev, excess, geom_of, oracle_threads,
+                     read_state, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -364,6 +364,43 @@ def test_no_sinks():
     orc = oracle.from_config(cfg, host)
     check_out(got, orc.step(q[:T], k[:T], v[:T]), "prefill")
     check_out(_tokens(cfg, st, q[T:], k[T:], v[T:]), orc.step(q[T:], k[T:], v[T:]), "tokens")
+    check_state(read_state(st), orc)
+
+
+@pytest.mark.parametrize("kscale,vscale", [(20.0, 1000.0), (1e-3, 1e-3)])
+def test_input_scales(kscale, vscale):
+    """Keys and values far from unit scale through the fp16 hi/lo products:
+    large keys (a very peaked near softmax: scores spread over about +-80 in
+    log2 units) with large values, and small ones (the remainders' absolute
+    floor).  The bound is the stated one taken norm-wise: 1e-4 of the
+    largest |output| of the same (row, head) plus 1e-5 times the value
+    scale.  An element-wise relative bound is out of reach of any fp32
+    evaluation here: a score carries an fp32 rounding error of order
+    2^-24 * sum_i |q_i k_i| (about 1e-5 with keys x 20) into its weight, and
+    that reaches an output through values of order 1000, also where those
+    cancel to an output of order 10.  (Far logits spread by more than about
+    87, the fp32 exp range, underflow for the rows of a sub-chunk before the
+    eviction that sets its post-sub-chunk max: there fp32 and the fp64
+    oracle part ways by the method's construction, so the key scale stops
+    short of that.)"""
+    banner(f"input scales k x {kscale:g}, v x {vscale:g}")
+    cfg = synth.Config("scale", G=2, H=2, d=64, dv=64, ns=4, W=128, m=16, rows=400)
+    host = synth.make_state(cfg)
+    host.sink_k = (host.sink_k * kscale).astype(np.float32)
+    host.sink_v = (host.sink_v * vscale).astype(np.float32)
+    q, k, v = synth.rows(cfg, 0, cfg.rows)
+    k = (k * kscale).astype(np.float32)
+    v = (v * vscale).astype(np.float32)
+    st = _state(cfg, host)
+    got = _prefill(cfg, st, q, k, v)
+    orc = oracle.from_config(cfg, host)
+    want = orc.step(q, k, v)
+    assert np.all(np.isfinite(got))
+    rowmax = np.max(np.abs(want), axis=2, keepdims=True)
+    e = excess(got, want, atol=ATOL * vscale, scale=rowmax)
+    rel = float(np.max(np.abs(got - want) / rowmax))
+    print(f"  max |d| / max|out of its row and head| = {rel:.3e}  excess {e:.3e}", flush=True)
+    assert e <= 0, f"beyond the norm-wise tolerance by {e:.3e}"
     check_state(read_state(st), orc)
 
 
