@@ -117,6 +117,24 @@ def rope_rotate(x: np.ndarray, pos: np.ndarray) -> np.ndarray:
     return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
 
 
+def rope_table(pos: np.ndarray, d: int) -> np.ndarray:
+    """RoPE table rows [rows][d] as float32: cos of the d/2 pair angles
+    pos * 10000^(-2j/d), then their sin, computed in float64."""
+    half = d // 2
+    j = np.arange(half, dtype=np.float64)
+    ang = np.asarray(pos, np.float64)[:, None] * (10000.0 ** (-2.0 * j / d))[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
+def gate_inputs(cfg: Config, start: int, count: int):
+    """Gate pre-activations z [count][nh][dv] (N(0, 1)) and the per-(head,
+    column) scale [nh][dv] (uniform in [0.5, 2]) as float32."""
+    r = _rng(cfg, 7, start)
+    z = r.standard_normal((count, cfg.nh, cfg.dv)).astype(np.float32)
+    s = np.random.default_rng([cfg.seed, 8]).uniform(0.5, 2.0, (cfg.nh, cfg.dv)).astype(np.float32)
+    return z, s
+
+
 @dataclasses.dataclass
 class State:
     """Host copy of a layer state (fp32 arrays, u32 meta)."""

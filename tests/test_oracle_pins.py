@@ -377,3 +377,95 @@ def test_rope_is_a_rotation():
     y = synth.rope_rotate(x, np.arange(5) + 7)
     np.testing.assert_allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
     np.testing.assert_allclose(synth.rope_rotate(x, np.zeros(5)), x)
+
+
+# ---- fused ingest (RoPE) and output gate ---------------------------------
+
+def test_rope_rows_equals_complex_multiplication():
+    """Pair (x_j, x_{j+d/2}) as the complex number x_j + i x_{j+d/2}: the
+    rotate-half step is its product with c_j + i s_j, for any table."""
+    from oracle import fused
+    r = np.random.default_rng(3)
+    x = r.standard_normal((6, 3, 16))
+    tab = r.standard_normal((6, 16))
+    z = (x[..., :8] + 1j * x[..., 8:]) * (tab[:, None, :8] + 1j * tab[:, None, 8:])
+    got = fused.rope_rows(x, tab)
+    np.testing.assert_allclose(got[..., :8], z.real, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(got[..., 8:], z.imag, rtol=0, atol=1e-13)
+
+
+def test_rope_rows_with_an_angle_table_matches_the_angle_rotation():
+    """With the table of positions p (cos, then sin of p * 10000^(-2j/d)) the
+    oracle's rotation is the rotation by those angles, which keeps norms,
+    is the identity at p = 0, and leaves <R_a q, R_b k> a function of a - b."""
+    from oracle import fused
+    r = np.random.default_rng(4)
+    d = 32
+    x = r.standard_normal((5, 2, d))
+    pos = np.array([0, 3, 17, 1000, 40000])
+    tab = np.concatenate([np.cos(pos[:, None] * 10000.0 ** (-2.0 * np.arange(d // 2) / d)),
+                          np.sin(pos[:, None] * 10000.0 ** (-2.0 * np.arange(d // 2) / d))], axis=1)
+    got = fused.rope_rows(x, tab)
+    np.testing.assert_allclose(got, synth.rope_rotate(x, pos), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(np.linalg.norm(got, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+    np.testing.assert_array_equal(got[0], x[0])
+    q, k = r.standard_normal(d), r.standard_normal(d)
+
+    def at(v, p):
+        a = p * 10000.0 ** (-2.0 * np.arange(d // 2) / d)
+        return fused.rope_rows(v[None, None], np.concatenate([np.cos(a), np.sin(a)])[None])[0, 0]
+    base = at(q, 9) @ at(k, 4)
+    for t in (1, 50, 777):
+        assert abs(at(q, 9 + t) @ at(k, 4 + t) - base) < 1e-12
+
+
+def test_rope_rows_catches_a_swapped_sign():
+    """A sign flip in either half of the rotation breaks the complex-product
+    identity (the pin above would catch it)."""
+    from oracle import fused
+    r = np.random.default_rng(5)
+    x = r.standard_normal((2, 1, 8))
+    tab = np.concatenate([np.full((2, 4), 0.6), np.full((2, 4), 0.8)], axis=1)
+    good = fused.rope_rows(x, tab)
+    z = (x[..., :4] + 1j * x[..., 4:]) * (0.6 + 0.8j)
+    wrong = np.concatenate([x[..., :4] * 0.6 + x[..., 4:] * 0.8, x[..., 4:] * 0.6 + x[..., :4] * 0.8], -1)
+    np.testing.assert_allclose(good[..., :4], z.real, atol=1e-14)
+    assert np.max(np.abs(wrong[..., :4] - z.real)) > 0.1
+
+
+def test_gate_matches_the_logistic_function():
+    """The gate is out * expit(z s): scipy's logistic function, 1/2 at 0,
+    sigma(x) + sigma(-x) = 1, and finite at +-1000."""
+    from scipy.special import expit
+    from oracle import fused
+    r = np.random.default_rng(6)
+    out = r.standard_normal((4, 3, 8))
+    z = r.standard_normal((4, 3, 8)) * 5
+    s = r.uniform(0.5, 2.0, (3, 8))
+    np.testing.assert_allclose(fused.gate_rows(out, z, s), out * expit(z * s[None]), rtol=1e-14)
+    np.testing.assert_array_equal(fused.gate_rows(out, np.zeros_like(z), s), out / 2)
+    xs = np.array([-1000.0, -30.0, -1.5, 0.0, 2.5, 40.0, 1000.0])
+    np.testing.assert_allclose(fused.sigmoid(xs) + fused.sigmoid(-xs), 1.0, rtol=1e-15)
+    assert fused.sigmoid(-1000.0) == 0.0 and fused.sigmoid(1000.0) == 1.0
+
+
+def test_step_fused_is_rotate_step_gate():
+    """The fused step with an identity table and no gate is the plain step;
+    with a table it is the plain step on rotated rows, and the gate scales
+    the plain output element by element."""
+    from oracle import fused
+    cfg = _cfg(rows=40)
+    st = synth.make_state(cfg)
+    q, k, v = _rand_rows(cfg, cfg.rows, seed=9)
+    ident = np.concatenate([np.ones((cfg.rows, cfg.d // 2)), np.zeros((cfg.rows, cfg.d // 2))], 1)
+    plain = oracle.from_config(cfg, st).step(q, k, v)
+    np.testing.assert_array_equal(fused.step_fused(oracle.from_config(cfg, st), q, k, v, rope=ident), plain)
+    tab = synth.rope_table(np.arange(cfg.rows) + 100, cfg.d)
+    rq = synth.rope_rotate(q.astype(np.float64), np.arange(cfg.rows) + 100).astype(np.float32)
+    rk = synth.rope_rotate(k.astype(np.float64), np.arange(cfg.rows) + 100).astype(np.float32)
+    want = oracle.from_config(cfg, st).step(rq, rk, v)
+    got = fused.step_fused(oracle.from_config(cfg, st), q, k, v, rope=tab)
+    np.testing.assert_allclose(got, want, rtol=1e-5, atol=1e-6)   # fp32 table vs fp64 angles
+    z, s = synth.gate_inputs(cfg, 0, cfg.rows)
+    gated = fused.step_fused(oracle.from_config(cfg, st), q, k, v, gate=z, gate_scale=s)
+    np.testing.assert_allclose(gated, plain / (1 + np.exp(-(z.astype(np.float64) * s))), rtol=1e-13)
