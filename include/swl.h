@@ -197,6 +197,62 @@ int swl_attend_token(const swl_geom* geom, const swl_state* st,
                      const float* q, const float* k, const float* v,
                      float* out, void* scratch, size_t scratch_bytes, void* stream);
 
+/* Fused ingest and output steps (dory.rs page: the preparation kernel
+ * dory_prep and the gate kernels dory_gate1 / dory_ogate), so that q and
+ * the output make no pass of their own through memory:
+ *   rope        [rows][d] floats, or NULL.  Row r holds cos of the d/2 pair
+ *               angles of the call's row r, then their sin.  When set, q and
+ *               k are the rows before RoPE: each kernel that reads a query
+ *               or key head of row r turns its pair (j, j + d/2) into
+ *               (x_j c_j - x_{j+d/2} s_j, x_{j+d/2} c_j + x_j s_j) in fp32,
+ *               and the ring receives the turned keys.  Values are not
+ *               turned.  (The page's kernel also normalises heads; that
+ *               model-specific step is not part of this.)
+ *   gate        [rows][G*H][dv] floats, or NULL: gate pre-activations z.
+ *               When set, each output element is multiplied by
+ *               1 / (1 + exp(-z s)) in fp32.
+ *   gate_scale  [G*H][dv] floats: the scale s of each (head, column);
+ *               required with gate (else SWL_EINVAL).
+ * Device memory owned by the caller and only read.  Row 0 of rope and gate
+ * is the call's first row (prefill advances them with its passes).  A NULL
+ * swl_fuse pointer turns both steps off: each _fused call is then its
+ * plain counterpart. */
+typedef struct swl_fuse {
+    const float* rope;
+    const float* gate;
+    const float* gate_scale;
+} swl_fuse;
+
+/* swl_prefill with the fused steps. */
+int swl_prefill_fused(const swl_geom* geom, const swl_state* st,
+                      const float* q, const float* k, const float* v, int64_t rows,
+                      const swl_fuse* fuse, float* out, void* scratch,
+                      size_t scratch_bytes, void* stream);
+
+/* swl_attend_chunk with the fused steps (1 <= rows <= 64). */
+int swl_attend_chunk_fused(const swl_geom* geom, const swl_state* st,
+                           const float* q, const float* k, const float* v, int32_t rows,
+                           const swl_fuse* fuse, float* out, void* scratch,
+                           size_t scratch_bytes, void* stream);
+
+/* swl_commit after swl_attend_chunk_fused: the same rope (the ring
+ * receives the turned keys); the gate is not used. */
+int swl_commit_fused(const swl_geom* geom, const swl_state* st,
+                     const float* k, const float* v, int32_t rows, const swl_fuse* fuse,
+                     void* scratch, size_t scratch_bytes, void* stream);
+
+/* swl_commit_rows over keys before RoPE (the gate is not used). */
+int swl_commit_rows_fused(const swl_geom* geom, const swl_state* st,
+                          const float* k, const float* v, int64_t rows,
+                          const swl_fuse* fuse, void* scratch, size_t scratch_bytes,
+                          void* stream);
+
+/* swl_attend_token with the fused steps (rope and gate of one row). */
+int swl_attend_token_fused(const swl_geom* geom, const swl_state* st,
+                           const float* q, const float* k, const float* v,
+                           const swl_fuse* fuse, float* out, void* scratch,
+                           size_t scratch_bytes, void* stream);
+
 /* A static description of a status code. */
 const char* swl_status_str(int status);
 

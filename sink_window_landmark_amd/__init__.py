@@ -26,7 +26,8 @@ SUB = 64
 # Entry points declared by include/swl.h.
 EXPORTS = ("swl_scratch_bytes", "swl_init_state", "swl_attend_chunk", "swl_commit",
            "swl_prefill", "swl_prefill_traced", "swl_commit_rows", "swl_seal", "swl_rewind",
-           "swl_attend_token", "swl_status_str")
+           "swl_attend_token", "swl_status_str", "swl_prefill_fused", "swl_attend_chunk_fused",
+           "swl_commit_fused", "swl_commit_rows_fused", "swl_attend_token_fused")
 
 # Stage ids of swl_stage_fn (enum swl_stage).
 STAGES = ("far_score", "far_scan", "dtheta", "theta_scan", "attend", "ring", "meta", "kv_split")
@@ -49,6 +50,10 @@ _P = ctypes.c_void_p
 class _State(ctypes.Structure):
     _fields_ = [("meta", _P), ("ring_k", _P), ("ring_v", _P), ("sink_k", _P), ("sink_v", _P),
                 ("k_tilde", _P), ("q_tilde", _P), ("mu", _P), ("mz", _P), ("theta", _P)]
+
+
+class _Fuse(ctypes.Structure):
+    _fields_ = [("rope", _P), ("gate", _P), ("gate_scale", _P)]
 
 
 _lib = None
@@ -85,6 +90,19 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.swl_rewind.argtypes = [G, S, _P]
     lib.swl_attend_token.restype = ctypes.c_int
     lib.swl_attend_token.argtypes = [G, S, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    F = ctypes.POINTER(_Fuse)
+    lib.swl_prefill_fused.restype = ctypes.c_int
+    lib.swl_prefill_fused.argtypes = [G, S, _P, _P, _P, ctypes.c_int64, F, _P, _P, ctypes.c_size_t,
+                                      _P]
+    lib.swl_attend_chunk_fused.restype = ctypes.c_int
+    lib.swl_attend_chunk_fused.argtypes = [G, S, _P, _P, _P, ctypes.c_int32, F, _P, _P,
+                                           ctypes.c_size_t, _P]
+    lib.swl_commit_fused.restype = ctypes.c_int
+    lib.swl_commit_fused.argtypes = [G, S, _P, _P, ctypes.c_int32, F, _P, ctypes.c_size_t, _P]
+    lib.swl_commit_rows_fused.restype = ctypes.c_int
+    lib.swl_commit_rows_fused.argtypes = [G, S, _P, _P, ctypes.c_int64, F, _P, ctypes.c_size_t, _P]
+    lib.swl_attend_token_fused.restype = ctypes.c_int
+    lib.swl_attend_token_fused.argtypes = [G, S, _P, _P, _P, F, _P, _P, ctypes.c_size_t, _P]
     lib.swl_status_str.restype = ctypes.c_char_p
     lib.swl_status_str.argtypes = [ctypes.c_int]
     _lib = lib
@@ -325,6 +343,79 @@ def swl_attend_token(state: LayerState, q, k, v, out, scratch, stream=None):
         ctypes.byref(state.geom.c()), ctypes.byref(state.c()), q.data_ptr(), k.data_ptr(),
         v.data_ptr(), out.data_ptr(), scratch.data_ptr(), scratch.numel(), _stream(stream))
     _raise(rc, "swl_attend_token")
+
+
+def _fuse_arg(state, rows, rope=None, gate=None, gate_scale=None):
+    """The swl_fuse struct of optional RoPE table [rows][d], gate
+    pre-activations [rows][nh][dv] and gate scale [nh][dv] (device tensors)."""
+    g = state.geom
+    if rope is not None:
+        _check("rope", rope, (rows, g.d))
+    if gate is not None:
+        _check("gate", gate, (rows, g.nh, g.dv))
+        if gate_scale is None:
+            raise ValueError("gate needs gate_scale")
+    if gate_scale is not None:
+        _check("gate_scale", gate_scale, (g.nh, g.dv))
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    return _Fuse(ptr(rope), ptr(gate), ptr(gate_scale))
+
+
+def swl_prefill_fused(state: LayerState, q, k, v, out, scratch, rope=None, gate=None,
+                      gate_scale=None, stream=None):
+    """swl_prefill with q, k before RoPE (``rope`` table rows) and/or the
+    sigmoid output gate (``gate``, ``gate_scale``)."""
+    rows = q.shape[0]
+    _rows_args(state, q, k, v, out, rows)
+    f = _fuse_arg(state, rows, rope, gate, gate_scale)
+    rc = load_library().swl_prefill_fused(
+        ctypes.byref(state.geom.c()), ctypes.byref(state.c()), q.data_ptr(), k.data_ptr(),
+        v.data_ptr(), rows, ctypes.byref(f), out.data_ptr(), scratch.data_ptr(), scratch.numel(),
+        _stream(stream))
+    _raise(rc, "swl_prefill_fused")
+
+
+def swl_attend_chunk_fused(state: LayerState, q, k, v, out, scratch, rope=None, gate=None,
+                           gate_scale=None, stream=None):
+    rows = q.shape[0]
+    _rows_args(state, q, k, v, out, rows)
+    f = _fuse_arg(state, rows, rope, gate, gate_scale)
+    rc = load_library().swl_attend_chunk_fused(
+        ctypes.byref(state.geom.c()), ctypes.byref(state.c()), q.data_ptr(), k.data_ptr(),
+        v.data_ptr(), rows, ctypes.byref(f), out.data_ptr(), scratch.data_ptr(), scratch.numel(),
+        _stream(stream))
+    _raise(rc, "swl_attend_chunk_fused")
+
+
+def swl_commit_fused(state: LayerState, k, v, scratch, rope=None, stream=None):
+    rows = k.shape[0]
+    _rows_args(state, None, k, v, None, rows)
+    f = _fuse_arg(state, rows, rope)
+    rc = load_library().swl_commit_fused(
+        ctypes.byref(state.geom.c()), ctypes.byref(state.c()), k.data_ptr(), v.data_ptr(), rows,
+        ctypes.byref(f), scratch.data_ptr(), scratch.numel(), _stream(stream))
+    _raise(rc, "swl_commit_fused")
+
+
+def swl_commit_rows_fused(state: LayerState, k, v, scratch, rope=None, stream=None):
+    rows = k.shape[0]
+    _rows_args(state, None, k, v, None, rows)
+    f = _fuse_arg(state, rows, rope)
+    rc = load_library().swl_commit_rows_fused(
+        ctypes.byref(state.geom.c()), ctypes.byref(state.c()), k.data_ptr(), v.data_ptr(), rows,
+        ctypes.byref(f), scratch.data_ptr(), scratch.numel(), _stream(stream))
+    _raise(rc, "swl_commit_rows_fused")
+
+
+def swl_attend_token_fused(state: LayerState, q, k, v, out, scratch, rope=None, gate=None,
+                           gate_scale=None, stream=None):
+    _rows_args(state, q, k, v, out, 1)
+    f = _fuse_arg(state, 1, rope, gate, gate_scale)
+    rc = load_library().swl_attend_token_fused(
+        ctypes.byref(state.geom.c()), ctypes.byref(state.c()), q.data_ptr(), k.data_ptr(),
+        v.data_ptr(), ctypes.byref(f), out.data_ptr(), scratch.data_ptr(), scratch.numel(),
+        _stream(stream))
+    _raise(rc, "swl_attend_token_fused")
 
 
 # Short aliases.

@@ -96,6 +96,17 @@ static void set_scratch(KParams& p, const swl_geom* g, void* scratch, int S)
     p.kv_tiles = kv_tiles(g->ns, g->W, S);
 }
 
+// The fused ingest/output pointers of a call whose rows start `row0` rows
+// into the caller's arrays (null fuse: both steps off).
+static bool fuse_ok(const swl_fuse* f) { return !f || !f->gate || f->gate_scale; }
+static void set_fuse(KParams& p, const swl_fuse* f, int64_t row0)
+{
+    if (!f) return;
+    if (f->rope) p.rope = f->rope + row0 * p.d;
+    if (f->gate) p.gate = f->gate + row0 * p.nh * p.dv;
+    p.gate_scale = f->gate_scale;
+}
+
 #define SWL_TRY(x)                          \
     do {                                    \
         if ((x) != hipSuccess) return SWL_EHIP; \
@@ -147,15 +158,16 @@ int swl_init_state(const swl_geom* geom, const swl_state* st, const uint32_t* wi
     return SWL_OK;
 }
 
-int swl_attend_chunk(const swl_geom* geom, const swl_state* st, const float* q, const float* k,
-                     const float* v, int32_t rows, float* out, void* scratch,
-                     size_t scratch_bytes, void* stream)
+int swl_attend_chunk_fused(const swl_geom* geom, const swl_state* st, const float* q,
+                           const float* k, const float* v, int32_t rows, const swl_fuse* fuse,
+                           float* out, void* scratch, size_t scratch_bytes, void* stream)
 {
-    if (!geom_ok(geom) || !state_ok(geom, st)) return SWL_EINVAL;
+    if (!geom_ok(geom) || !state_ok(geom, st) || !fuse_ok(fuse)) return SWL_EINVAL;
     if (rows < 1 || rows > SUB || !q || !k || !v || !out || !scratch) return SWL_EINVAL;
     if (scratch_bytes < carve(geom, 1).total) return SWL_EINVAL;
     KParams p = make_params(geom, st);
     p.q = q; p.k = k; p.v = v; p.out = out;
+    set_fuse(p, fuse, 0);
     p.T = rows; p.S = 1;
     set_scratch(p, geom, scratch, 1);
     p.theta_prev = st->theta;
@@ -163,17 +175,33 @@ int swl_attend_chunk(const swl_geom* geom, const swl_state* st, const float* q, 
     return run_attend(p, static_cast<hipStream_t>(stream));
 }
 
-int swl_commit(const swl_geom* geom, const swl_state* st, const float* k, const float* v,
-               int32_t rows, void* scratch, size_t scratch_bytes, void* stream)
+int swl_attend_chunk(const swl_geom* geom, const swl_state* st, const float* q, const float* k,
+                     const float* v, int32_t rows, float* out, void* scratch,
+                     size_t scratch_bytes, void* stream)
 {
-    if (!geom_ok(geom) || !state_ok(geom, st)) return SWL_EINVAL;
+    return swl_attend_chunk_fused(geom, st, q, k, v, rows, nullptr, out, scratch, scratch_bytes,
+                                  stream);
+}
+
+int swl_commit_fused(const swl_geom* geom, const swl_state* st, const float* k, const float* v,
+                     int32_t rows, const swl_fuse* fuse, void* scratch, size_t scratch_bytes,
+                     void* stream)
+{
+    if (!geom_ok(geom) || !state_ok(geom, st) || !fuse_ok(fuse)) return SWL_EINVAL;
     if (rows < 1 || rows > SUB || !k || !v || !scratch) return SWL_EINVAL;
     if (scratch_bytes < carve(geom, 1).total) return SWL_EINVAL;
     KParams p = make_params(geom, st);
     p.k = k; p.v = v;
     p.T = rows; p.S = 1;
+    set_fuse(p, fuse, 0);
     set_scratch(p, geom, scratch, 1);
     return run_commit(p, static_cast<hipStream_t>(stream));
+}
+
+int swl_commit(const swl_geom* geom, const swl_state* st, const float* k, const float* v,
+               int32_t rows, void* scratch, size_t scratch_bytes, void* stream)
+{
+    return swl_commit_fused(geom, st, k, v, rows, nullptr, scratch, scratch_bytes, stream);
 }
 
 }  // extern "C"
@@ -182,10 +210,10 @@ int swl_commit(const swl_geom* geom, const swl_state* st, const float* k, const 
 // to PASS_SUBS sub-chunks: far_e, far commit, (attention,) ring commit and
 // meta of each pass.  Without `attend`, q and out are not used.
 static int run_rows(const swl_geom* geom, const swl_state* st, const float* q, const float* k,
-                    const float* v, int64_t rows, float* out, void* scratch, size_t scratch_bytes,
-                    void* stream, swl_stage_fn fn, void* user, bool attend)
+                    const float* v, int64_t rows, const swl_fuse* fuse, float* out, void* scratch,
+                    size_t scratch_bytes, void* stream, swl_stage_fn fn, void* user, bool attend)
 {
-    if (!geom_ok(geom) || !state_ok(geom, st)) return SWL_EINVAL;
+    if (!geom_ok(geom) || !state_ok(geom, st) || !fuse_ok(fuse)) return SWL_EINVAL;
     if (rows < 0) return SWL_EINVAL;
     if (rows == 0) return SWL_OK;
     if (!k || !v || !scratch || (attend && (!q || !out))) return SWL_EINVAL;
@@ -210,6 +238,7 @@ static int run_rows(const swl_geom* geom, const swl_state* st, const float* q, c
         }
         p.k = k + done * geom->G * geom->d;
         p.v = v + done * geom->G * geom->dv;
+        set_fuse(p, fuse, done);
         p.T = (int)T;
         p.S = (int)((T + SUB - 1) / SUB);
         set_scratch(p, geom, scratch, S_max);
@@ -237,21 +266,38 @@ int swl_prefill_traced(const swl_geom* geom, const swl_state* st, const float* q
                        const float* k, const float* v, int64_t rows, float* out, void* scratch,
                        size_t scratch_bytes, void* stream, swl_stage_fn fn, void* user)
 {
-    return run_rows(geom, st, q, k, v, rows, out, scratch, scratch_bytes, stream, fn, user, true);
+    return run_rows(geom, st, q, k, v, rows, nullptr, out, scratch, scratch_bytes, stream, fn,
+                    user, true);
 }
 
 int swl_prefill(const swl_geom* geom, const swl_state* st, const float* q, const float* k,
                 const float* v, int64_t rows, float* out, void* scratch, size_t scratch_bytes,
                 void* stream)
 {
-    return run_rows(geom, st, q, k, v, rows, out, scratch, scratch_bytes, stream, nullptr,
+    return run_rows(geom, st, q, k, v, rows, nullptr, out, scratch, scratch_bytes, stream,
+                    nullptr, nullptr, true);
+}
+
+int swl_prefill_fused(const swl_geom* geom, const swl_state* st, const float* q, const float* k,
+                      const float* v, int64_t rows, const swl_fuse* fuse, float* out,
+                      void* scratch, size_t scratch_bytes, void* stream)
+{
+    return run_rows(geom, st, q, k, v, rows, fuse, out, scratch, scratch_bytes, stream, nullptr,
                     nullptr, true);
 }
 
 int swl_commit_rows(const swl_geom* geom, const swl_state* st, const float* k, const float* v,
                     int64_t rows, void* scratch, size_t scratch_bytes, void* stream)
 {
-    return run_rows(geom, st, nullptr, k, v, rows, nullptr, scratch, scratch_bytes, stream,
+    return run_rows(geom, st, nullptr, k, v, rows, nullptr, nullptr, scratch, scratch_bytes,
+                    stream, nullptr, nullptr, false);
+}
+
+int swl_commit_rows_fused(const swl_geom* geom, const swl_state* st, const float* k,
+                          const float* v, int64_t rows, const swl_fuse* fuse, void* scratch,
+                          size_t scratch_bytes, void* stream)
+{
+    return run_rows(geom, st, nullptr, k, v, rows, fuse, nullptr, scratch, scratch_bytes, stream,
                     nullptr, nullptr, false);
 }
 
@@ -275,20 +321,28 @@ int swl_rewind(const swl_geom* geom, const swl_state* st, void* stream)
     return SWL_OK;
 }
 
-int swl_attend_token(const swl_geom* geom, const swl_state* st, const float* q, const float* k,
-                     const float* v, float* out, void* scratch, size_t scratch_bytes,
-                     void* stream)
+int swl_attend_token_fused(const swl_geom* geom, const swl_state* st, const float* q,
+                           const float* k, const float* v, const swl_fuse* fuse, float* out,
+                           void* scratch, size_t scratch_bytes, void* stream)
 {
-    if (!geom_ok(geom) || !state_ok(geom, st)) return SWL_EINVAL;
+    if (!geom_ok(geom) || !state_ok(geom, st) || !fuse_ok(fuse)) return SWL_EINVAL;
     if (!q || !k || !v || !out || !scratch) return SWL_EINVAL;
     const Carve cv = carve(geom, 1);
     if (scratch_bytes < cv.total) return SWL_EINVAL;
     KParams p = make_params(geom, st);
     p.q = q; p.k = k; p.v = v; p.out = out;
     p.T = 1; p.S = 1;
+    set_fuse(p, fuse, 0);
     float* part = reinterpret_cast<float*>(static_cast<char*>(scratch) + cv.tok);
     SWL_TRY(launch_token(p, part, static_cast<hipStream_t>(stream)));
     return SWL_OK;
+}
+
+int swl_attend_token(const swl_geom* geom, const swl_state* st, const float* q, const float* k,
+                     const float* v, float* out, void* scratch, size_t scratch_bytes,
+                     void* stream)
+{
+    return swl_attend_token_fused(geom, st, q, k, v, nullptr, out, scratch, scratch_bytes, stream);
 }
 
 const char* swl_status_str(int status)

@@ -235,6 +235,7 @@ __global__ __launch_bounds__(256) void k_kv_split(KParams p)
         const int r = e / (D / 4), c4 = (e % (D / 4)) * 4;
         const float* kp;
         const float* vp;
+        const float* kt = nullptr;   // RoPE table row of a key from the pass's rows
         if (t < nst) {
             const int64_t off = ((int64_t)g * p.ns + min(t * KT + r, p.ns - 1)) * D;
             kp = p.sink_k + off;
@@ -243,8 +244,9 @@ __global__ __launch_bounds__(256) void k_kv_split(KParams p)
             const int pos = min((t - nst) * KT + r, last);
             kp = key_row(p, c, g, pos);
             vp = val_row(p, c, g, pos);
+            if (p.rope && pos >= c.len0) kt = p.rope + (int64_t)(pos - c.len0) * D;
         }
-        const float4 kx = *reinterpret_cast<const float4*>(kp + c4);
+        const float4 kx = rope4(kp, kt, c4, D);
         const float4 vx = *reinterpret_cast<const float4*>(vp + c4);
         kf[r][c4] = kx.x; kf[r][c4 + 1] = kx.y; kf[r][c4 + 2] = kx.z; kf[r][c4 + 3] = kx.w;
         vf[r][c4] = vx.x; vf[r][c4 + 1] = vx.y; vf[r][c4 + 2] = vx.z; vf[r][c4 + 3] = vx.w;
@@ -335,13 +337,14 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
         const float qs = p.scale * LOG2E;
         const bool ok = active && i < ks;
         const float* qr = p.q + ((int64_t)(r0 + i) * p.nh + gh) * D;
+        const float* qt = p.rope ? p.rope + (int64_t)(r0 + i) * D : nullptr;   // RoPE on the way in
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
             const int d0 = st * 16 + hf * 8;
             float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = x;
             if (ok & (d0 < D)) {
-                x = *reinterpret_cast<const float4*>(qr + d0);
-                y = *reinterpret_cast<const float4*>(qr + d0 + 4);
+                x = rope4(qr, qt, d0, D);
+                y = rope4(qr, qt, d0 + 4, D);
             }
             const Split<true> s0(x.x * qs, x.y * qs), s1(x.z * qs, x.w * qs);
             const Split<true> s2(y.x * qs, y.y * qs), s3(y.z * qs, y.w * qs);
@@ -705,15 +708,26 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
     if (active && i < ks) {
         const float inv = 1.f / fmaxf(den, 1e-30f);
         float* orow = p.out + ((int64_t)(r0 + i) * p.nh + gh) * D;
+        // the output gate, when on, multiplies each element on its way out
+        const float* zr = p.gate ? p.gate + ((int64_t)(r0 + i) * p.nh + gh) * D : nullptr;
+        const float* sr = p.gate_scale + (int64_t)gh * D;
         // accumulator row rho of block blk is value column 32 blk + rho; rows
         // kappa(4a .. 4a+3, hf) are the adjacent columns 8a + 4hf .. +3
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
-            for (int a = 0; a < (D >= 32 ? 4 : D / 8); ++a)
-                *reinterpret_cast<float4*>(orow + blk * 32 + 8 * a + 4 * hf) =
-                    make_float4(O[blk][4 * a] * inv, O[blk][4 * a + 1] * inv, O[blk][4 * a + 2] * inv,
-                                O[blk][4 * a + 3] * inv);
+            for (int a = 0; a < (D >= 32 ? 4 : D / 8); ++a) {
+                const int col = blk * 32 + 8 * a + 4 * hf;
+                float4 o = make_float4(O[blk][4 * a] * inv, O[blk][4 * a + 1] * inv, O[blk][4 * a + 2] * inv,
+                                       O[blk][4 * a + 3] * inv);
+                if (zr) {
+                    const float4 z = *reinterpret_cast<const float4*>(zr + col);
+                    const float4 s = *reinterpret_cast<const float4*>(sr + col);
+                    o = make_float4(o.x * gate_of(z.x, s.x), o.y * gate_of(z.y, s.y), o.z * gate_of(z.z, s.z),
+                                    o.w * gate_of(z.w, s.w));
+                }
+                *reinterpret_cast<float4*>(orow + col) = o;
+            }
     }
 }
 

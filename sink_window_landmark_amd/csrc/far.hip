@@ -109,7 +109,10 @@ __global__ __launch_bounds__(FS_THREADS) void k_far_score(KParams p)
             const int pos = max(c.len0 + r0 + min(j, ks - 1) - c.wg, 0);
             const float* ra = p.ring_k + ((int64_t)g * p.W + (c.head0 + min(pos, max(c.len0 - 1, 0))) % c.wg) * D;
             const float* ia = p.k + ((int64_t)max(pos - c.len0, 0) * p.G + g) * D;
-            x[u] = *reinterpret_cast<const v4*>((pos < c.len0 ? ra : ia) + c4);
+            // a key from the call's rows takes the RoPE of its row on the way in
+            const float* kt = (p.rope && pos >= c.len0) ? p.rope + (int64_t)(pos - c.len0) * D : nullptr;
+            const float4 kx = rope4(pos < c.len0 ? ra : ia, kt, c4, D);
+            x[u] = v4{kx.x, kx.y, kx.z, kx.w};
         }
 #pragma unroll
         for (int u = 0; u < PT; ++u) {

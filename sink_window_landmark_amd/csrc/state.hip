@@ -39,8 +39,9 @@ __global__ __launch_bounds__(256) void k_ring_commit(KParams p)
     const float* vs = p.v + ((int64_t)r * p.G + g) * p.dv;
     float* kd = p.ring_k + ((int64_t)g * p.W + slot) * p.d;
     float* vd = p.ring_v + ((int64_t)g * p.W + slot) * p.dv;
+    const float* kt = p.rope ? p.rope + (int64_t)r * p.d : nullptr;   // the ring holds turned keys
     for (int t = threadIdx.x; t < p.d / 4; t += 256)
-        reinterpret_cast<float4*>(kd)[t] = reinterpret_cast<const float4*>(ks)[t];
+        reinterpret_cast<float4*>(kd)[t] = rope4(ks, kt, 4 * t, p.d);
     for (int t = threadIdx.x; t < p.dv / 4; t += 256)
         reinterpret_cast<float4*>(vd)[t] = reinterpret_cast<const float4*>(vs)[t];
 }

@@ -46,7 +46,40 @@ struct KParams {
     int64_t theta_prev_stride;
     unsigned short* kvs;      // [G][kv_tiles] fp16 key tiles of the pass (k_kv_split)
     int kv_tiles;             // tiles per group: the sinks, then the aligned window tiles
+    // fused ingest and output steps (null: off)
+    const float* rope;        // [T][d] row r: cos of the d/2 pair angles, then their sin
+    const float* gate;        // [T][nh][dv] gate pre-activations
+    const float* gate_scale;  // [nh][dv]
 };
+
+// Elements c4 .. c4+3 of row x (a query or key head of D elements) after
+// the rotate-half RoPE of table row tab (cos of the D/2 pair angles, then
+// their sin): pair (j, j + D/2) becomes (x_j c - x_{j+D/2} s,
+// x_{j+D/2} c + x_j s).  tab null: the elements as they are.  c4 a
+// multiple of 4 and D of 8, so that a float4 never straddles the halves.
+__device__ __forceinline__ float4 rope4(const float* x, const float* tab, int c4, int D)
+{
+    if (!tab) return *reinterpret_cast<const float4*>(x + c4);
+    const int h = D >> 1;
+    const bool first = c4 < h;
+    const int j = first ? c4 : c4 - h;
+    const float4 a = *reinterpret_cast<const float4*>(x + j);
+    const float4 b = *reinterpret_cast<const float4*>(x + j + h);
+    const float4 cs = *reinterpret_cast<const float4*>(tab + j);
+    const float4 sn = *reinterpret_cast<const float4*>(tab + h + j);
+    if (first)
+        return make_float4(a.x * cs.x - b.x * sn.x, a.y * cs.y - b.y * sn.y, a.z * cs.z - b.z * sn.z,
+                           a.w * cs.w - b.w * sn.w);
+    return make_float4(b.x * cs.x + a.x * sn.x, b.y * cs.y + a.y * sn.y, b.z * cs.z + a.z * sn.z,
+                       b.w * cs.w + a.w * sn.w);
+}
+
+// The output gate 1 / (1 + exp(-z s)) (0 for very negative z s, 1 for
+// very positive: exp overflows to inf or underflows to 0, no NaN).
+__device__ __forceinline__ float gate_of(float z, float s)
+{
+    return 1.f / (1.f + expf(-z * s));
+}
 
 // Ring bookkeeping of group g at the start of a call.
 struct GMeta {

@@ -126,6 +126,14 @@ __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x)
 
 __device__ __forceinline__ float dot4(f4 a, f4 b) { return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w; }
 
+// Elements c4 .. c4+3 of the row's query or key head x, turned by the RoPE
+// table row tab when there is one.
+__device__ __forceinline__ f4 tok_in(const float* x, const float* tab, int c4, int D)
+{
+    const float4 v = rope4(x, tab, c4, D);
+    return f4{v.x, v.y, v.z, v.w};
+}
+
 // Near partial of group g, keys k0 .. k0+63 taken by physical position (the
 // sinks, then ring slots 0 .. W-1), which needs no bookkeeping to address:
 // the softmax does not depend on their order.  Thread (rb, li) holds columns
@@ -167,8 +175,8 @@ __device__ __forceinline__ void tok_near(const KParams& p, float* nearp, int nsp
         vx[u] = *reinterpret_cast<const f4*>((x < p.ns ? vs : vr) + c4);
     }
 #pragma unroll
-    for (int j = 0; j < HC; ++j) q0[j] = *reinterpret_cast<const f4*>(p.q + ((int64_t)g * H + min(j, H - 1)) * D + c4);
-    const f4 knew = *reinterpret_cast<const f4*>(p.k + (int64_t)g * D + c4);
+    for (int j = 0; j < HC; ++j) q0[j] = tok_in(p.q + ((int64_t)g * H + min(j, H - 1)) * D, p.rope, c4, D);
+    const f4 knew = tok_in(p.k + (int64_t)g * D, p.rope, c4, D);
     const f4 vnew = *reinterpret_cast<const f4*>(p.v + (int64_t)g * D + c4);
     const GMeta c = load_gmeta(p.meta, g, p.W);
     const TokRow r = tok_row(c);
@@ -192,7 +200,7 @@ __device__ __forceinline__ void tok_near(const KParams& p, float* nearp, int nsp
         f4 qc[HC];
 #pragma unroll
         for (int j = 0; j < HC; ++j)
-            qc[j] = hc == 0 ? q0[j] : *reinterpret_cast<const f4*>(p.q + ((int64_t)g * H + min(hc + j, H - 1)) * D + c4);
+            qc[j] = hc == 0 ? q0[j] : tok_in(p.q + ((int64_t)g * H + min(hc + j, H - 1)) * D, p.rope, c4, D);
         float s[NL * HC];
 #pragma unroll
         for (int u = 0; u < NL; ++u)
@@ -315,7 +323,7 @@ __device__ __forceinline__ void tok_far(const KParams& p, float* farp, int fbk, 
         const int a = min(rb + u * RPP, m - 1);
         kt[u] = *reinterpret_cast<const f4*>(p.k_tilde + ((int64_t)g * m + a) * D + c4);
     }
-    const f4 qh = *reinterpret_cast<const f4*>(p.q + (int64_t)gh * D + c4);
+    const f4 qh = tok_in(p.q + (int64_t)gh * D, p.rope, c4, D);
 #pragma unroll
     for (int u = 0; u < NQ; ++u) {
         const int j = min(rb + u * RPP, nb - 1);
@@ -515,7 +523,7 @@ __global__ __launch_bounds__(TOK_MT) void k_tok_merge(KParams p, const float* pa
     // the commit's loads go out with the others (every block issues them;
     // only the first head of a group stores)
     const GMeta c = load_gmeta(p.meta, g, p.W);
-    const f4 kn = *reinterpret_cast<const f4*>(p.k + (int64_t)g * D + c4 * 4);
+    const f4 kn = tok_in(p.k + (int64_t)g * D, p.rope, c4 * 4, D);
     const f4 vn = *reinterpret_cast<const f4*>(p.v + (int64_t)g * D + c4 * 4);
     // far range prt (parts 0 .. TOK_FB-1), loaded unconditionally
     const float* fr = farp + (int64_t)min(prt, TOK_FB - 1) * rl;
@@ -607,7 +615,13 @@ __global__ __launch_bounds__(TOK_MT) void k_tok_merge(KParams p, const float* pa
             den += w * sl[q];
             num += w * sa[q];
         }
-        *reinterpret_cast<f4*>(p.out + (int64_t)gh * D + tid * 4) = num * (1.f / fmaxf(den, 1e-30f));
+        f4 o = num * (1.f / fmaxf(den, 1e-30f));
+        if (p.gate) {   // the output gate, when on
+            const f4 z = *reinterpret_cast<const f4*>(p.gate + (int64_t)gh * D + tid * 4);
+            const f4 s = *reinterpret_cast<const f4*>(p.gate_scale + (int64_t)gh * D + tid * 4);
+            o = f4{o.x * gate_of(z.x, s.x), o.y * gate_of(z.y, s.y), o.z * gate_of(z.z, s.z), o.w * gate_of(z.w, s.w)};
+        }
+        *reinterpret_cast<f4*>(p.out + (int64_t)gh * D + tid * 4) = o;
         if (h == 0) {
             const TokRow r = tok_row(c);
             *reinterpret_cast<f4*>(p.ring_k + ((int64_t)g * p.W + r.slot) * D + tid * 4) = kn;

@@ -142,3 +142,28 @@ def test_init_rejects_window_wider_than_stride():
                               None) == swl.SWL_EINVAL
     bad = _geom(G=0).c()
     assert lib.swl_init_state(ctypes.byref(bad), ctypes.byref(st), None, None) == swl.SWL_EINVAL
+
+
+@needs_no_gpu
+def test_fused_calls_reject_a_gate_without_its_scale():
+    lib = swl.load_library()
+    g = _geom().c()
+    st = _fake_state()
+    n = swl.swl_scratch_bytes(_geom(), 64)
+    bad = swl._Fuse(FAKE, FAKE, None)
+    assert lib.swl_prefill_fused(ctypes.byref(g), ctypes.byref(st), FAKE, FAKE, FAKE, 64,
+                                 ctypes.byref(bad), FAKE, FAKE, n, None) == swl.SWL_EINVAL
+    assert lib.swl_attend_chunk_fused(ctypes.byref(g), ctypes.byref(st), FAKE, FAKE, FAKE, 64,
+                                      ctypes.byref(bad), FAKE, FAKE, n, None) == swl.SWL_EINVAL
+    assert lib.swl_attend_token_fused(ctypes.byref(g), ctypes.byref(st), FAKE, FAKE, FAKE,
+                                      ctypes.byref(bad), FAKE, FAKE, n, None) == swl.SWL_EINVAL
+    assert lib.swl_commit_fused(ctypes.byref(g), ctypes.byref(st), FAKE, FAKE, 64,
+                                ctypes.byref(bad), FAKE, n, None) == swl.SWL_EINVAL
+    assert lib.swl_commit_rows_fused(ctypes.byref(g), ctypes.byref(st), FAKE, FAKE, 64,
+                                     ctypes.byref(bad), FAKE, n, None) == swl.SWL_EINVAL
+    # the fused calls keep their plain counterparts' checks
+    ok = swl._Fuse(FAKE, None, None)
+    assert lib.swl_attend_chunk_fused(ctypes.byref(g), ctypes.byref(st), FAKE, FAKE, FAKE, 65,
+                                      ctypes.byref(ok), FAKE, FAKE, n, None) == swl.SWL_EINVAL
+    assert lib.swl_prefill_fused(ctypes.byref(g), ctypes.byref(st), None, None, None, 0,
+                                 ctypes.byref(ok), None, None, 0, None) == swl.SWL_OK
