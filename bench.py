@@ -274,6 +274,38 @@ def run_gpu(args, cfg):
                              bytes_per_token=db, achieved_gbs=db / (us * 1e-6) / 1e9,
                              frac_hbm=db / (us * 1e-6) / 1e9 / HBM_PEAK_GBS)
 
+    # the fused ingest and output steps: the same prompt through
+    # swl_prefill_fused with q, k taken before RoPE (a cos/sin table row per
+    # prompt row) and the sigmoid output gate (pre-activations per output
+    # element, a scale per head and column)
+    if args.fused:
+        tab = torch.from_numpy(synth.rope_table(np.arange(T), cfg.d)).to(dev)
+        zh, sh_ = synth.gate_inputs(cfg, 0, T)
+        z = torch.from_numpy(zh).to(dev)
+        gsc = torch.from_numpy(sh_).to(dev)
+        del zh
+
+        def fstep():
+            swl.swl_init_state(st, windows)
+            swl.swl_prefill_fused(st, q, k, v, out, scratch, rope=tab, gate=z, gate_scale=gsc)
+
+        for _ in range(max(1, args.warmup)):
+            fstep()
+        torch.cuda.synchronize()
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record()
+        for _ in range(args.steps):
+            fstep()
+        f1.record()
+        torch.cuda.synchronize()
+        fms = f0.elapsed_time(f1) / args.steps
+        res["fused"] = dict(ms_per_step=fms, rows_per_s=T / (fms * 1e-3),
+                            vs_plain_step=fms / ms_per_step,
+                            extra_bytes_per_step=(tab.numel() + z.numel() + gsc.numel()) * 4,
+                            what="swl_prefill_fused: q, k before RoPE (table rows) and the "
+                                 "sigmoid output gate, fused into the kernels")
+        del tab, z, gsc
+
     # the per-sub-chunk API (attend_chunk + commit per 64 rows), for comparison
     if args.chunk_api:
         cscr = swl.alloc_scratch(geom, 64, device=dev)
@@ -372,6 +404,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-exact", dest="exact", action="store_false")
     ap.add_argument("--no-chunk-api", dest="chunk_api", action="store_false")
+    ap.add_argument("--no-fused", dest="fused", action="store_false",
+                    help="skip the fused RoPE + gate prefill leg")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy (the reference kernel "
                          "for scaling HBM byte counters)")
@@ -434,6 +468,8 @@ def main():
         line["roofline"]["traffic_detail"] = tr
     if "decode" in res:
         line["decode"] = res["decode"]
+    if "fused" in res:
+        line["fused"] = res["fused"]
     if "chunk_api_rows_per_s" in res:
         line["chunk_api_rows_per_s"] = res["chunk_api_rows_per_s"]
     if "exact_attention" in res:
