@@ -423,6 +423,15 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
             if (st + 2 < NS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
         __builtin_amdgcn_s_setprio(0);
+        // the value product's first operands are read now, so that their LDS
+        // latency hides behind the softmax
+        const unsigned short* vr = tiles + buf * BUF + 2 * L::KH;
+        auto vaddr = [&](int k) {
+            const int rho = min((k >> 1) * 32 + ln, D - 1);
+            return rho * KT + vchunk(rho, 2 * (k & 1) + hf) * 8;
+        };
+        u32x4 vh = *reinterpret_cast<const u32x4*>(vr + vaddr(0));
+        u32x4 vl = *reinterpret_cast<const u32x4*>(vr + L::VH + vaddr(0));
         floatx16 sacc;
 #pragma unroll
         for (int v = 0; v < 16; ++v) sacc[v] = fmaf(sx[v], LO_DOWN, sh[v]);
@@ -481,17 +490,10 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
             ph[t] = u32x4{s0.hi, s1.hi, s2.hi, s3.hi};
             pl[t] = u32x4{s0.lo, s1.lo, s2.lo, s3.lo};
         }
-        const unsigned short* vr = tiles + buf * BUF + 2 * L::KH;
         __builtin_amdgcn_s_setprio(1);
         // step (blk, t) = step k = 2 blk + t; operands of step k+1 are read
         // before the products of step k, and the products of a step go to one
         // accumulator while the next step's go to another
-        auto vaddr = [&](int k) {
-            const int rho = min((k >> 1) * 32 + ln, D - 1);
-            return rho * KT + vchunk(rho, 2 * (k & 1) + hf) * 8;
-        };
-        u32x4 vh = *reinterpret_cast<const u32x4*>(vr + vaddr(0));
-        u32x4 vl = *reinterpret_cast<const u32x4*>(vr + L::VH + vaddr(0));
 #pragma unroll
         for (int k = 0; k < 2 * NB; ++k) {
             u32x4 vhn = vh, vln = vl;
