@@ -40,7 +40,7 @@ static bool state_ok(const swl_geom* g, const swl_state* st)
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Carve {
-    size_t tok, e, p, ms, rs, tz, th, kv, total;
+    size_t tok, apart, e, p, ms, rs, tz, th, kv, total;
 };
 
 static Carve carve(const swl_geom* g, int S)
@@ -50,6 +50,7 @@ static Carve carve(const swl_geom* g, int S)
     size_t off = 0;
     // the decode plane comes first, at an offset that does not depend on S
     c.tok = off; off += align256(sizeof(float) * tok_part_floats(g->G, g->H, g->dv, g->ns, g->W));
+    c.apart = off; off += align256(sizeof(float) * attend_part_floats(g->d));
     c.e = off;  off += align256(sizeof(float) * (size_t)S * nhm * SUB);
     c.p = off;  off += align256(sizeof(float) * (size_t)S * g->G * g->H * SUB * 64);
     c.ms = off; off += align256(sizeof(float) * (size_t)S * nhm);
@@ -92,6 +93,7 @@ static void set_scratch(KParams& p, const swl_geom* g, void* scratch, int S)
     p.Rs = reinterpret_cast<float*>(b + c.rs);
     p.TZ = reinterpret_cast<float*>(b + c.tz);
     p.TH = reinterpret_cast<float*>(b + c.th);
+    p.apart = reinterpret_cast<float*>(b + c.apart);
     p.kvs = reinterpret_cast<unsigned short*>(b + c.kv);
     p.kv_tiles = kv_tiles(g->ns, g->W, S);
 }

@@ -278,7 +278,16 @@ __global__ __launch_bounds__(256) void k_kv_split(KParams p)
     }
 }
 
-template <int D, int MT>
+// MODE: AT_FULL, one block per (sub-chunk, group, head group) over all of its
+// key tiles; AT_PART, p.nsp blocks per (sub-chunk, group, head group), each
+// over one contiguous range of the tiles, writing its softmax state (running
+// reference, mass, O^T) to p.apart; AT_MERGE, one block per (sub-chunk,
+// group, head group) that merges those states and runs the far readout.
+// The split serves launches with few blocks (a single sub-chunk, short
+// prompts), where one block per sub-chunk would leave most CUs idle.
+constexpr int AT_FULL = 0, AT_PART = 1, AT_MERGE = 2;
+
+template <int D, int MT, int MODE>
 __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
 {
     constexpr int AT_THREADS = AtCfg<D>::THREADS;
@@ -308,7 +317,9 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
     // work item = (head group, group, sub-chunk), sub-chunk fastest, dealt
     // to XCDs in contiguous runs
     const int hgroups = (p.H + HPB - 1) / HPB;
-    const int w = xcd_work_item(blockIdx.x, p.S * p.G * hgroups);
+    const int nsp = MODE == AT_PART ? p.nsp : 1;
+    const int wx = xcd_work_item(blockIdx.x, p.S * p.G * hgroups * nsp);
+    const int sp = wx % nsp, w = wx / nsp;   // split, and the (sub-chunk, group, head group) item
     const int s = w % p.S, g = (w / p.S) % p.G, hgrp = w / (p.S * p.G);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int hf = lane >> 5, ln = lane & 31;
@@ -330,6 +341,36 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
     const int w_lo = max(0, base + ia - c.wg + 1);  // lowest position a row of the wave sees
     const int w_hi = base + ib;                      // highest
     const int lo_ib = max(0, base + ib - c.wg + 1);  // every row of the wave sees [lo_ib, base+ia]
+
+    floatx16 O[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) zero16(O[b]);
+    float mrun = -INFINITY, lsum = 0.f;
+
+    // split-window partials, one record of PF4 float4 per (item, split,
+    // thread): the running reference, the mass, then O^T.  AT_PART stores
+    // this lane's state after its tiles; AT_MERGE combines the p.nsp states
+    // of its lane against their largest reference, before the query halves
+    // take their registers (two records in flight at a time).
+    constexpr int PF4 = (NB * 16 + 2 + 3) / 4;
+    if constexpr (MODE == AT_MERGE) {
+        const float4* pp = reinterpret_cast<const float4*>(p.apart) + ((int64_t)w * p.nsp * AT_THREADS + tid) * PF4;
+        for (int k = 0; k < p.nsp; ++k) mrun = fmaxf(mrun, pp[(int64_t)k * AT_THREADS * PF4].x);
+#pragma unroll 2
+        for (int k = 0; k < p.nsp; ++k) {
+            const float4* pk = pp + (int64_t)k * AT_THREADS * PF4;
+            float4 r[PF4];
+#pragma unroll
+            for (int f = 0; f < PF4; ++f) r[f] = pk[f];
+            const float* x = reinterpret_cast<const float*>(r);
+            const float wk = x[0] == -INFINITY ? 0.f : ex2(x[0] - mrun);   // a split that saw no key adds nothing
+            lsum += wk * x[1];
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) O[b][v] += wk * x[2 + b * 16 + v];
+        }
+    }
 
     // Q^T halves of this lane: q[r0+i][gh][16 st + 8 hf + e] * scale * log2 e
     u32x4 qh[NS], ql[NS];
@@ -366,19 +407,18 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
             dma16(src + ch * 512, __builtin_amdgcn_readfirstlane(lds_addr(tiles + buf * BUF + ch * 512)));
     };
 
-    floatx16 O[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) zero16(O[b]);
-    float mrun = -INFINITY, lsum = 0.f;
-
     // ---- near part: online softmax over the key tiles ----
-    issue(0, 0);
+    // the block's tiles: all of them, split sp's range of them, or none (merge)
+    const int per = (ntiles + nsp - 1) / nsp;
+    const int tA = MODE == AT_MERGE ? 0 : min(ntiles, sp * per);
+    const int tB = MODE == AT_MERGE ? 0 : min(ntiles, tA + per);
+    if (tA < tB) issue(tA, 0);
 #pragma unroll 1
-    for (int tt = 0; tt < ntiles; ++tt) {
-        const int buf = tt & 1;
+    for (int tt = tA; tt < tB; ++tt) {
+        const int buf = (tt - tA) & 1;
         __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of tile tt have landed
         __syncthreads();                 // ... and every wave's; tile tt-1 is no longer read
-        if (tt + 1 < ntiles) issue(tt + 1, buf ^ 1);
+        if (tt + 1 < tB) issue(tt + 1, buf ^ 1);
 
         const bool sink = tt < nst;
         const int tb = sink ? tt * KT : (j0 + tt - nst) * KT;
@@ -515,6 +555,22 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
             if (k + 2 < 2 * NB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
         __builtin_amdgcn_s_setprio(0);
+    }
+    if constexpr (MODE == AT_PART) {
+        float4 r[PF4];
+        float* x = reinterpret_cast<float*>(r);
+        x[0] = mrun;
+        x[1] = lsum;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) x[2 + b * 16 + v] = O[b][v];
+#pragma unroll
+        for (int f = NB * 16 + 2; f < PF4 * 4; ++f) x[f] = 0.f;
+        float4* pp = reinterpret_cast<float4*>(p.apart) + (((int64_t)w * nsp + sp) * AT_THREADS + tid) * PF4;
+#pragma unroll
+        for (int f = 0; f < PF4; ++f) pp[f] = r[f];
+        return;
     }
     float den = lsum + __shfl_xor(lsum, 32, 64);   // near mass relative to mrun
 
@@ -733,14 +789,46 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
     }
 }
 
+// Splits of the window per (sub-chunk, group, head group) item: enough for
+// about 256 blocks, at most 16, at least 4 key tiles per split, and never
+// more than the partials plane holds (256 pairs).
+static int attend_splits(const KParams& p, int items)
+{
+    const int max_tiles = (p.ns + KT - 1) / KT + (p.W + SUB + KT - 1) / KT + 1;
+    int n = min(16, 256 / max(items, 1));
+    n = min(n, max_tiles / 4);
+    return max(n, 1);
+}
+
+template <int D, int MT>
+static hipError_t launch_dm(const KParams& p0, hipStream_t st)
+{
+    constexpr int HPB = AtCfg<D>::HPB;
+    const int items = p0.S * p0.G * ((p0.H + HPB - 1) / HPB);
+    KParams p = p0;
+    p.nsp = attend_splits(p, items);
+    if (p.nsp == 1) {
+        hipLaunchKernelGGL((k_attend<D, MT, AT_FULL>), dim3(items), dim3(AtCfg<D>::THREADS), 0, st, p);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((k_attend<D, MT, AT_PART>), dim3(items * p.nsp), dim3(AtCfg<D>::THREADS), 0, st, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_attend<D, MT, AT_MERGE>), dim3(items), dim3(AtCfg<D>::THREADS), 0, st, p);
+    return hipGetLastError();
+}
+
 template <int D>
 static hipError_t launch_d(const KParams& p, hipStream_t st)
 {
-    constexpr int HPB = AtCfg<D>::HPB;
-    dim3 grid(p.S * p.G * ((p.H + HPB - 1) / HPB));
-    if (p.m <= 32) hipLaunchKernelGGL((k_attend<D, 1>), grid, dim3(AtCfg<D>::THREADS), 0, st, p);
-    else hipLaunchKernelGGL((k_attend<D, 2>), grid, dim3(AtCfg<D>::THREADS), 0, st, p);
-    return hipGetLastError();
+    return p.m <= 32 ? launch_dm<D, 1>(p, st) : launch_dm<D, 2>(p, st);
+}
+
+size_t attend_part_floats(int d)
+{
+    const int threads = d > 128 ? AtCfg<256>::THREADS : AtCfg<128>::THREADS;
+    const int nb = d >= 32 ? d / 32 : 1;
+    return (size_t)256 * threads * 4 * ((nb * 16 + 2 + 3) / 4);
 }
 
 int kv_tiles(int ns, int W, int S)

@@ -44,6 +44,8 @@ struct KParams {
     float* TH;   // [S][nh*m][dv]   Theta increments, then Theta before each sub-chunk
     const float* theta_prev;  // Theta before sub-chunk s at theta_prev + s*theta_prev_stride
     int64_t theta_prev_stride;
+    float* apart;             // split-window attention partials (attend_part_floats())
+    int nsp;                  // splits of the window per attention work item (set by launch_attend)
     unsigned short* kvs;      // [G][kv_tiles] fp16 key tiles of the pass (k_kv_split)
     int kv_tiles;             // tiles per group: the sinks, then the aligned window tiles
     // fused ingest and output steps (null: off)
@@ -155,6 +157,9 @@ hipError_t launch_attend(const KParams& p, hipStream_t st);
 // tiles per group and bytes per tile of the fp16 key tiles
 int kv_tiles(int ns, int W, int S);
 size_t kv_tile_bytes(int d);
+// floats of the split-window attention partials (a plane of fixed size: at
+// most 256 (block, split) pairs of one launch)
+size_t attend_part_floats(int d);
 hipError_t launch_ring_commit(const KParams& p, hipStream_t st);
 hipError_t launch_meta(const KParams& p, hipStream_t st);
 hipError_t launch_rewind(const KParams& p, hipStream_t st);

@@ -280,6 +280,28 @@ def test_small_full():
     check_state(read_state(st), orc)
 
 
+def test_split_window_calls():
+    """Calls with few attention work items split the window over several
+    blocks and merge their partial softmax states: prefills of 1500 and 700
+    rows (2 and 5 splits; the far field starts at row 2048), then 64-, 37-
+    and 64-row attend_chunk + commit calls (16 splits), at the max-window
+    geometry, every output against the oracle."""
+    cfg = synth.CONFIGS["maxwin"]
+    banner("maxwin split-window calls: prefill 1500 + 700, chunks 64/37/64")
+    host = synth.make_state(cfg)
+    sizes = [64, 37, 64]
+    n = 2200 + sum(sizes)
+    q, k, v = synth.rows(cfg, 0, n)
+    st = _state(cfg, host)
+    orc = oracle.from_config(cfg, host, threads=oracle_threads())
+    for a, b in ((0, 1500), (1500, 2200)):
+        got = _prefill(cfg, st, q[a:b], k[a:b], v[a:b], poison=True)
+        check_out(got, orc.step(q[a:b], k[a:b], v[a:b]), f"prefill rows {a}..{b - 1}")
+    got = _chunks(cfg, st, q[2200:], k[2200:], v[2200:], sizes, poison=True)
+    check_out(got, orc.step(q[2200:], k[2200:], v[2200:]), f"chunks {sizes}")
+    check_state(read_state(st), orc)
+
+
 def _sample_rows(T, w, seed=0):
     r = np.random.default_rng(seed)
     s = set(range(0, 3)) | set(range(T - 64, T)) | set(r.integers(0, T, 96).tolist())
