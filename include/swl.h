@@ -86,7 +86,7 @@ typedef struct swl_state {
 /* Bytes of scratch a call over `rows` rows needs (attend_chunk + commit on
  * the same rows, prefill, or attend_token with rows = 1).  Prefill over
  * more rows than one pass holds reuses the scratch pass after pass, so the
- * size stops growing at 16384 rows.  Returns 0 for an invalid geometry. */
+ * size stops growing at 32768 rows.  Returns 0 for an invalid geometry. */
 size_t swl_scratch_bytes(const swl_geom* geom, int64_t rows);
 
 /* The empty state (o1b_meta's fields at zero pushes; o1b_far_e's empty far

@@ -3,7 +3,7 @@
 // pages' encoder (cortiq-engine 0.8.51 src/gpu_wgpu/o1_batch.rs, encode:
 // far_e, attend, far_commit, ring_commit, meta): the far commit must follow
 // every read of the old accumulator, and the ring commit every read of the
-// evicted rows.  A prefill pass runs the same steps over up to 256
+// evicted rows.  A prefill pass runs the same steps over up to 512
 // sub-chunks per launch.
 #include <math.h>
 #include <string.h>

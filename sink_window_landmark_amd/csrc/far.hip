@@ -251,11 +251,14 @@ __device__ __forceinline__ MZ mz_merge(MZ a, MZ b)
     return {M, za + zb};
 }
 
-// One wave per landmark row; lane l takes sub-chunks 4l .. 4l+3 (S <= 256):
+// One wave per landmark row; lane l takes sub-chunks MZ_PER l .. MZ_PER l +
+// MZ_PER - 1 (MZ_PER = PASS_SUBS / 64, so S <= PASS_SUBS):
 // the merge of each lane's run, an exclusive scan of the runs over the wave,
 // then every lane applies the recurrence above to its own sub-chunks from
 // the state before them (so M'_s and R_s are exactly the serial ones and Z
 // differs from the serial sum only in rounding order).
+constexpr int MZ_PER = PASS_SUBS / 64;
+
 __global__ __launch_bounds__(256) void k_mz_scan(KParams p)
 {
     const int64_t nhm = (int64_t)p.nh * p.m;
@@ -263,17 +266,17 @@ __global__ __launch_bounds__(256) void k_mz_scan(KParams p)
     const int64_t ghb = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (ghb >= nhm) return;   // (uniform over the wave)
     const int64_t gh = ghb / p.m, b = ghb % p.m;
-    float mx[4], zl[4];
+    float mx[MZ_PER], zl[MZ_PER];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int s = min(4 * lane + k, p.S - 1);
+    for (int k = 0; k < MZ_PER; ++k) {
+        const int s = min(MZ_PER * lane + k, p.S - 1);
         mx[k] = p.Ms[(int64_t)s * nhm + ghb];
         zl[k] = p.Rs[(int64_t)s * nhm + ghb];
-        if (4 * lane + k >= p.S) mx[k] = -INFINITY;   // past the last sub-chunk: empty
+        if (MZ_PER * lane + k >= p.S) mx[k] = -INFINITY;   // past the last sub-chunk: empty
     }
     MZ run = {-INFINITY, 0.f};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) run = mz_merge(run, MZ{mx[k], zl[k]});
+    for (int k = 0; k < MZ_PER; ++k) run = mz_merge(run, MZ{mx[k], zl[k]});
     // inclusive scan over the lanes, then shift to the exclusive prefix
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -286,8 +289,8 @@ __global__ __launch_bounds__(256) void k_mz_scan(KParams p)
     MZ st = mz_merge(MZ{p.mz[gh * 2 * p.m + b], p.mz[gh * 2 * p.m + p.m + b]}, pre);
     float M = st.M, Z = st.Z;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int s = 4 * lane + k;
+    for (int k = 0; k < MZ_PER; ++k) {
+        const int s = MZ_PER * lane + k;
         if (s < p.S) {
             const float Mn = fmaxf(M, mx[k]);
             const float R = (Mn == M) ? 1.0f : expf(M - Mn);

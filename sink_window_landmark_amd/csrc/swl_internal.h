@@ -10,7 +10,7 @@
 namespace swl {
 
 constexpr int SUB = SWL_SUB;           // rows of a sub-chunk
-constexpr int PASS_SUBS = 256;         // sub-chunks per prefill pass (16384 rows)
+constexpr int PASS_SUBS = 512;         // sub-chunks per prefill pass (32768 rows)
 
 // Everything a kernel of one call (or one prefill pass) needs, passed by value.
 struct KParams {

@@ -57,7 +57,7 @@ def test_scratch_bytes_grows_then_caps():
     b64 = swl.swl_scratch_bytes(g, 64)
     b65 = swl.swl_scratch_bytes(g, 65)
     assert 0 < b1 == b64 < b65
-    assert swl.swl_scratch_bytes(g, 16384) == swl.swl_scratch_bytes(g, 10 ** 7)
+    assert swl.swl_scratch_bytes(g, 32768) == swl.swl_scratch_bytes(g, 10 ** 7)
     assert swl.swl_scratch_bytes(g, 0) == b1
 
 

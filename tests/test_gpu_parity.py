@@ -457,8 +457,8 @@ def test_resume_from_copied_state():
 
 
 def test_prefill_passes_match_one_long_call():
-    """More rows than one prefill pass holds (16384) against the oracle."""
-    cfg = synth.Config("long", G=1, H=2, d=32, dv=32, ns=4, W=512, m=8, rows=20000, rope=True,
+    """More rows than one prefill pass holds (32768) against the oracle."""
+    cfg = synth.Config("long", G=1, H=2, d=32, dv=32, ns=4, W=512, m=8, rows=36000, rope=True,
                        landmark_scale=0.2)
     banner(f"long prefill T={cfg.rows}")
     host = synth.make_state(cfg)
@@ -466,7 +466,7 @@ def test_prefill_passes_match_one_long_call():
     st = _state(cfg, host)
     got = _prefill(cfg, st, q, k, v)
     rows = _sample_rows(cfg.rows, cfg.W)
-    rows = np.union1d(rows, np.arange(16384 - 70, 16384 + 70))
+    rows = np.union1d(rows, np.arange(32768 - 70, 32768 + 70))
     mask = np.zeros(cfg.rows, bool)
     mask[rows] = True
     orc = oracle.from_config(cfg, host)
