@@ -394,6 +394,78 @@ def cpu_baseline(cfg, budget_s):
                        f"evicting), after a {fill}-row fill; {el:.1f} s")
 
 
+def other_configs(args):
+    """The other workloads of the layer, timed through the same entry points:
+    the tiny layer's one 64-row chunk from its 10/16 ring (attend_chunk +
+    commit, the state restored between repetitions outside the timed
+    region), the small layer's 4096-row prompt and the mixed-window layer's
+    131072-row prompt from the empty state (swl_init_state + swl_prefill)."""
+    import torch
+    import synth
+    import sink_window_landmark_amd as swl
+
+    dev = "cuda"
+    res = {}
+
+    def tensors(cfg, T):
+        q, k, v = synth.rows(cfg, 0, T)
+        return [torch.from_numpy(x).to(dev) for x in (q, k, v)]
+
+    # tiny: one chunk, latency per call pair
+    cfg = synth.TINY
+    geom = swl.Geom(cfg.G, cfg.H, cfg.m, cfg.W, cfg.ns, cfg.d, cfg.dv)
+    host = synth.make_state(cfg)
+    st = swl.LayerState.from_host(geom, host, device=dev)
+    saved = {n: getattr(st, n).clone() for n in ("meta", "ring_k", "ring_v", "mz", "theta")}
+    q, k, v = tensors(cfg, cfg.rows)
+    out = torch.empty((cfg.rows, cfg.nh, cfg.dv), dtype=torch.float32, device=dev)
+    scr = swl.alloc_scratch(geom, cfg.rows, device=dev)
+    times = []
+    for rep in range(25):
+        for n, t in saved.items():
+            getattr(st, n).copy_(t)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        swl.swl_attend_chunk(st, q, k, v, out, scr)
+        swl.swl_commit(st, k, v, scr)
+        b.record()
+        torch.cuda.synchronize()
+        if rep >= 5:
+            times.append(a.elapsed_time(b) * 1e3)
+    res["tiny"] = dict(us_per_chunk=float(np.median(times)), rows=cfg.rows,
+                       what="attend_chunk + commit of one 64-row chunk, median of 20")
+
+    for cfg, steps in ((synth.SMALL, 10), (synth.MIXED, 3)):
+        T = cfg.rows
+        geom = swl.Geom(cfg.G, cfg.H, cfg.m, cfg.W, cfg.ns, cfg.d, cfg.dv)
+        st = swl.LayerState.from_host(geom, synth.make_state(cfg), device=dev)
+        q, k, v = tensors(cfg, T)
+        out = torch.empty((T, cfg.nh, cfg.dv), dtype=torch.float32, device=dev)
+        scr = swl.alloc_scratch(geom, T, device=dev)
+        windows = cfg.meta_windows()
+
+        def step():
+            swl.swl_init_state(st, windows)
+            swl.swl_prefill(st, q, k, v, out, scr)
+
+        step()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            step()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        fl = near_flops(cfg, T) + sum(far_flops(cfg, T))
+        res[cfg.name] = dict(ms_per_prompt=ms, rows=T, rows_per_s=T / (ms * 1e-3),
+                             algorithmic_tflops=fl / (ms * 1e-3) / 1e12,
+                             windows=[cfg.window(g) for g in range(cfg.G)])
+        del q, k, v, out, scr, st
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -406,6 +478,8 @@ def main():
     ap.add_argument("--no-chunk-api", dest="chunk_api", action="store_false")
     ap.add_argument("--no-fused", dest="fused", action="store_false",
                     help="skip the fused RoPE + gate prefill leg")
+    ap.add_argument("--no-configs", dest="configs", action="store_false",
+                    help="skip the tiny, small and mixed-window workloads")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy (the reference kernel "
                          "for scaling HBM byte counters)")
@@ -474,6 +548,8 @@ def main():
         line["chunk_api_rows_per_s"] = res["chunk_api_rows_per_s"]
     if "exact_attention" in res:
         line["exact_attention"] = res["exact_attention"]
+    if args.configs:
+        line["other_configs"] = other_configs(args)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(line), flush=True)
