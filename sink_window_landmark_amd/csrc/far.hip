@@ -68,40 +68,52 @@ __device__ __forceinline__ int kswz(int r, int c)
 // ---------------------------------------------------------------------------
 // far_score: L[s][gh*m+b][j] = scale <q~_{gh,b}, key evicted by row j>, -inf
 // for rows that do not evict, and per landmark row the local max mx and mass
-// zl = sum_j exp(l_j - mx) of the sub-chunk.  One block per (sub-chunk,
-// group); the evicted keys are staged in LDS as fp16 hi/lo.  MFMA
-// C[hb][j] = Q~ K_e^T on v_mfma_f32_32x32x16_f16 (three split products per
-// k-step; lane (row, hf) holds columns 16 st + 8 hf .. +7 of its row).
+// zl = sum_j exp(l_j - mx) of the sub-chunk.  One block per (group, run of
+// FS_RUN consecutive sub-chunks); wave w of the block's NWV takes
+// landmark-row tiles w, w + NWV, ..., and when a group has at most NWV of
+// them its tile's query halves stay in registers for the whole run.  The evicted keys of a
+// sub-chunk are staged in LDS as fp16 hi/lo, double-buffered: the loads for
+// the next sub-chunk are in flight while the current one is multiplied.
+// MFMA C[hb][j] = Q~ K_e^T on v_mfma_f32_32x32x16_f16 (three split products
+// per k-step; lane (row, hf) holds columns 16 st + 8 hf .. +7 of its row).
 // ---------------------------------------------------------------------------
-constexpr int FS_THREADS = 256;
+constexpr int FS_RUN = 4;
+// eight waves; four at d = 256, where the query halves alone take 128 registers
+template <int D>
+constexpr int fs_threads() { return D > 128 ? 256 : 512; }
 
 template <int D>
-__global__ __launch_bounds__(FS_THREADS) void k_far_score(KParams p)
+__global__ __launch_bounds__(fs_threads<D>()) void k_far_score(KParams p)
 {
+    constexpr int FS_THREADS = fs_threads<D>();
     constexpr int KD = D < 16 ? 16 : D;    // key width padded to whole k-steps
     constexpr int NS = KD / 16;
     constexpr int KH = 32 * KD;            // halves of one [32][KD] tile
-    // evicted keys of the sub-chunk as fp16 hi/lo: rows j = 32 jt + r in
-    // tile jt (hi at ek + jt * 2 KH, lo KH further), zero for rows that do
-    // not evict and for the columns past D
-    __shared__ __align__(16) unsigned short ek[2 * 2 * KH];
-    const int w = xcd_work_item(blockIdx.x, p.S * p.G);
-    const int s = w % p.S, g = w / p.S;
-    const int r0 = s * SUB;
-    const int ks = min(SUB, p.T - r0);
+    constexpr int NWV = FS_THREADS / 64;
+    // two buffers of the evicted keys of a sub-chunk as fp16 hi/lo: rows
+    // j = 32 jt + r in tile jt (hi at jt * 2 KH, lo KH further), zero for
+    // rows that do not evict and for the columns past D
+    __shared__ __align__(16) unsigned short ek[2][2 * 2 * KH];
+    typedef float v4 __attribute__((ext_vector_type(4)));
+    constexpr int N = SUB * (KD / 4);      // 4-column pieces of the 64 rows
+    constexpr int PT = (N + FS_THREADS - 1) / FS_THREADS;
+
+    const int nrun = (p.S + FS_RUN - 1) / FS_RUN;
+    const int w = xcd_work_item(blockIdx.x, nrun * p.G);
+    const int run = w % nrun, g = w / nrun;
+    const int s_lo = run * FS_RUN, s_hi = min(p.S, s_lo + FS_RUN);
     const GMeta c = load_gmeta(p.meta, g, p.W);
-    const SubMeta sm = sub_meta(c, r0);
-    const int jlo = max(sm.j0, 0);
     const int hm = p.H * p.m;
     const int64_t nhm = (int64_t)p.nh * p.m;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, ln = lane & 31;
-    {
-        // 4-column pieces of the 64 rows: clamped unconditional loads (all in
-        // flight at once), the row and column selection at the store
-        typedef float v4 __attribute__((ext_vector_type(4)));
-        constexpr int N = SUB * (KD / 4);
-        constexpr int PT = (N + FS_THREADS - 1) / FS_THREADS;
-        v4 x[PT];
+    const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, ln = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nht = (hm + 31) / 32;
+    const bool resident = nht <= NWV;      // one landmark-row tile per wave at most
+
+    // clamped unconditional loads of sub-chunk s's evicted keys (all in
+    // flight at once), then their rows and columns selected at the store
+    auto load_keys = [&](int s, v4 (&x)[PT]) {
+        const int r0 = s * SUB, ks = min(SUB, p.T - r0);
 #pragma unroll
         for (int u = 0; u < PT; ++u) {
             const int e = min(tid + u * FS_THREADS, N - 1);
@@ -114,6 +126,10 @@ __global__ __launch_bounds__(FS_THREADS) void k_far_score(KParams p)
             const float4 kx = rope4(pos < c.len0 ? ra : ia, kt, c4, D);
             x[u] = v4{kx.x, kx.y, kx.z, kx.w};
         }
+    };
+    auto store_keys = [&](int s, const v4 (&x)[PT], unsigned short* eb) {
+        const int r0 = s * SUB, ks = min(SUB, p.T - r0);
+        const int jlo = max(sub_meta(c, r0).j0, 0);
 #pragma unroll
         for (int u = 0; u < PT; ++u) {
             const int e = tid + u * FS_THREADS;
@@ -124,107 +140,126 @@ __global__ __launch_bounds__(FS_THREADS) void k_far_score(KParams p)
                 fsplit<true>(live ? x[u].x : 0.f, live ? x[u].y : 0.f, h0, l0);
                 fsplit<true>(live ? x[u].z : 0.f, live ? x[u].w : 0.f, h1, l1);
                 const int jt = j >> 5, r = j & 31;
-                unsigned short* t = ek + jt * 2 * KH + r * KD + kswz<KD>(r, c4 >> 3) * 8 + (c4 & 4);
+                unsigned short* t = eb + jt * 2 * KH + r * KD + kswz<KD>(r, c4 >> 3) * 8 + (c4 & 4);
                 *reinterpret_cast<fu32x2*>(t) = fu32x2{h0, h1};
                 *reinterpret_cast<fu32x2*>(t + KH) = fu32x2{l0, l1};
             }
         }
-    }
-    __syncthreads();
-    float* L = p.E + ((int64_t)s * nhm + (int64_t)g * hm) * SUB;
-    float* MX = p.Ms + (int64_t)s * nhm + (int64_t)g * hm;   // local max (the scan overwrites)
-    float* ZL = p.Rs + (int64_t)s * nhm + (int64_t)g * hm;   // local mass (the scan overwrites)
-    const int nht = (hm + 31) / 32;
-    for (int ht = wave; ht < nht; ht += FS_THREADS / 64) {
+    };
+    // landmark query halves of tile ht: q~[hb][16 st + 8 hf + e]
+    fu32x4 qah[NS], qal[NS];
+    auto load_q = [&](int ht) {
         const int hb_a = ht * 32 + ln;   // A row of this lane
-        // landmark query halves: q~[hb][16 st + 8 hf + e]
-        fu32x4 qah[NS], qal[NS];
-        {
-            const float* qr = p.q_tilde + ((int64_t)g * hm + min(hb_a, hm - 1)) * D;
+        const float* qr = p.q_tilde + ((int64_t)g * hm + min(hb_a, hm - 1)) * D;
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            const int d0 = 16 * st + 8 * hf;
+            float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = x;
+            if (d0 < D) {
+                x = *reinterpret_cast<const float4*>(qr + d0);
+                y = *reinterpret_cast<const float4*>(qr + d0 + 4);
+            }
+            unsigned h[4], l[4];
+            fsplit<true>(x.x, x.y, h[0], l[0]);
+            fsplit<true>(x.z, x.w, h[1], l[1]);
+            fsplit<true>(y.x, y.y, h[2], l[2]);
+            fsplit<true>(y.z, y.w, h[3], l[3]);
+            qah[st] = fu32x4{h[0], h[1], h[2], h[3]};
+            qal[st] = fu32x4{l[0], l[1], l[2], l[3]};
+        }
+    };
+
+    {
+        v4 x[PT];
+        load_keys(s_lo, x);
+        store_keys(s_lo, x, ek[0]);
+    }
+    if (resident && wave < nht) load_q(wave);
+#pragma unroll 1
+    for (int s = s_lo; s < s_hi; ++s) {
+        const int buf = (s - s_lo) & 1;
+        __syncthreads();   // ek[buf] holds sub-chunk s; ek[buf ^ 1] is no longer read
+        v4 xn[PT];
+        const bool next = s + 1 < s_hi;
+        if (next) load_keys(s + 1, xn);
+
+        const int r0 = s * SUB, ks = min(SUB, p.T - r0);
+        const int jlo = max(sub_meta(c, r0).j0, 0);
+        float* L = p.E + ((int64_t)s * nhm + (int64_t)g * hm) * SUB;
+        float* MX = p.Ms + (int64_t)s * nhm + (int64_t)g * hm;   // local max (the scan overwrites)
+        float* ZL = p.Rs + (int64_t)s * nhm + (int64_t)g * hm;   // local mass (the scan overwrites)
+        const unsigned short* eb = ek[buf];
+        for (int ht = wave; ht < nht; ht += NWV) {
+            if (!resident) load_q(ht);
+            // both 32-row tiles of evicted keys in one k-step loop: each
+            // step's query halves feed six products on four accumulators,
+            // and the LDS reads run two steps ahead of their products
+            floatx16 sh[2], sx[2];
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    sh[jt][v] = 0.f;
+                    sx[jt][v] = 0.f;
+                }
 #pragma unroll
             for (int st = 0; st < NS; ++st) {
-                const int d0 = 16 * st + 8 * hf;
-                float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = x;
-                if (d0 < D) {
-                    x = *reinterpret_cast<const float4*>(qr + d0);
-                    y = *reinterpret_cast<const float4*>(qr + d0 + 4);
-                }
-                unsigned h[4], l[4];
-                fsplit<true>(x.x, x.y, h[0], l[0]);
-                fsplit<true>(x.z, x.w, h[1], l[1]);
-                fsplit<true>(y.x, y.y, h[2], l[2]);
-                fsplit<true>(y.z, y.w, h[3], l[3]);
-                qah[st] = fu32x4{h[0], h[1], h[2], h[3]};
-                qal[st] = fu32x4{l[0], l[1], l[2], l[3]};
-            }
-        }
-        // both 32-row tiles of evicted keys in one k-step loop: each step's
-        // query halves feed six products on four accumulators, and the LDS
-        // reads run two steps ahead of their products
-        floatx16 sh[2], sx[2];
+                const int ck = kswz<KD>(ln, 2 * st + hf) * 8;
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
+                for (int jt = 0; jt < 2; ++jt) {
+                    const unsigned short* kr = eb + jt * 2 * KH + ln * KD + ck;
+                    const fu32x4 bh = *reinterpret_cast<const fu32x4*>(kr);
+                    const fu32x4 bl = *reinterpret_cast<const fu32x4*>(kr + KH);
+                    sh[jt] = fmfma16(qah[st], bh, sh[jt]);
+                    sx[jt] = fmfma16(qah[st], bl, sx[jt]);
+                    sx[jt] = fmfma16(qal[st], bh, sx[jt]);
+                }
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+            for (int st = 0; st < NS; ++st) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+                if (st + 2 < NS) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            }
+            floatx16 acc[2];
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[jt][v] = fmaf(sx[jt][v], F_LO_DOWN, sh[jt][v]);
+            // lane holds rows hb = ht*32 + kappa(v, hf), columns j = jt*32 + ln
+            float mx[16];
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                sh[jt][v] = 0.f;
-                sx[jt][v] = 0.f;
+                float m2 = -INFINITY;
+#pragma unroll
+                for (int jt = 0; jt < 2; ++jt) {
+                    const int j = jt * 32 + ln;
+                    const float l = (j >= jlo && j < ks) ? acc[jt][v] * p.scale : -INFINITY;
+                    acc[jt][v] = l;
+                    m2 = fmaxf(m2, l);
+                }
+                mx[v] = max32(m2);   // over the 32 evicting rows j of this lane half
             }
 #pragma unroll
-        for (int st = 0; st < NS; ++st) {
-            const int ck = kswz<KD>(ln, 2 * st + hf) * 8;
+            for (int v = 0; v < 16; ++v) {
+                const int hb = ht * 32 + fkap(v, hf);
+                float z = 0.f;
+                if (mx[v] != -INFINITY) {
 #pragma unroll
-            for (int jt = 0; jt < 2; ++jt) {
-                const unsigned short* kr = ek + jt * 2 * KH + ln * KD + ck;
-                const fu32x4 bh = *reinterpret_cast<const fu32x4*>(kr);
-                const fu32x4 bl = *reinterpret_cast<const fu32x4*>(kr + KH);
-                sh[jt] = fmfma16(qah[st], bh, sh[jt]);
-                sx[jt] = fmfma16(qah[st], bl, sx[jt]);
-                sx[jt] = fmfma16(qal[st], bh, sx[jt]);
-            }
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+                    for (int jt = 0; jt < 2; ++jt) z += expf(acc[jt][v] - mx[v]);
+                }
+                z = sum32(z);
+                if (hb < hm) {
 #pragma unroll
-        for (int st = 0; st < NS; ++st) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
-            if (st + 2 < NS) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        }
-        floatx16 acc[2];
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[jt][v] = fmaf(sx[jt][v], F_LO_DOWN, sh[jt][v]);
-        // lane holds rows hb = ht*32 + kappa(v, hf), columns j = jt*32 + ln
-        float mx[16];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            float m2 = -INFINITY;
-#pragma unroll
-            for (int jt = 0; jt < 2; ++jt) {
-                const int j = jt * 32 + ln;
-                const float l = (j >= jlo && j < ks) ? acc[jt][v] * p.scale : -INFINITY;
-                acc[jt][v] = l;
-                m2 = fmaxf(m2, l);
-            }
-            mx[v] = max32(m2);   // over the 32 evicting rows j of this lane half
-        }
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int hb = ht * 32 + fkap(v, hf);
-            float z = 0.f;
-            if (mx[v] != -INFINITY) {
-#pragma unroll
-                for (int jt = 0; jt < 2; ++jt) z += expf(acc[jt][v] - mx[v]);
-            }
-            z = sum32(z);
-            if (hb < hm) {
-#pragma unroll
-                for (int jt = 0; jt < 2; ++jt) L[(int64_t)hb * SUB + jt * 32 + ln] = acc[jt][v];
-                if (ln == 0) {
-                    MX[hb] = mx[v];
-                    ZL[hb] = z;
+                    for (int jt = 0; jt < 2; ++jt) L[(int64_t)hb * SUB + jt * 32 + ln] = acc[jt][v];
+                    if (ln == 0) {
+                        MX[hb] = mx[v];
+                        ZL[hb] = z;
+                    }
                 }
             }
         }
+        if (next) store_keys(s + 1, xn, ek[buf ^ 1]);
     }
 }
 
@@ -525,7 +560,8 @@ __global__ __launch_bounds__(256) void k_theta_scan(KParams p, int commit)
 template <int D>
 static void launch_fs(const KParams& p, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_far_score<D>, dim3(p.S * p.G), dim3(FS_THREADS), 0, st, p);
+    const int nrun = (p.S + FS_RUN - 1) / FS_RUN;
+    hipLaunchKernelGGL(k_far_score<D>, dim3(nrun * p.G), dim3(fs_threads<D>()), 0, st, p);
 }
 
 hipError_t launch_far_score(const KParams& p, hipStream_t st)
