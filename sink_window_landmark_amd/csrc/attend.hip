@@ -59,6 +59,7 @@
 //   product.
 // Softmax runs online in base 2 (q is pre-scaled by scale*log2 e).
 #include "swl_internal.h"
+#include "lanes.h"
 
 namespace swl {
 
@@ -500,7 +501,7 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
                 tmax = fmaxf(tmax, sv);
             }
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        tmax = pair_max<5>(tmax);   // with the lane 32 away (permlane swap, no LDS)
         // raise the reference (and rescale the running sums) only when some
         // query's score exceeds it by more than TAU
         if (__any(tmax > mrun + TAU)) {
@@ -572,7 +573,7 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
         for (int f = 0; f < PF4; ++f) pp[f] = r[f];
         return;
     }
-    float den = lsum + __shfl_xor(lsum, 32, 64);   // near mass relative to mrun
+    float den = pair_sum<5>(lsum);   // near mass relative to mrun
 
     // ---- far readout (o1b_attend's far half) ----
     const SubMeta sm = sub_meta(c, r0);
@@ -649,7 +650,7 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
                     if (at * 32 + kap(v, hf) >= m) ef[at][v] = -INFINITY;
                     fmax = fmaxf(fmax, ef[at][v]);
                 }
-            fmax = fmaxf(fmax, __shfl_xor(fmax, 32, 64));
+            fmax = pair_max<5>(fmax);
 #pragma unroll
             for (int at = 0; at < MT; ++at)
 #pragma unroll
@@ -685,7 +686,7 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
                     mb[bt][v] = b < m ? Ms[b] * LOG2E : -INFINITY;
                     mmax = fmaxf(mmax, mb[bt][v]);
                 }
-            mmax = fmaxf(mmax, __shfl_xor(mmax, 32, 64));
+            mmax = pair_max<5>(mmax);
             const float cexp = lane_far ? fmaxf(mrun, fmax + mmax) : mrun;
             float dfar = 0.f;
 #pragma unroll
@@ -705,7 +706,7 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
                         dfar += lane_far & (b < m) ? gain * pb[r] : 0.f;
                     }
                 }
-            dfar += __shfl_xor(dfar, 32, 64);
+            dfar = pair_sum<5>(dfar);
             const bool have = lane_far && dfar >= 0.f;
             if (!have) {
                 dfar = 0.f;
