@@ -302,6 +302,30 @@ def test_split_window_calls():
     check_state(read_state(st), orc)
 
 
+@pytest.mark.parametrize("d", [32, 64])
+def test_split_window_small_heads(d):
+    """The split-window path at d = 32 and 64 (m = 16: one landmark tile),
+    three query heads per group (an idle head slot in every block) and
+    per-group windows 256/128: a 700-row prompt (3 splits per work item),
+    then 64- and 20-row attend_chunk + commit calls, against the oracle."""
+    import math
+    cfg = synth.Config("splitd", G=2, H=3, d=d, dv=d, ns=4, W=256, m=16, rows=700, windows=(256, 128),
+                       rope=True, landmark_scale=1.0 / math.sqrt(d))
+    banner(f"split-window d={d}: prefill 700, chunks 64/20")
+    host = synth.make_state(cfg)
+    sizes = [64, 20]
+    n = cfg.rows + sum(sizes)
+    q, k, v = synth.rows(cfg, 0, n)
+    st = _state(cfg, host)
+    orc = oracle.from_config(cfg, host, threads=oracle_threads())
+    T = cfg.rows
+    got = _prefill(cfg, st, q[:T], k[:T], v[:T], poison=True)
+    check_out(got, orc.step(q[:T], k[:T], v[:T]), "prefill")
+    got = _chunks(cfg, st, q[T:], k[T:], v[T:], sizes, poison=True)
+    check_out(got, orc.step(q[T:], k[T:], v[T:]), f"chunks {sizes}")
+    check_state(read_state(st), orc)
+
+
 def _sample_rows(T, w, seed=0):
     r = np.random.default_rng(seed)
     s = set(range(0, 3)) | set(range(T - 64, T)) | set(r.integers(0, T, 96).tolist())
