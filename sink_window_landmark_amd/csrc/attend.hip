@@ -288,11 +288,21 @@ __global__ __launch_bounds__(256) void k_kv_split(KParams p)
 // prompts), where one block per sub-chunk would leave most CUs idle.
 constexpr int AT_FULL = 0, AT_PART = 1, AT_MERGE = 2;
 
+// Block shape per mode: the merge takes one head per block (two waves, each
+// on a SIMD of its own), so that the few merge blocks of a small call spread
+// their far readouts over more CUs; it reads the split blocks' records by
+// their shape (AtCfg).
+template <int D, int MODE>
+struct AtShape {
+    static constexpr int HPB = MODE == AT_MERGE ? 1 : AtCfg<D>::HPB;
+    static constexpr int THREADS = HPB * 2 * 64;
+};
+
 template <int D, int MT, int MODE>
-__global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
+__global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams p)
 {
-    constexpr int AT_THREADS = AtCfg<D>::THREADS;
-    constexpr int HPB = AtCfg<D>::HPB;
+    constexpr int AT_THREADS = AtShape<D, MODE>::THREADS;
+    constexpr int HPB = AtShape<D, MODE>::HPB;
     constexpr int NB = D >= 32 ? D / 32 : 1;  // 32-row blocks of O^T
     using L = KvTile<D>;
     constexpr int KD = L::KD;
@@ -355,11 +365,16 @@ __global__ __launch_bounds__(AtCfg<D>::THREADS) void k_attend(KParams p)
     // take their registers (two records in flight at a time).
     constexpr int PF4 = (NB * 16 + 2 + 3) / 4;
     if constexpr (MODE == AT_MERGE) {
-        const float4* pp = reinterpret_cast<const float4*>(p.apart) + ((int64_t)w * p.nsp * AT_THREADS + tid) * PF4;
-        for (int k = 0; k < p.nsp; ++k) mrun = fmaxf(mrun, pp[(int64_t)k * AT_THREADS * PF4].x);
+        // this head's records among those of the split blocks' item (their
+        // shape: PH heads, PT threads)
+        constexpr int PT = AtCfg<D>::THREADS, PH = AtCfg<D>::HPB;
+        const int wp = s + p.S * (g + p.G * (h / PH));
+        const int tp = (h % PH) * 128 + tid;
+        const float4* pp = reinterpret_cast<const float4*>(p.apart) + ((int64_t)wp * p.nsp * PT + tp) * PF4;
+        for (int k = 0; k < p.nsp; ++k) mrun = fmaxf(mrun, pp[(int64_t)k * PT * PF4].x);
 #pragma unroll 2
         for (int k = 0; k < p.nsp; ++k) {
-            const float4* pk = pp + (int64_t)k * AT_THREADS * PF4;
+            const float4* pk = pp + (int64_t)k * PT * PF4;
             float4 r[PF4];
 #pragma unroll
             for (int f = 0; f < PF4; ++f) r[f] = pk[f];
@@ -815,7 +830,9 @@ static hipError_t launch_dm(const KParams& p0, hipStream_t st)
     hipLaunchKernelGGL((k_attend<D, MT, AT_PART>), dim3(items * p.nsp), dim3(AtCfg<D>::THREADS), 0, st, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_attend<D, MT, AT_MERGE>), dim3(items), dim3(AtCfg<D>::THREADS), 0, st, p);
+    // the merge: one block per (sub-chunk, group, head)
+    constexpr int MERGE_THREADS = AtShape<D, AT_MERGE>::THREADS;
+    hipLaunchKernelGGL((k_attend<D, MT, AT_MERGE>), dim3(p.S * p.G * p.H), dim3(MERGE_THREADS), 0, st, p);
     return hipGetLastError();
 }
 
