@@ -394,6 +394,29 @@ def cpu_baseline(cfg, budget_s):
                        f"evicting), after a {fill}-row fill; {el:.1f} s")
 
 
+def hbm_copy_gbs():
+    """Achievable HBM bandwidth on this GPU: a 1 GiB device-to-device copy
+    (read + write counted), best of 10 after 2 warm-up copies."""
+    import torch
+    a = torch.empty(256 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    gbs = 2 * a.numel() * 4 / (best * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return gbs
+
+
 def other_configs(args):
     """The other workloads of the layer, timed through the same entry points:
     the tiny layer's one 64-row chunk from its 10/16 ring (attend_chunk +
@@ -540,8 +563,11 @@ def main():
     if tr is not None:
         line["roofline"]["traffic"] = tr["bytes"]
         line["roofline"]["traffic_detail"] = tr
+    copy_gbs = hbm_copy_gbs()
+    line["hbm_copy_gbs"] = copy_gbs
     if "decode" in res:
         line["decode"] = res["decode"]
+        line["decode"]["frac_copy_bandwidth"] = res["decode"]["achieved_gbs"] / copy_gbs
     if "fused" in res:
         line["fused"] = res["fused"]
     if "chunk_api_rows_per_s" in res:
