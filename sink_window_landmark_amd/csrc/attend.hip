@@ -1,5 +1,6 @@
-// Attention of a call: sinks + ring window on fp32 MFMA, and the far readout
-// in the same block's epilogue.
+// Attention of a call: sinks + ring window on fp16 matrix cores at fp32
+// accuracy (hi/lo splits, below), and the far readout in the same block's
+// epilogue.
 //
 // cortiq-engine 0.8.51 src/gpu_wgpu/o1_batch.rs, o1b_attend.  Row i of a
 // sub-chunk attends to the sinks and to the last min(w_g, len0+i+1) keys of
@@ -17,7 +18,9 @@
 // The near part never depends on the far field, so every sub-chunk of a call
 // is computed in one launch: one block per (sub-chunk, KV group, group of up
 // to 4 query heads; 2 at d = 256), two waves per head, each wave owning 32
-// query rows.
+// query rows.  A launch of fewer than 256 such blocks splits each one's key
+// tiles over several blocks and merges their softmax states before the far
+// readout (AT_PART, AT_MERGE below).
 // The block's keys (the sinks, then the band of positions its rows reach)
 // stream through LDS in tiles of 32 keys shared by all heads of the group
 // (the GQA reuse of the pages' Metal and Dory kernels).
