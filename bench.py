@@ -481,8 +481,9 @@ def other_configs(args):
         torch.cuda.synchronize()
         ms = a.elapsed_time(b) / steps
         fl = near_flops(cfg, T) + sum(far_flops(cfg, T))
+        tf = fl / (ms * 1e-3) / 1e12
         res[cfg.name] = dict(ms_per_prompt=ms, rows=T, rows_per_s=T / (ms * 1e-3),
-                             algorithmic_tflops=fl / (ms * 1e-3) / 1e12,
+                             algorithmic_tflops=tf, frac_split_peak=tf / MFMA_SPLIT_PEAK_TFLOPS,
                              windows=[cfg.window(g) for g in range(cfg.G)])
         del q, k, v, out, scr, st
         torch.cuda.empty_cache()
