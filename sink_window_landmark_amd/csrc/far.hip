@@ -69,7 +69,7 @@ __device__ __forceinline__ int kswz(int r, int c)
 // far_score: L[s][gh*m+b][j] = scale <q~_{gh,b}, key evicted by row j>, -inf
 // for rows that do not evict, and per landmark row the local max mx and mass
 // zl = sum_j exp(l_j - mx) of the sub-chunk.  One block per (group, run of
-// FS_RUN consecutive sub-chunks); wave w of the block's NWV takes
+// `rl` consecutive sub-chunks, up to FS_RUN); wave w of the block's NWV takes
 // landmark-row tiles w, w + NWV, ..., and when a group has at most NWV of
 // them its tile's query halves stay in registers for the whole run.  The evicted keys of a
 // sub-chunk are staged in LDS as fp16 hi/lo, double-buffered: the loads for
@@ -78,6 +78,14 @@ __device__ __forceinline__ int kswz(int r, int c)
 // per k-step; lane (row, hf) holds columns 16 st + 8 hf .. +7 of its row).
 // ---------------------------------------------------------------------------
 constexpr int FS_RUN = 4;
+// sub-chunks per block: FS_RUN while the launch keeps at least 256 blocks,
+// fewer for short calls
+__host__ __device__ inline int fs_run(int S, int G)
+{
+    int rl = FS_RUN;
+    while (rl > 1 && ((S + rl - 1) / rl) * G < 256) rl >>= 1;
+    return rl;
+}
 // eight waves; four at d = 256, where the query halves alone take 128 registers
 template <int D>
 constexpr int fs_threads() { return D > 128 ? 256 : 512; }
@@ -98,10 +106,11 @@ __global__ __launch_bounds__(fs_threads<D>()) void k_far_score(KParams p)
     constexpr int N = SUB * (KD / 4);      // 4-column pieces of the 64 rows
     constexpr int PT = (N + FS_THREADS - 1) / FS_THREADS;
 
-    const int nrun = (p.S + FS_RUN - 1) / FS_RUN;
+    const int rl = fs_run(p.S, p.G);
+    const int nrun = (p.S + rl - 1) / rl;
     const int w = xcd_work_item(blockIdx.x, nrun * p.G);
     const int run = w % nrun, g = w / nrun;
-    const int s_lo = run * FS_RUN, s_hi = min(p.S, s_lo + FS_RUN);
+    const int s_lo = run * rl, s_hi = min(p.S, s_lo + rl);
     const GMeta c = load_gmeta(p.meta, g, p.W);
     const int hm = p.H * p.m;
     const int64_t nhm = (int64_t)p.nh * p.m;
@@ -560,7 +569,8 @@ __global__ __launch_bounds__(256) void k_theta_scan(KParams p, int commit)
 template <int D>
 static void launch_fs(const KParams& p, hipStream_t st)
 {
-    const int nrun = (p.S + FS_RUN - 1) / FS_RUN;
+    const int rl = fs_run(p.S, p.G);
+    const int nrun = (p.S + rl - 1) / rl;
     hipLaunchKernelGGL(k_far_score<D>, dim3(nrun * p.G), dim3(fs_threads<D>()), 0, st, p);
 }
 
