@@ -126,8 +126,9 @@ int swl_prefill(const swl_geom* geom, const swl_state* st,
                 const float* q, const float* k, const float* v, int64_t rows,
                 float* out, void* scratch, size_t scratch_bytes, void* stream);
 
-/* Stages of a call, as reported to a swl_stage_fn.  Launch order: far
- * score, far scan, dtheta, theta scan, kv split, attend, ring, meta. */
+/* Stages of a call, as reported to a swl_stage_fn.  Launch order: value
+ * scale, far score, far scan, dtheta, theta scan, kv split, attend, ring,
+ * meta. */
 enum swl_stage {
     SWL_STAGE_FAR_SCORE = 0,  /* evicted key x landmark scores */
     SWL_STAGE_FAR_SCAN = 1,   /* post-sub-chunk max, rescale and incoming mass */
@@ -137,7 +138,8 @@ enum swl_stage {
     SWL_STAGE_RING = 5,       /* ring commit */
     SWL_STAGE_META = 6,       /* len, head, nfar */
     SWL_STAGE_KV_SPLIT = 7,   /* the pass's keys and values as fp16 hi/lo tiles */
-    SWL_STAGE_COUNT = 8
+    SWL_STAGE_VALUE_SCALE = 8, /* the largest |value| of the pass, per group */
+    SWL_STAGE_COUNT = 9
 };
 
 /* Host callback invoked around each launch while the launches are being

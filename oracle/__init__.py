@@ -175,14 +175,20 @@ class SerialOracle:
     def rewind(self) -> None:
         """Undo the bookkeeping of the last push of every group, as the
         pages' ``dory_o1_back`` (cortiq-engine 0.8.77 src/gpu_wgpu/dory.rs)
-        does: with a full window the head steps back one slot and the far
-        count drops by one, otherwise the window loses its newest row.  Ring
-        rows and M, Z, Theta stay as they are.  Reading for an empty window
-        (the page does not guard it): nothing changes."""
+        does: after a push that evicted, the head steps back one slot and
+        the far count drops by one; after any other push the window loses
+        its newest row.  Ring rows and M, Z, Theta stay as they are.
+
+        Readings where the page is silent: the page takes a full window to
+        mean that the last push evicted, which is not so for the push that
+        filled the window (it evicted nothing, and the far count is still
+        0); a full window with a far count of 0 is therefore undone as a
+        plain push.  An empty window (the page does not guard it) is left
+        alone."""
         for p in self.parts:
             wg = self.windows[p["g"]]
             ln, hd, nf = (int(x) for x in p["meta"])
-            if ln == wg:
+            if ln == wg and nf > 0:
                 p["meta"][1] = (hd + wg - 1) % wg
                 p["meta"][2] = nf - 1
             elif ln > 0:

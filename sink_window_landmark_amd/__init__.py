@@ -30,7 +30,8 @@ EXPORTS = ("swl_scratch_bytes", "swl_init_state", "swl_attend_chunk", "swl_commi
            "swl_commit_fused", "swl_commit_rows_fused", "swl_attend_token_fused")
 
 # Stage ids of swl_stage_fn (enum swl_stage).
-STAGES = ("far_score", "far_scan", "dtheta", "theta_scan", "attend", "ring", "meta", "kv_split")
+STAGES = ("far_score", "far_scan", "dtheta", "theta_scan", "attend", "ring", "meta", "kv_split",
+          "value_scale")
 STAGE_FN = ctypes.CFUNCTYPE(None, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p)
 
 

@@ -40,7 +40,7 @@ static bool state_ok(const swl_geom* g, const swl_state* st)
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Carve {
-    size_t tok, apart, e, p, ms, rs, tz, th, kv, total;
+    size_t tok, apart, vm, e, p, ms, rs, tz, th, kv, total;
 };
 
 static Carve carve(const swl_geom* g, int S)
@@ -51,6 +51,7 @@ static Carve carve(const swl_geom* g, int S)
     // the decode plane comes first, at an offset that does not depend on S
     c.tok = off; off += align256(sizeof(float) * tok_part_floats(g->G, g->H, g->dv, g->ns, g->W));
     c.apart = off; off += align256(sizeof(float) * attend_part_floats(g->d));
+    c.vm = off; off += align256(sizeof(float) * (size_t)g->G * VM_BLOCKS);
     c.e = off;  off += align256(sizeof(float) * (size_t)S * nhm * SUB);
     c.p = off;  off += align256(sizeof(float) * (size_t)S * g->G * g->H * SUB * 64);
     c.ms = off; off += align256(sizeof(float) * (size_t)S * nhm);
@@ -94,6 +95,7 @@ static void set_scratch(KParams& p, const swl_geom* g, void* scratch, int S)
     p.TZ = reinterpret_cast<float*>(b + c.tz);
     p.TH = reinterpret_cast<float*>(b + c.th);
     p.apart = reinterpret_cast<float*>(b + c.apart);
+    p.vmax = reinterpret_cast<float*>(b + c.vm);
     p.kvs = reinterpret_cast<unsigned short*>(b + c.kv);
     p.kv_tiles = kv_tiles(g->ns, g->W, S);
 }
@@ -114,10 +116,12 @@ static void set_fuse(KParams& p, const swl_fuse* f, int64_t row0)
         if ((x) != hipSuccess) return SWL_EHIP; \
     } while (0)
 
-// far_e (scores, scan, E/P and the accumulator increment) + attention (near
-// part and far readout) of one call; the state is unchanged.
+// The values' scale, far_e (scores, scan, E/P and the accumulator
+// increment) + attention (near part and far readout) of one call; the state
+// is unchanged.
 static int run_attend(const KParams& p, hipStream_t st)
 {
+    SWL_TRY(launch_vmax(p, st));
     SWL_TRY(launch_far_score(p, st));
     SWL_TRY(launch_far_scan(p, st));
     SWL_TRY(launch_dtheta(p, st));
@@ -246,6 +250,7 @@ static int run_rows(const swl_geom* geom, const swl_state* st, const float* q, c
         set_scratch(p, geom, scratch, S_max);
         p.theta_prev = p.TH;
         p.theta_prev_stride = (int64_t)nh * geom->m * geom->dv;
+        SWL_STAGE(SWL_STAGE_VALUE_SCALE, launch_vmax(p, hs));
         SWL_STAGE(SWL_STAGE_FAR_SCORE, launch_far_score(p, hs));
         SWL_STAGE(SWL_STAGE_FAR_SCAN, launch_far_scan(p, hs));
         SWL_STAGE(SWL_STAGE_DTHETA, launch_dtheta(p, hs));

@@ -33,10 +33,13 @@
 // accumulation (the hi*lo terms of the scores in an accumulator of their
 // own); the dropped lo*lo term and the rounding of lo leave at most
 // 3 * 2^-22 of |a*b| per product a*b, at a fifth of
-// the fp32 MFMA's time for the three products.  Values split unscaled (an
-// absolute error floor of 2^-24), and the softmax weights are kept in
-// (0, 2^15] with a sum of at least 2^8 so that theirs stays far below that.  Range: |k| and
-// |scale * log2(e) * q| below 2^15, |v| below 65504.
+// the fp32 MFMA's time for the three products.  Values split unscaled
+// after a power-of-two scale per (pass, group) that brings their largest
+// magnitude into [2^13, 2^14) (k_vmax; an absolute floor of 2^-24 against
+// that), and the softmax weights are kept in (0, 2^15] with a sum of at
+// least 2^8 so that theirs stays far below that.  Range of the split
+// operands: |k| and |scale * log2(e) * q| at most 65504 (fp16's largest
+// finite value); values of any finite magnitude.
 //
 // MFMA layout (32x32 tiles; lane l, half hf = l/32, n = l%32;
 // kappa(v, hf) = (v/4)*8 + hf*4 + v%4 is the row of accumulator v):
@@ -222,7 +225,8 @@ __device__ __forceinline__ void pv_step(floatx16 (&O)[NB], const float* row, int
 // 0 .. nst-1 hold the sinks, tile nst + j the window positions 32 j ..
 // 32 j + 31 (ring positions, then the pass's rows), up to the last position
 // of the pass; rows past the end repeat the last real key (attention masks
-// them).
+// them).  Values are split times the pass's power of two (value_exp), which
+// attention takes back out of its value sums.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void k_kv_split(KParams p)
@@ -235,6 +239,7 @@ __global__ __launch_bounds__(256) void k_kv_split(KParams p)
     const GMeta c = load_gmeta(p.meta, g, p.W);
     const int last = c.len0 + p.T - 1;   // last window position of the pass
     if (t >= nst && (t - nst) * KT > last) return;
+    const int vexp = value_exp(p, g);   // values enter their split times 2^vexp
     for (int e = threadIdx.x; e < KT * (D / 4); e += 256) {
         const int r = e / (D / 4), c4 = (e % (D / 4)) * 4;
         const float* kp;
@@ -274,7 +279,7 @@ __global__ __launch_bounds__(256) void k_kv_split(KParams p)
         const int rho = e >> 2, cc = e & 3;
         float x[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = vf[kperm(cc * 8 + j)][rho];
+        for (int j = 0; j < 8; ++j) x[j] = ldexpf(vf[kperm(cc * 8 + j)][rho], vexp);
         const Split<false> s0(x[0], x[1]), s1(x[2], x[3]), s2(x[4], x[5]), s3(x[6], x[7]);
         const int dst = rho * KT + vchunk(rho, cc) * 8;
         *reinterpret_cast<u32x4*>(vo + dst) = u32x4{s0.hi, s1.hi, s2.hi, s3.hi};
@@ -343,6 +348,9 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
     const int r0 = s * SUB;
     const int ks = min(SUB, p.T - r0);
     const GMeta c = load_gmeta(p.meta, g, p.W);
+    // the key tiles hold the values times 2^vexp: the near value sums carry
+    // that factor until the epilogue
+    const int vexp = MODE == AT_PART ? 0 : value_exp(p, g);
     const int base = c.len0 + r0;                   // position of chunk row 0
     const int lo_blk = max(0, base - c.wg + 1);
     const int hi_blk = base + ks - 1;
@@ -755,11 +763,13 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
                 }
             }
             // near part to the common exponent, then the far numerator
-            const float wn = ex2(mrun - cexp - P_EXP);   // the near weights carry 2^P_EXP
+            // the near weights carry 2^P_EXP, the value sums also 2^vexp
+            const float wn = ex2(mrun - cexp - P_EXP);
+            const float wo = ldexpf(wn, -vexp);
 #pragma unroll
             for (int b = 0; b < NB; ++b)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) O[b][v] *= wn;
+                for (int v = 0; v < 16; ++v) O[b][v] *= wo;
             den = den * wn + dfar;
 #pragma unroll
             for (int bt = 0; bt < MT; ++bt) {
@@ -783,7 +793,9 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
     }
 
     if (active && i < ks) {
-        const float inv = 1.f / fmaxf(den, 1e-30f);
+        // without a far part the value sums still carry 2^vexp (with one,
+        // the near part was brought to the far part's scale above)
+        const float inv = ldexpf(1.f / fmaxf(den, 1e-30f), blk_far ? 0 : -vexp);
         float* orow = p.out + ((int64_t)(r0 + i) * p.nh + gh) * D;
         // the output gate, when on, multiplies each element on its way out
         const float* zr = p.gate ? p.gate + ((int64_t)(r0 + i) * p.nh + gh) * D : nullptr;

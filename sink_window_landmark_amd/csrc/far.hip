@@ -66,6 +66,40 @@ __device__ __forceinline__ int kswz(int r, int c)
 }
 
 // ---------------------------------------------------------------------------
+// vmax: the largest |value| of each group's pass inputs -- its sinks, the
+// window at the start of the call and the pass's rows -- as VM_BLOCKS block
+// maxima per group (value_exp reduces them): the value products of the
+// pass (key tiles, accumulator increments) scale their fp16 splits by it.
+// Block b of group g takes rows b, b + VM_BLOCKS, ... of that list, DV/4
+// lanes per row.
+// ---------------------------------------------------------------------------
+template <int DV>
+__global__ __launch_bounds__(256) void k_vmax(KParams p)
+{
+    constexpr int LPR = DV / 4 < 64 ? DV / 4 : 64;   // lanes per row (64 at dv = 256: two float4 each)
+    constexpr int RPB = 256 / LPR;                    // rows per block step
+    __shared__ float red[4];
+    const int g = blockIdx.x / VM_BLOCKS, b = blockIdx.x % VM_BLOCKS;
+    const GMeta c = load_gmeta(p.meta, g, p.W);
+    const int n = p.ns + c.len0 + p.T;
+    const int li = threadIdx.x % LPR, rb = threadIdx.x / LPR;
+    float mx = 0.f;
+    for (int r = b * RPB + rb; r < n; r += VM_BLOCKS * RPB) {
+        const float* row = r < p.ns ? p.sink_v + ((int64_t)g * p.ns + r) * DV : val_row(p, c, g, r - p.ns);
+#pragma unroll
+        for (int c4 = 4 * li; c4 < DV; c4 += 4 * LPR) {
+            const float4 x = *reinterpret_cast<const float4*>(row + c4);
+            mx = fmaxf(mx, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
+        }
+    }
+    mx = wmax(mx);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        p.vmax[(int64_t)g * VM_BLOCKS + b] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// ---------------------------------------------------------------------------
 // far_score: L[s][gh*m+b][j] = scale <q~_{gh,b}, key evicted by row j>, -inf
 // for rows that do not evict, and per landmark row the local max mx and mass
 // zl = sum_j exp(l_j - mx) of the sub-chunk.  One block per (group, run of
@@ -357,10 +391,11 @@ __global__ __launch_bounds__(256) void k_mz_scan(KParams p)
 // the commit), and TH[s][gh*m+b][t] = sum_j E_bj v_evicted(j)[t] on fp16
 // MFMA with hi/lo splits (C[b][t]; each lane holds rows hf*32 .. +31 of its
 // E row, so its prefix is a register loop, and k-step st takes rows
-// 32 hf + 8 st .. +7).  E is scaled by 2^12 before the split so that the
-// fp16 remainders of its small values stay far above their absolute floor;
-// the result is scaled back exactly.  The evicted values are staged in LDS
-// transposed.
+// 32 hf + 8 st .. +7).  E is scaled by 2^12 and the values by the pass's
+// power of two (value_exp) before the split, so that the fp16 remainders of
+// small values stay far above their absolute floor and large values stay in
+// fp16 range; the result is scaled back exactly.  The evicted values are
+// staged in LDS transposed.
 // ---------------------------------------------------------------------------
 template <int DV>
 __global__ __launch_bounds__(256) void k_dtheta(KParams p)
@@ -381,6 +416,7 @@ __global__ __launch_bounds__(256) void k_dtheta(KParams p)
     const int hm = p.H * p.m;
     const int64_t nhm = (int64_t)p.nh * p.m;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, ln = lane & 31;
+    const int vexp = value_exp(p, g);   // the values enter the split times 2^vexp
     {
         // units of two rows (2 jp, 2 jp + 1) x four columns: clamped
         // unconditional loads, then per column one fp16 pair of each half
@@ -411,7 +447,7 @@ __global__ __launch_bounds__(256) void k_dtheta(KParams p)
                 for (int q = 0; q < 4; ++q) {
                     const int t = c4 + q;
                     unsigned hi, lo;
-                    fsplit<false>(l0 ? x[u][0][q] : 0.f, l1 ? x[u][1][q] : 0.f, hi, lo);
+                    fsplit<false>(l0 ? ldexpf(x[u][0][q], vexp) : 0.f, l1 ? ldexpf(x[u][1][q], vexp) : 0.f, hi, lo);
                     const int at = t * SUB + (((jp >> 2) ^ ((t >> 1) & 7)) << 3) + ((2 * jp) & 7);
                     *reinterpret_cast<unsigned*>(vt + at) = hi;
                     *reinterpret_cast<unsigned*>(vt + VH + at) = lo;
@@ -506,7 +542,7 @@ __global__ __launch_bounds__(256) void k_dtheta(KParams p)
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[tt][v] *= 1.f / 4096.f;
+            for (int v = 0; v < 16; ++v) acc[tt][v] = ldexpf(acc[tt][v], -12 - vexp);
         // lane holds rows hb = ht*32 + kappa(v, hf), columns t = tt*32 + ln
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -528,15 +564,36 @@ __global__ __launch_bounds__(256) void k_dtheta(KParams p)
 // TH[s] <- Theta (the value before sub-chunk s, which the readout of s uses),
 // Theta <- R_s Theta + dTheta_s.  With `commit` the final Theta, M and Z go
 // to the state (o1b_far_commit: M <- M', Z <- the mass after the rows).
+//
+// Theta is carried as an unevaluated sum th + tc of two fp32 numbers
+// (compensated summation): the rounding error of each product R_s th (an
+// fma gives it exactly) and of each sum (Knuth's two-sum) goes into tc, so
+// the running value keeps about twice fp32's precision over the hundreds of
+// sub-chunks of a pass, and only its final rounding to one fp32 number
+// (and each TH[s]) is left.  The element of an accumulator that sums tens
+// of thousands of signed terms can cancel to a value far below the terms'
+// scale; plain fp32 accumulation would leave there an error of order
+// 2^-24 times the partial sums' magnitude per sub-chunk.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void two_sum(float a, float b, float& s, float& e)
+{
+#pragma clang fp contract(off)
+    s = a + b;
+    const float bv = s - a;
+    e = (a - (s - bv)) + (b - bv);
+}
+
 __global__ __launch_bounds__(256) void k_theta_scan(KParams p, int commit)
 {
+    // every product and sum below rounds on its own: a product fused into a
+    // later sum would no longer be the value whose error the fma takes
+#pragma clang fp contract(off)
     const int64_t nhm = (int64_t)p.nh * p.m;
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= nhm * p.dv) return;
     const int64_t ghb = idx / p.dv;
     const int64_t stride = nhm * p.dv;
-    float th = p.theta[idx];
+    float th = p.theta[idx], tc = 0.f;
     for (int s0 = 0; s0 < p.S; s0 += SCAN_AHEAD) {
         float dth[SCAN_AHEAD], rs[SCAN_AHEAD];
 #pragma unroll
@@ -550,7 +607,13 @@ __global__ __launch_bounds__(256) void k_theta_scan(KParams p, int commit)
             const int s = s0 + k;
             if (s < p.S) {
                 p.TH[(int64_t)s * stride + idx] = th;
-                th = rs[k] * th + dth[k];
+                // (th + tc) R + d, with the errors of R th and of the sum kept
+                const float pr = rs[k] * th;
+                const float pe = fmaf(rs[k], th, -pr);
+                float sm, se;
+                two_sum(pr, dth[k], sm, se);
+                const float lo = fmaf(rs[k], tc, pe + se);
+                two_sum(sm, lo, th, tc);
             }
         }
     }
@@ -592,6 +655,26 @@ hipError_t launch_far_scan(const KParams& p, hipStream_t st)
 {
     const int64_t nhm = (int64_t)p.nh * p.m;
     hipLaunchKernelGGL(k_mz_scan, dim3((unsigned)((nhm + 3) / 4)), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+template <int DV>
+static void launch_vm(const KParams& p, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_vmax<DV>, dim3(p.G * VM_BLOCKS), dim3(256), 0, st, p);
+}
+
+hipError_t launch_vmax(const KParams& p, hipStream_t st)
+{
+    switch (p.dv) {
+    case 8: launch_vm<8>(p, st); break;
+    case 16: launch_vm<16>(p, st); break;
+    case 32: launch_vm<32>(p, st); break;
+    case 64: launch_vm<64>(p, st); break;
+    case 128: launch_vm<128>(p, st); break;
+    case 256: launch_vm<256>(p, st); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -3,6 +3,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "swl_internal.h"
+
 namespace swl {
 
 // Lane exchanges without LDS.  The partner of a lane at bit B is the lane
@@ -145,6 +147,15 @@ __device__ __forceinline__ float max32(float x)
     x = pair_max<2>(x);
     x = pair_max<3>(x);
     return pair_max<4>(x);
+}
+
+// value_exp_of over group g's block maxima (k_vmax), evaluated by every
+// lane of the calling wave (all 64 lanes must call it).
+__device__ __forceinline__ int value_exp(const KParams& p, int g)
+{
+    static_assert(VM_BLOCKS == 64, "one block maximum per lane");
+    const float x = wmax(p.vmax[(int64_t)g * VM_BLOCKS + (threadIdx.x & 63)]);
+    return __builtin_amdgcn_readfirstlane(value_exp_of(x));   // the same in every lane
 }
 
 }  // namespace swl

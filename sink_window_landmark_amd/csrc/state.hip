@@ -88,16 +88,19 @@ hipError_t launch_meta(const KParams& p, hipStream_t st)
     return hipGetLastError();
 }
 
-// The bookkeeping of one push undone, per group (dory.rs dory_o1_back): a
-// full window moves its head back one slot and gives back one far count;
-// otherwise the window is one row shorter.  The ring's rows and M, Z, Theta
-// stay as they are.  An empty window is left alone.
+// The bookkeeping of one push undone, per group (dory.rs dory_o1_back).  A
+// push that evicted left the window full with at least one far key: its
+// inverse moves the head back one slot and gives back one far count.  Any
+// other push (the one that filled the window included: it evicted nothing,
+// so the far count is still 0) only lengthened the window, which loses its
+// newest row.  The ring's rows and M, Z, Theta stay as they are.  An empty
+// window is left alone.
 __global__ void k_rewind(KParams p)
 {
     const int g = blockIdx.x * blockDim.x + threadIdx.x;
     if (g >= p.G) return;
     const GMeta c = load_gmeta(p.meta, g, p.W);
-    if (c.len0 == c.wg) {
+    if (c.len0 == c.wg && c.nfar0 > 0) {
         p.meta[4 * g + 1] = (uint32_t)((c.head0 + c.wg - 1) % c.wg);
         p.meta[4 * g + 2] = (uint32_t)(c.nfar0 - 1);
     } else if (c.len0 > 0) {

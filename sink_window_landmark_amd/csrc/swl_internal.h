@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "../../include/swl.h"
@@ -11,6 +12,7 @@ namespace swl {
 
 constexpr int SUB = SWL_SUB;           // rows of a sub-chunk
 constexpr int PASS_SUBS = 512;         // sub-chunks per prefill pass (32768 rows)
+constexpr int VM_BLOCKS = 64;          // blocks per group of the value-range pass (one wave's lanes)
 
 // Everything a kernel of one call (or one prefill pass) needs, passed by value.
 struct KParams {
@@ -46,6 +48,7 @@ struct KParams {
     int64_t theta_prev_stride;
     float* apart;             // split-window attention partials (attend_part_floats())
     int nsp;                  // splits of the window per attention work item (set by launch_attend)
+    float* vmax;              // [G][VM_BLOCKS] largest |value| seen by each block of k_vmax
     unsigned short* kvs;      // [G][kv_tiles] fp16 key tiles of the pass (k_kv_split)
     int kv_tiles;             // tiles per group: the sinks, then the aligned window tiles
     // fused ingest and output steps (null: off)
@@ -146,8 +149,24 @@ __device__ __forceinline__ int xcd_work_item(int b, int n)
     return x * q + (x < r ? x : r) + k;
 }
 
+// The power-of-two scale of a group's values in a pass: with vmax the
+// largest |value| among the pass's sinks, call-start window and rows, the
+// values times 2^e have magnitudes below 2^14, so that both fp16 halves of
+// their splits are normal numbers far inside fp16 range whatever the values'
+// own scale (exact: a power of two; undone on the products' results).  0
+// for no values, or when the largest is not finite (the results are then
+// not finite either, as they would be without the scale).
+__host__ __device__ inline int value_exp_of(float vmax)
+{
+    if (!(vmax > 0.f) || !(vmax <= 3.4028235e38f)) return 0;
+    int ex;
+    frexpf(vmax, &ex);   // vmax = f 2^ex, 0.5 <= f < 1
+    return 14 - ex;
+}
+
 // Launchers (each returns the launch's hipGetLastError).
 hipError_t launch_init(const KParams& p, const uint32_t* windows, hipStream_t st);
+hipError_t launch_vmax(const KParams& p, hipStream_t st);
 hipError_t launch_far_score(const KParams& p, hipStream_t st);
 hipError_t launch_far_scan(const KParams& p, hipStream_t st);
 hipError_t launch_dtheta(const KParams& p, hipStream_t st);

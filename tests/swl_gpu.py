@@ -54,22 +54,26 @@ def excess(got, want, atol=ATOL, rtol=RTOL, scale=None):
     return float(np.max(d - (atol + rtol * ref))) if d.size else -1.0
 
 
-def check_out(got, want, what="out"):
+def check_out(got, want, what="out", atol=ATOL):
+    """Elementwise |got - want| <= atol + RTOL |want| (atol scales with the
+    values' scale when a test scales the values: the output is linear in
+    them)."""
     got = np.asarray(got)
     assert np.all(np.isfinite(got)), f"{what}: non-finite values"
-    e = excess(got, want)
+    e = excess(got, want, atol=atol)
     md = float(np.max(np.abs(got.astype(np.float64) - want))) if got.size else 0.0
     print(f"  {what}: max|d| {md:.3e}  excess {e:.3e}", flush=True)
     if e > 0:
         w = np.asarray(want, np.float64)
-        at = np.unravel_index(np.argmax(np.abs(got - w) - (ATOL + RTOL * np.abs(w))), w.shape)
+        at = np.unravel_index(np.argmax(np.abs(got - w) - (atol + RTOL * np.abs(w))), w.shape)
         raise AssertionError(f"{what}: beyond tolerance by {e:.3e} (max|d| {md:.3e}); worst at "
                              f"{tuple(int(i) for i in at)}: got {float(got[at]):.8g}, "
                              f"want {float(w[at]):.8g}, max|want| {float(np.max(np.abs(w))):.4g}")
 
 
-def check_state(gpu, orc, ring=True):
-    """GPU state (read_state) against a SerialOracle's state."""
+def check_state(gpu, orc, ring=True, vscale=1.0):
+    """GPU state (read_state) against a SerialOracle's state.  vscale: the
+    values' scale, by which Theta's absolute bound scales."""
     np.testing.assert_array_equal(gpu["meta"][:, :3], orc.meta()[:, :3])
     if ring:
         rk, rv = orc.ring()
@@ -84,10 +88,25 @@ def check_state(gpu, orc, ring=True):
     eM = excess(M, orc.M)
     eZ = excess(Z, orc.Z)
     sc = np.max(np.abs(orc.theta), axis=2, keepdims=True)
-    eT = excess(gpu["theta"], orc.theta, scale=sc)
-    mt = float(np.max(np.abs(gpu["theta"] - orc.theta)))
-    print(f"  state: M excess {eM:.3e}  Z excess {eZ:.3e}  Theta max|d| {mt:.3e} excess {eT:.3e}",
-          flush=True)
+    eT = excess(gpu["theta"], orc.theta, atol=ATOL * vscale, scale=sc)
+    th = np.asarray(gpu["theta"], np.float64)
+    dT = np.abs(th - orc.theta)
+    mt = float(np.max(dT)) if dT.size else 0.0
+    # elementwise reading, reported beside the accumulator-scale one: the
+    # excess, how many elements exceed, and how far the worst one has
+    # cancelled (|Theta| of that element against its landmark's largest)
+    lim = ATOL * vscale + RTOL * np.abs(orc.theta)
+    over = dT - lim
+    eTe = float(np.max(over)) if over.size else -1.0
+    nbad = int(np.sum(over > 0))
+    if over.size:
+        at = np.unravel_index(np.argmax(over), over.shape)
+        canc = float(abs(orc.theta[at]) / max(float(sc[at[0], at[1], 0]), 1e-300))
+    else:
+        canc = 1.0
+    print(f"  state: M excess {eM:.3e}  Z excess {eZ:.3e}  Theta max|d| {mt:.3e} "
+          f"excess {eT:.3e} (accumulator scale)  elementwise excess {eTe:.3e} "
+          f"({nbad} of {over.size} over; worst |Theta|/scale {canc:.2e})", flush=True)
     assert eM <= 0 and eZ <= 0 and eT <= 0
 
 

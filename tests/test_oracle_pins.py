@@ -255,6 +255,27 @@ def test_rewind_undoes_the_last_push(wg, len0, head0, T):
     assert o2.meta()[0, :3].tolist() == [0, 0, 0]
 
 
+@pytest.mark.parametrize("wg,N", [(8, 7), (8, 8), (8, 9), (8, 30), (5, 17), (1, 4)])
+def test_rewinds_walk_back_through_every_push(wg, N):
+    """From the empty state, N single pushes then N rewinds: rewind i
+    restores exactly the meta that stood before push N - i, through the
+    push that filled the window (it evicted nothing, so its rewind must
+    shorten the window and leave head and the far count alone) and every
+    evicting push after it.  The metas walked back to are the oracle's own
+    after each push, which the closed-form pin above fixes."""
+    cfg = _cfg(G=1, W=wg, rows=N, m=2)
+    orc = oracle.from_config(cfg, synth.make_state(cfg))
+    q, k, v = _rand_rows(cfg, N, seed=11)
+    seen = [orc.meta()[0, :3].tolist()]
+    for r in range(N):
+        orc.step(q[r:r + 1], k[r:r + 1], v[r:r + 1], want=np.zeros(1, bool))
+        seen.append(orc.meta()[0, :3].tolist())
+    for i in range(N):
+        orc.rewind()
+        assert orc.meta()[0, :3].tolist() == seen[N - 1 - i], f"rewind {i + 1} of {N}"
+    assert seen[0] == [0, 0, 0]
+
+
 # -- rect and the negative-mass guard ----------------------------------------------
 
 def test_rect_clamps_negative_far_weights():
