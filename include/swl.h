@@ -59,6 +59,10 @@ extern "C" {
 #define SWL_OK 0
 #define SWL_EINVAL 1
 #define SWL_EHIP 2
+#define SWL_ESIZE 3   /* swl_attend_token_noalloc: the geometry needs more scratch than it holds */
+
+/* Bytes of the library's static scratch (swl_attend_token_noalloc). */
+#define SWL_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
 
 /* Rows of one sub-chunk (the pages' OB_K): a chunk longer than this is
  * processed as consecutive sub-chunks of this many rows. */
@@ -254,6 +258,24 @@ int swl_attend_token_fused(const swl_geom* geom, const swl_state* st,
                            const float* q, const float* k, const float* v,
                            const swl_fuse* fuse, float* out, void* scratch,
                            size_t scratch_bytes, void* stream);
+
+/* swl_attend_token_fused for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same kernels and results as swl_attend_token_fused (fuse
+ * may be NULL: then swl_attend_token), but no scratch argument: the
+ * decode partials go to a static device array of SWL_NOALLOC_SCRATCH_BYTES
+ * bytes inside the library, one per GPU, which the first call on a GPU
+ * looks up (hipGetSymbolAddress) and which stays allocated until the process
+ * ends.  The call allocates nothing itself (no hipMalloc, no library routine
+ * that allocates).  Geometries whose partials need more than that
+ * (4 * ((G * ceil((ns + W) / 64) + 4 * G) * H * (dv + 4)) bytes) return
+ * SWL_ESIZE before anything is enqueued.  Every call on one GPU shares that
+ * GPU's array and each call overwrites what it reads, so calls that may
+ * overlap on one GPU (other streams, other threads) race: order them on
+ * one stream.  q, k, v, out and the state as in swl_attend_token. */
+int swl_attend_token_noalloc(const swl_geom* geom, const swl_state* st,
+                             const float* q, const float* k, const float* v,
+                             const swl_fuse* fuse, float* out, void* stream);
 
 /* A static description of a status code. */
 const char* swl_status_str(int status);

@@ -20,14 +20,16 @@ from typing import Optional, Sequence
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libswl.so")
 
-SWL_OK, SWL_EINVAL, SWL_EHIP = 0, 1, 2
+SWL_OK, SWL_EINVAL, SWL_EHIP, SWL_ESIZE = 0, 1, 2, 3
 SUB = 64
+NOALLOC_SCRATCH_BYTES = 4 << 20   # SWL_NOALLOC_SCRATCH_BYTES
 
 # Entry points declared by include/swl.h.
 EXPORTS = ("swl_scratch_bytes", "swl_init_state", "swl_attend_chunk", "swl_commit",
            "swl_prefill", "swl_prefill_traced", "swl_commit_rows", "swl_seal", "swl_rewind",
            "swl_attend_token", "swl_status_str", "swl_prefill_fused", "swl_attend_chunk_fused",
-           "swl_commit_fused", "swl_commit_rows_fused", "swl_attend_token_fused")
+           "swl_commit_fused", "swl_commit_rows_fused", "swl_attend_token_fused",
+           "swl_attend_token_noalloc")
 
 # Stage ids of swl_stage_fn (enum swl_stage).
 STAGES = ("far_score", "far_scan", "dtheta", "theta_scan", "attend", "ring", "meta", "kv_split",
@@ -104,6 +106,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.swl_commit_rows_fused.argtypes = [G, S, _P, _P, ctypes.c_int64, F, _P, ctypes.c_size_t, _P]
     lib.swl_attend_token_fused.restype = ctypes.c_int
     lib.swl_attend_token_fused.argtypes = [G, S, _P, _P, _P, F, _P, _P, ctypes.c_size_t, _P]
+    lib.swl_attend_token_noalloc.restype = ctypes.c_int
+    lib.swl_attend_token_noalloc.argtypes = [G, S, _P, _P, _P, F, _P, _P]
     lib.swl_status_str.restype = ctypes.c_char_p
     lib.swl_status_str.argtypes = [ctypes.c_int]
     _lib = lib
@@ -417,6 +421,21 @@ def swl_attend_token_fused(state: LayerState, q, k, v, out, scratch, rope=None, 
         v.data_ptr(), ctypes.byref(f), out.data_ptr(), scratch.data_ptr(), scratch.numel(),
         _stream(stream))
     _raise(rc, "swl_attend_token_fused")
+
+
+def swl_attend_token_noalloc(state: LayerState, q, k, v, out, rope=None, gate=None,
+                             gate_scale=None, stream=None):
+    """swl_attend_token(_fused) without a scratch argument: the library's
+    static per-GPU scratch holds the partials (for callers that cannot
+    allocate).  Calls that overlap on one GPU race."""
+    _rows_args(state, q, k, v, out, 1)
+    fz = rope is not None or gate is not None or gate_scale is not None
+    f = _fuse_arg(state, 1, rope, gate, gate_scale) if fz else None
+    rc = load_library().swl_attend_token_noalloc(
+        ctypes.byref(state.geom.c()), ctypes.byref(state.c()), q.data_ptr(), k.data_ptr(),
+        v.data_ptr(), ctypes.byref(f) if f is not None else None, out.data_ptr(),
+        _stream(stream))
+    _raise(rc, "swl_attend_token_noalloc")
 
 
 # Short aliases.

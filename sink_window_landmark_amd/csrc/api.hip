@@ -8,9 +8,49 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "swl_internal.h"
 
 namespace swl {
+
+// Scratch of swl_attend_token_noalloc: file-scope device memory of a fixed
+// size.  Every GPU the library runs on holds its own copy, at its own
+// address, until the process ends.  In host code the array's name is only a
+// stand-in for the symbol: its device address comes from
+// hipGetSymbolAddress, once per device (noalloc_scratch below), and only
+// that address is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[SWL_NOALLOC_SCRATCH_BYTES];
+
+constexpr int NOALLOC_MAX_DEV = 64;
+static std::mutex noalloc_mu;
+static void* noalloc_addr[NOALLOC_MAX_DEV];
+
+// This stream's GPU's copy of `scratch` (NULL stream: the current GPU), its
+// address taken with that GPU current on the first call there; null on a
+// HIP error.
+static void* noalloc_scratch(hipStream_t stream)
+{
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    int dev = cur;
+    if (stream) {
+        hipDevice_t d;
+        if (hipStreamGetDevice(stream, &d) != hipSuccess) return nullptr;
+        dev = (int)d;
+    }
+    if (dev < 0 || dev >= NOALLOC_MAX_DEV) return nullptr;
+    std::lock_guard<std::mutex> lock(noalloc_mu);
+    if (!noalloc_addr[dev]) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) return nullptr;
+        void* addr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+        if (dev != cur && hipSetDevice(cur) != hipSuccess) return nullptr;
+        if (e != hipSuccess || !addr) return nullptr;
+        noalloc_addr[dev] = addr;
+    }
+    return noalloc_addr[dev];
+}
 
 static bool geom_ok(const swl_geom* g)
 {
@@ -352,12 +392,32 @@ int swl_attend_token(const swl_geom* geom, const swl_state* st, const float* q, 
     return swl_attend_token_fused(geom, st, q, k, v, nullptr, out, scratch, scratch_bytes, stream);
 }
 
+int swl_attend_token_noalloc(const swl_geom* geom, const swl_state* st, const float* q,
+                             const float* k, const float* v, const swl_fuse* fuse, float* out,
+                             void* stream)
+{
+    if (!geom_ok(geom) || !state_ok(geom, st) || !fuse_ok(fuse)) return SWL_EINVAL;
+    if (!q || !k || !v || !out) return SWL_EINVAL;
+    const size_t need = sizeof(float) * tok_part_floats(geom->G, geom->H, geom->dv, geom->ns, geom->W);
+    if (need > SWL_NOALLOC_SCRATCH_BYTES) return SWL_ESIZE;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    void* part = noalloc_scratch(hs);
+    if (!part) return SWL_EHIP;
+    KParams p = make_params(geom, st);
+    p.q = q; p.k = k; p.v = v; p.out = out;
+    p.T = 1; p.S = 1;
+    set_fuse(p, fuse, 0);
+    SWL_TRY(launch_token(p, static_cast<float*>(part), hs));
+    return SWL_OK;
+}
+
 const char* swl_status_str(int status)
 {
     switch (status) {
     case SWL_OK: return "ok";
     case SWL_EINVAL: return "invalid argument";
     case SWL_EHIP: return "HIP launch failed";
+    case SWL_ESIZE: return "the geometry needs more than the static scratch (SWL_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
     }
 }

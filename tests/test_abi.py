@@ -74,6 +74,30 @@ def test_status_strings():
     assert lib.swl_status_str(0) == b"ok"
     assert lib.swl_status_str(1) == b"invalid argument"
     assert lib.swl_status_str(2) == b"HIP launch failed"
+    assert b"static scratch" in lib.swl_status_str(3)
+
+
+@needs_no_gpu
+def test_noalloc_token_rejects_oversized_geometry_and_null_pointers():
+    """The allocation-free token call refuses, before any HIP call, a geometry
+    whose decode partials outgrow its static scratch (SWL_ESIZE), and null
+    pointers (SWL_EINVAL)."""
+    lib = swl.load_library()
+    st = _fake_state()
+    big = swl.Geom(G=64, H=16, m=8, W=65536, ns=4, d=128, dv=128).c()
+    rc = lib.swl_attend_token_noalloc(ctypes.byref(big), ctypes.byref(st), FAKE, FAKE, FAKE, None,
+                                      FAKE, None)
+    assert rc == swl.SWL_ESIZE
+    g = _geom().c()
+    for args in ((None, FAKE, FAKE, FAKE), (FAKE, None, FAKE, FAKE), (FAKE, FAKE, None, FAKE),
+                 (FAKE, FAKE, FAKE, None)):
+        q, k, v, out = args
+        rc = lib.swl_attend_token_noalloc(ctypes.byref(g), ctypes.byref(st), q, k, v, None, out,
+                                          None)
+        assert rc == swl.SWL_EINVAL
+    rc = lib.swl_attend_token_noalloc(ctypes.byref(g), ctypes.byref(_fake_state(theta=True)),
+                                      FAKE, FAKE, FAKE, None, FAKE, None)
+    assert rc == swl.SWL_EINVAL
 
 
 FAKE = 0x10000
