@@ -18,7 +18,20 @@
  * query head gh = g*H + h), m landmarks, W ring stride (the widest group
  * window), ns sinks, d key width, dv value width, scale (usually 1/sqrt(d)),
  * rect (1: clamp u_b at 0).  Supported: d == dv in {8, 16, 32, 64, 128, 256},
- * 1 <= m <= 64, 1 <= H <= 16, 1 <= G <= 64, 0 <= ns <= 256, 1 <= W <= 65536.
+ * 1 <= m <= 64, 1 <= H <= 16, 1 <= G <= 64, 0 <= ns <= 256, 1 <= W <= 65536;
+ * anything else is SWL_EINVAL.  (The pages admit their batch kernels only
+ * for w >= 64, ns <= 255, ns + w <= 2052 and m <= 32 -- o1_batch.rs
+ * min_window, o1c.rs admits, dory.rs forward -- capacities of their
+ * fixed-size workgroup arrays; these kernels stream keys through LDS tiles
+ * and have no such arrays.)
+ *
+ * Input range.  The prefill path multiplies on fp16 matrix cores with
+ * fp32-accurate hi/lo splits of its operands, so keys, landmark keys,
+ * landmark queries and scale * log2(e) * q must have magnitudes of at most
+ * 65504 (fp16's largest value); beyond that the split rounds to infinity
+ * and the outputs are inf or NaN (inputs are not scanned for it).  Values
+ * may have any finite magnitude: each pass scales them by a power of two
+ * before their split.  The decode path computes in fp32 throughout.
  *
  * Device arrays (swl_state; all row-major, fp32 unless noted):
  *   meta    u32 [G][4]   len, head, nfar, window override (0 = W)
@@ -125,7 +138,10 @@ int swl_commit(const swl_geom* geom, const swl_state* st,
 /* attend + commit over any number of rows (rows >= 0; 0 is a no-op), as
  * consecutive 64-row sub-chunks with each sub-chunk's semantics (its own
  * post-sub-chunk far max): the same result as looping swl_attend_chunk +
- * swl_commit, up to rounding.  Sub-chunks are batched into few launches. */
+ * swl_commit, up to rounding (o1_batch.rs encode, whose loop runs the
+ * chunk kernels over sub-chunks of OB_K rows).  Sub-chunks are batched
+ * into few launches: passes of up to 32768 rows.  q, k, v and out hold the
+ * rows in order; scratch: swl_scratch_bytes(geom, rows) bytes. */
 int swl_prefill(const swl_geom* geom, const swl_state* st,
                 const float* q, const float* k, const float* v, int64_t rows,
                 float* out, void* scratch, size_t scratch_bytes, void* stream);
