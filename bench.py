@@ -103,25 +103,43 @@ def attend_bytes(cfg, T, len0=0):
     return 4 * f
 
 
-def attend_counters(launch_bytes):
-    """HBM traffic of one attend launch from the committed counter summary,
-    or None when the kernel's source has changed since it was taken."""
+def source_sha256():
+    """sha256 over every source of the HIP library (csrc/*.hip, *.h and the
+    C ABI header), in name order: a profile summary taken on other sources
+    does not describe the kernels that run."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "attend_maxwin_counters.md")
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sink_window_landmark_amd", "csrc")
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith((".hip", ".h")))
+    files.append(os.path.join(ROOT, "include", "swl.h"))
+    for f in files:
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def profile_values(name):
+    """The `key = value` lines of a committed profile summary, or None when
+    it is missing or was taken on other library sources."""
     try:
-        text = open(path).read()
+        text = open(os.path.join(ROOT, "profiles", name)).read()
     except OSError:
         return None
     kv = {}
     for line in text.splitlines():
-        if " = " in line:
+        if " = " in line and not line.startswith(("    ", "|")):
             k, v = line.split(" = ", 1)
-            kv[k.strip()] = v.strip()
-    h = hashlib.sha256()
-    for f in ("attend.hip", "swl_internal.h"):
-        with open(os.path.join(ROOT, "sink_window_landmark_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    if kv.get("source_sha256") != h.hexdigest():
+            kv[k.strip().strip("`")] = v.strip().strip("`")
+    if kv.get("source_sha256") != source_sha256():
+        return None
+    return kv
+
+
+def attend_counters(launch_bytes):
+    """HBM traffic of one attend launch from the committed counter summary,
+    or None when the library's sources have changed since it was taken."""
+    kv = profile_values("attend_maxwin_counters.md")
+    if kv is None:
         return None
     read = float(kv["fetch_kib_per_launch"]) * float(kv["fetch_factor"]) * 1024
     write = float(kv["write_kib_per_launch"]) * float(kv["write_factor"]) * 1024
@@ -273,6 +291,9 @@ def run_gpu(args, cfg):
                              f"{seg}-token segments", us_per_token_host_loop=us_host,
                              bytes_per_token=db, achieved_gbs=db / (us * 1e-6) / 1e9,
                              frac_hbm=db / (us * 1e-6) / 1e9 / HBM_PEAK_GBS)
+        if args.cold_states > 0:
+            res["decode"]["cold"] = decode_cold(args, cfg, st, views[:seg], tscr, db)
+        res["decode"]["launch_floor_us"] = launch_floor_us()
 
     # the fused ingest and output steps: the same prompt through
     # swl_prefill_fused with q, k taken before RoPE (a cos/sin table row per
@@ -326,6 +347,63 @@ def run_gpu(args, cfg):
     return res
 
 
+def decode_cold(args, cfg, st, views, tscr, db):
+    """us/token with the state out of every cache: token i of a captured
+    segment runs on state copy i mod N (N byte copies of the prefilled
+    state, every array its own), so that the other N - 1 states' ~10 MB
+    each pass through the caches between two visits to one state (N = 32:
+    ~330 MB, above the 256 MB Infinity Cache)."""
+    import torch
+    import sink_window_landmark_amd as swl
+    n = args.cold_states
+    states = [st.clone() for _ in range(n)]
+    state_bytes = sum(getattr(st, f).numel() * 4 for f in swl.LayerState.FIELDS)
+    seg = len(views)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gs = torch.cuda.current_stream().cuda_stream
+        for i in range(seg):
+            swl.swl_attend_token(states[i % n], *views[i], tscr, stream=gs)
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = 8
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / (reps * seg)
+    del graph, states
+    torch.cuda.empty_cache()
+    return dict(us_per_token=us, states=n, bytes_rotated=n * state_bytes,
+                achieved_gbs=db / (us * 1e-6) / 1e9, frac_hbm=db / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                timing=f"HIP graph replay of {seg}-token segments, token i on state copy i mod {n}")
+
+
+def launch_floor_us():
+    """The time of two dependent launches of a trivial kernel (a one-element
+    add), per pair, under HIP-graph replay: the floor of any two-launch
+    token path on this GPU and runtime."""
+    import torch
+    x = torch.zeros(1, device="cuda")
+    seg = 256
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(seg):
+            x.add_(1.0)
+            x.add_(1.0)
+    graph.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(8):
+        graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (8 * seg)
+
+
 def exact_attention(cfg, host, q, k, v):
     """Exact fp32 causal softmax attention over sinks + every key, same heads,
     blockwise torch.matmul (for the "faster than exact" comparison only)."""
@@ -365,33 +443,71 @@ def exact_attention(cfg, host, q, k, v):
                 rows=T)
 
 
-def cpu_baseline(cfg, budget_s):
-    """The oracle (float64 serial steps, threads = min(G*H, cores)) on the
-    max-window layer: the ring is filled (2048 rows, no outputs), then rows
-    with outputs are stepped in 256-row batches until ~budget_s has passed."""
+def _oracle_rate(cfg, fill, batch, budget_s, threads):
+    """Rows/s of the oracle on `cfg` after `fill` rows stepped without
+    outputs: rows with outputs in batches of `batch` until ~budget_s."""
     import oracle
     import synth
-    cores = min(cfg.nh, os.cpu_count() or 1, 16)
     host = synth.make_state(cfg)
-    orc = oracle.from_config(cfg, host, threads=cores)
-    fill = max(cfg.window(g) for g in range(cfg.G))
-    q, k, v = synth.rows(cfg, 0, fill)
-    orc.step(q, k, v, want=np.zeros(fill, bool))
+    orc = oracle.from_config(cfg, host, threads=threads)
+    if fill:
+        q, k, v = synth.rows(cfg, 0, fill)
+        orc.step(q, k, v, want=np.zeros(fill, bool))
     done, r0 = 0, fill
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
-        q, k, v = synth.rows(cfg, r0, r0 + 256)
+    el = 0.0
+    while el < budget_s:
+        q, k, v = synth.rows(cfg, r0, r0 + batch)
         ts = time.perf_counter()
         orc.step(q, k, v)
-        done += 256
-        r0 += 256
-        if time.perf_counter() - t0 > 3 * budget_s:
-            break
-        _ = ts
-    el = time.perf_counter() - t0
-    return dict(value=done / el, unit="rows/s", cores=cores, kind="oracle",
+        el += time.perf_counter() - ts
+        done += batch
+        r0 += batch
+    return done / el, done, el, orc.threads
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, budget_s):
+    """The oracle (float64 serial steps, threads = min(G*H, cores, 16)) on
+    the max-window layer: the ring is filled (2048 rows, no outputs), then
+    rows with outputs are stepped in 256-row batches for ~budget_s (timed:
+    the stepping only).  Beside it, bounded samples of the other workloads:
+    the tiny layer's 64-row chunk and the small layer at a full window,
+    each also on one thread, and the mixed-window layer once every window
+    is full; a decode token is one serial row step at the max-window layer's
+    full window, so its us/token is the inverse of the main rate."""
+    import synth
+    cores = min(cfg.nh, os.cpu_count() or 1, 16)
+    fill = max(cfg.window(g) for g in range(cfg.G))
+    rate, done, el, thr = _oracle_rate(cfg, fill, 256, budget_s, cores)
+    per = {}
+    for name, c, fl, batch, bud, single in (
+            ("tiny", synth.TINY, 0, 64, 1.0, True),
+            ("small", synth.SMALL, synth.SMALL.W, 256, 2.0, True),
+            ("mixed", synth.MIXED, synth.MIXED.W, 256, 3.0, False)):
+        r, n, e, t = _oracle_rate(c, fl, batch, bud, min(c.nh, cores))
+        per[name] = dict(rows_per_s=r, threads=t, rows=n, seconds=e,
+                         sample=f"rows {fl}..{fl + n}" + (" (full window)" if fl else
+                                                          " from its 10/16 ring, in 64-row chunks"))
+        if single:
+            r1, n1, e1, _ = _oracle_rate(c, fl, batch, bud, 1)
+            per[name]["rows_per_s_1_thread"] = r1
+    per["maxwin"] = dict(rows_per_s=rate, threads=thr)
+    per["decode"] = dict(us_per_token=1e6 / rate, threads=thr,
+                         sample="a token is one serial row step at the max-window layer's full "
+                                "window: the inverse of the max-window rate")
+    return dict(value=rate, unit="rows/s", cores=thr, kind="oracle",
                 sample=f"max-window layer rows {fill}..{fill + done} (full window, every row "
-                       f"evicting), after a {fill}-row fill; {el:.1f} s")
+                       f"evicting), after a {fill}-row fill; {el:.1f} s of stepping",
+                cpu_model=cpu_model(), host_cores=os.cpu_count(), per_config=per)
 
 
 def hbm_copy_gbs():
@@ -497,6 +613,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--decode-steps", type=int, default=4096)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cold-states", type=int, default=32,
+                    help="state copies the cold decode figure rotates over (0: skip it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-exact", dest="exact", action="store_false")
     ap.add_argument("--no-chunk-api", dest="chunk_api", action="store_false")
@@ -560,6 +678,16 @@ def main():
                  "frac_split_peak": res["step_tflops"] / MFMA_SPLIT_PEAK_TFLOPS,
                  "stages_ms": res["stages_ms_per_step"]},
     }
+    rf = line["roofline"]
+    rf["frac_dense_fp16"] = near["achieved_tflops"] / MFMA_FP16_PEAK_TFLOPS
+    kt = profile_values("prefill_maxwin_kernel_trace.md")
+    if kt is not None and "attend_avg_ns" in kt:
+        traced_ms = float(kt["attend_avg_ns"]) * 1e-6
+        ach = near["flops_per_launch"] / (traced_ms * 1e-3) / 1e12
+        rf["traced"] = dict(avg_launch_ms=traced_ms, achieved=ach, frac=ach / near["peak_tflops"],
+                            frac_dense_fp16=ach / MFMA_FP16_PEAK_TFLOPS,
+                            source="profiles/prefill_maxwin_kernel_trace.md (rocprofv3 kernel "
+                                   "trace of the same command)")
     tr = attend_counters(near["bytes_per_launch"])
     if tr is not None:
         line["roofline"]["traffic"] = tr["bytes"]

@@ -80,7 +80,7 @@ static bool state_ok(const swl_geom* g, const swl_state* st)
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Carve {
-    size_t tok, apart, vm, e, p, ms, rs, tz, th, kv, total;
+    size_t tok, apart, vm, e, ms, rs, tz, th, kv, total;
 };
 
 static Carve carve(const swl_geom* g, int S)
@@ -93,7 +93,6 @@ static Carve carve(const swl_geom* g, int S)
     c.apart = off; off += align256(sizeof(float) * attend_part_floats(g->d));
     c.vm = off; off += align256(sizeof(float) * (size_t)g->G * VM_BLOCKS);
     c.e = off;  off += align256(sizeof(float) * (size_t)S * nhm * SUB);
-    c.p = off;  off += align256(sizeof(float) * (size_t)S * g->G * g->H * SUB * 64);
     c.ms = off; off += align256(sizeof(float) * (size_t)S * nhm);
     c.rs = off; off += align256(sizeof(float) * (size_t)S * nhm);
     c.tz = off; off += align256(sizeof(float) * (size_t)(S + 1) * nhm);
@@ -129,7 +128,6 @@ static void set_scratch(KParams& p, const swl_geom* g, void* scratch, int S)
     Carve c = carve(g, S);
     char* b = static_cast<char*>(scratch);
     p.E = reinterpret_cast<float*>(b + c.e);
-    p.P = reinterpret_cast<float*>(b + c.p);
     p.Ms = reinterpret_cast<float*>(b + c.ms);
     p.Rs = reinterpret_cast<float*>(b + c.rs);
     p.TZ = reinterpret_cast<float*>(b + c.tz);

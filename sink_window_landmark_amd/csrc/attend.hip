@@ -10,10 +10,13 @@
 //   rect), c = max(c_near, max_b f_max + M'_b), gain_b = u_b e^{f_max+M'_b-c},
 //   D_far = sum_b gain_b P_bi, N_far = sum_b gain_b R_b Theta_b
 //   + sum_{j0<=j<=i} cf_j v_evicted(j) with cf_j = sum_b gain_b E_bj,
-//   both dropped when D_far is not >= 0;
+//   both dropped when D_far is not >= 0; P_bi = R_b Z_b + sum_{j<=i} E_bj
+//   is the far mass prefix, so D_far = sum_b gain_b R_b Z_b +
+//   sum_{j0<=j<=i} cf_j, which is how it is formed here;
 //   out = (N_far + sum p v) / max(D_far + sum p, 1e-30), p = e^{s-c}.
-// M', R, E, P (far_scan) and Theta before the sub-chunk (theta_scan, or the
-// state for a single sub-chunk) are ready before this kernel runs.
+// M', R, the incoming mass Z (far_scan), E (dtheta) and Theta before the
+// sub-chunk (theta_scan, or the state for a single sub-chunk) are ready
+// before this kernel runs.
 //
 // The near part never depends on the far field, so every sub-chunk of a call
 // is computed in one launch: one block per (sub-chunk, KV group, group of up
@@ -321,7 +324,7 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
     constexpr int LDF = D + 4;                // fp32 row stride of the epilogue's tiles
     constexpr int NEAR_BYTES = 2 * L::BYTES;
     constexpr int KTB = 2 * 2 * L::KH * 2;     // landmark keys as two fp16 hi/lo K tiles
-    constexpr int FAR_BYTES = KTB + 2 * KT * LDF * 4 + HPB * 2 * 64 * 4;
+    constexpr int FAR_BYTES = KTB + 2 * KT * LDF * 4 + HPB * 3 * 64 * 4;
     constexpr int SMEM = NEAR_BYTES > FAR_BYTES ? NEAR_BYTES : FAR_BYTES;
     constexpr float LOG2E = 1.4426950408889634f;
     __shared__ __align__(16) unsigned char smem[SMEM];
@@ -330,16 +333,18 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
     // hi/lo K tiles and the sub-chunk's evicted values (64 rows) in fp32
     unsigned short* const Kt = reinterpret_cast<unsigned short*>(smem);
     float(*const Vs)[LDF] = reinterpret_cast<float(*)[LDF]>(smem + KTB);
-    // and the post-sub-chunk max M' and rescale R of each head's landmarks
-    float(*const MR)[2][64] = reinterpret_cast<float(*)[2][64]>(smem + KTB + 2 * KT * LDF * 4);
+    // and the post-sub-chunk max M', rescale R and incoming mass Z of each
+    // head's landmarks
+    float(*const MR)[3][64] = reinterpret_cast<float(*)[3][64]>(smem + KTB + 2 * KT * LDF * 4);
 
-    // work item = (head group, group, sub-chunk), sub-chunk fastest, dealt
-    // to XCDs in contiguous runs
+    // work item = (sub-chunk, group, head group), dealt to XCDs as ranges of
+    // sub-chunks (range_item)
     const int hgroups = (p.H + HPB - 1) / HPB;
     const int nsp = MODE == AT_PART ? p.nsp : 1;
-    const int wx = xcd_work_item(blockIdx.x, p.S * p.G * hgroups * nsp);
-    const int sp = wx % nsp, w = wx / nsp;   // split, and the (sub-chunk, group, head group) item
-    const int s = w % p.S, g = (w / p.S) % p.G, hgrp = w / (p.S * p.G);
+    int s, gi, sp;
+    range_item(xcd_work_item(blockIdx.x, p.S * p.G * hgroups * nsp), p.S, p.G * hgroups, nsp, s, gi, sp);
+    const int g = gi % p.G, hgrp = gi / p.G;
+    const int w = s + p.S * gi;   // the (sub-chunk, group, head group) item
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int hf = lane >> 5, ln = lane & 31;
     const int h = hgrp * HPB + (wave >> 1);
@@ -628,10 +633,10 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
             *reinterpret_cast<u32x2*>(t) = u32x2{s0.hi, s1.hi};
             *reinterpret_cast<u32x2*>(t + L::KH) = u32x2{s0.lo, s1.lo};
         }
-        for (int e = tid; e < HPB * 2 * 64; e += AT_THREADS) {
-            const int hh = e >> 7, which = (e >> 6) & 1, b = e & 63;
+        for (int e = tid; e < HPB * 3 * 64; e += AT_THREADS) {
+            const int hh = e / 192, which = (e / 64) % 3, b = e & 63;
             const int ghh = g * p.H + min(hgrp * HPB + hh, p.H - 1);
-            const float* src = which ? p.Rs : p.Ms;
+            const float* src = which == 0 ? p.Ms : which == 1 ? p.Rs : p.TZ;
             MR[hh][which][b] = src[((int64_t)s * p.nh + ghh) * m + min(b, m - 1)];
         }
         __syncthreads();
@@ -643,8 +648,8 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
             const int64_t ghb0 = (int64_t)s * nhm + (int64_t)gh * m;   // (s, gh, b = 0)
             const float* Ms = MR[wave >> 1][0];   // (b < 64: entries past m are not used)
             const float* Rs = MR[wave >> 1][1];
-            const float* Eb = p.E + ghb0 * SUB;                         // [b][j]
-            const float* Pt = p.P + (((int64_t)s * p.nh + gh) * SUB + i) * 64 + hf * 4;   // [b] of row i
+            const float* Zs = MR[wave >> 1][2];
+            const float* Eb = p.E + ghb0 * SUB;   // [b][j] exp(l - M'), 0 where row j evicts nothing
             const float* Th = p.theta_prev + (int64_t)s * p.theta_prev_stride + (int64_t)gh * m * D;
 
             // f^T = K~ Q^T (log2 units) from the near part's Q^T halves, three
@@ -714,31 +719,21 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
                 }
             mmax = pair_max<5>(mmax);
             const float cexp = lane_far ? fmaxf(mrun, fmax + mmax) : mrun;
+            // gains, and the part of the far mass the sub-chunk starts from:
+            // sum_b gain_b R_b Z_b (the mass of the rows it evicts is the sum
+            // of the in-chunk coefficients below)
             float dfar = 0.f;
 #pragma unroll
             for (int bt = 0; bt < MT; ++bt)
 #pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    // landmarks kappa(4a .. 4a+3, hf) = 32 bt + 8a + 4hf .. +3
-                    const float4 pq = *reinterpret_cast<const float4*>(Pt + bt * 32 + 8 * a);
-                    const float pb[4] = {pq.x, pq.y, pq.z, pq.w};
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int v = 4 * a + r, b = bt * 32 + kap(v, hf);
-                        float u = gn[bt][v];
-                        if (p.rect) u = fmaxf(u, 0.f);
-                        const float gain = lane_far & (b < m) ? u * ex2(fmax + mb[bt][v] - cexp) : 0.f;
-                        gn[bt][v] = gain;
-                        dfar += lane_far & (b < m) ? gain * pb[r] : 0.f;
-                    }
+                for (int v = 0; v < 16; ++v) {
+                    const int b = bt * 32 + kap(v, hf);
+                    float u = gn[bt][v];
+                    if (p.rect) u = fmaxf(u, 0.f);
+                    const float gain = lane_far & (b < m) ? u * ex2(fmax + mb[bt][v] - cexp) : 0.f;
+                    gn[bt][v] = gain;
+                    dfar += lane_far & (b < m) ? gain * (Rs[b] * Zs[b]) : 0.f;
                 }
-            dfar = pair_sum<5>(dfar);
-            const bool have = lane_far && dfar >= 0.f;
-            if (!have) {
-                dfar = 0.f;
-#pragma unroll
-                for (int bt = 0; bt < MT; ++bt) zero16(gn[bt]);
-            }
             // in-chunk coefficients cf^T = E^T g^T over rows j0 <= j <= i
             floatx16 cf[2];
 #pragma unroll
@@ -760,7 +755,17 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
                 for (int v = 0; v < 16; ++v) {
                     const int jj = jt * 32 + kap(v, hf);
                     if (jj < jlo || jj > i) cf[jt][v] = 0.f;
+                    dfar += cf[jt][v];
                 }
+            }
+            dfar = pair_sum<5>(dfar);
+            const bool have = lane_far && dfar >= 0.f;
+            if (!have) {
+                dfar = 0.f;
+#pragma unroll
+                for (int bt = 0; bt < MT; ++bt) zero16(gn[bt]);
+#pragma unroll
+                for (int jt = 0; jt < 2; ++jt) zero16(cf[jt]);
             }
             // near part to the common exponent, then the far numerator
             // the near weights carry 2^P_EXP, the value sums also 2^vexp

@@ -11,8 +11,8 @@
 //   M'_s = max(M_{s-1}, max_j l_j);  R_s = 1 if M'_s == M_{s-1} else
 //   exp(M_{s-1} - M'_s) (an empty field at -inf keeps R = 1 until its first
 //   eviction, which then rescales the zero mass by exp(-inf) = 0);
-//   E_sj = exp(l_j - M'_s);  P_sj = R_s Z_{s-1} + sum_{j'<=j} E_sj';
-//   Z_s = P_s,63;  Theta_s = R_s Theta_{s-1} + sum_j E_sj v_evicted(j).
+//   E_sj = exp(l_j - M'_s);  Z_s = R_s Z_{s-1} + sum_j E_sj;
+//   Theta_s = R_s Theta_{s-1} + sum_j E_sj v_evicted(j).
 #include "swl_internal.h"
 #include "lanes.h"
 
@@ -83,14 +83,24 @@ __global__ __launch_bounds__(256) void k_vmax(KParams p)
     const GMeta c = load_gmeta(p.meta, g, p.W);
     const int n = p.ns + c.len0 + p.T;
     const int li = threadIdx.x % LPR, rb = threadIdx.x / LPR;
+    constexpr int U = 8;   // rows whose loads are in flight together
     float mx = 0.f;
-    for (int r = b * RPB + rb; r < n; r += VM_BLOCKS * RPB) {
-        const float* row = r < p.ns ? p.sink_v + ((int64_t)g * p.ns + r) * DV : val_row(p, c, g, r - p.ns);
+    for (int r0 = b * RPB + rb; r0 < n; r0 += U * VM_BLOCKS * RPB) {
+        float4 x[U][DV / (4 * LPR)];
 #pragma unroll
-        for (int c4 = 4 * li; c4 < DV; c4 += 4 * LPR) {
-            const float4 x = *reinterpret_cast<const float4*>(row + c4);
-            mx = fmaxf(mx, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
+        for (int u = 0; u < U; ++u) {
+            const int r = min(r0 + u * VM_BLOCKS * RPB, n - 1);   // clamped: rows past n repeat row n-1
+            const float* row = r < p.ns ? p.sink_v + ((int64_t)g * p.ns + r) * DV : val_row(p, c, g, r - p.ns);
+#pragma unroll
+            for (int k = 0; k < DV / (4 * LPR); ++k)
+                x[u][k] = *reinterpret_cast<const float4*>(row + 4 * li + 4 * LPR * k);
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int k = 0; k < DV / (4 * LPR); ++k)
+                mx = fmaxf(mx, fmaxf(fmaxf(fabsf(x[u][k].x), fabsf(x[u][k].y)),
+                                     fmaxf(fabsf(x[u][k].z), fabsf(x[u][k].w))));
     }
     mx = wmax(mx);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
@@ -309,8 +319,8 @@ __global__ __launch_bounds__(fs_threads<D>()) void k_far_score(KParams p)
 // ---------------------------------------------------------------------------
 // mz_scan: one thread per landmark row (gh, b), walking the sub-chunks in
 // order on scalars: M'_s, R_s and the incoming mass Z_{s-1} (into TZ[s]),
-// with Z_s = R_s Z_{s-1} + zl_s exp(mx_s - M'_s) (the same sum as
-// P_{s,63}, up to rounding), and the final mass into TZ[S].  Reads the local
+// with Z_s = R_s Z_{s-1} + zl_s exp(mx_s - M'_s) (the sub-chunk's mass
+// sum_j E_sj, up to rounding), and the final mass into TZ[S].  Reads the local
 // (mx, zl) that far_score left in Ms/Rs and replaces them with M'_s and R_s.
 // ---------------------------------------------------------------------------
 constexpr int SCAN_AHEAD = 32;  // theta_scan's prefetch depth
@@ -386,12 +396,11 @@ __global__ __launch_bounds__(256) void k_mz_scan(KParams p)
 }
 
 // ---------------------------------------------------------------------------
-// dtheta: per (sub-chunk, group): E = exp(l - M'_s) and P = R_s Z_{s-1} +
-// prefix_j E for every landmark row (written for the attention epilogue and
-// the commit), and TH[s][gh*m+b][t] = sum_j E_bj v_evicted(j)[t] on fp16
+// dtheta: per (sub-chunk, group): E = exp(l - M'_s) for every landmark row
+// (written over the scores, for the attention epilogue), and
+// TH[s][gh*m+b][t] = sum_j E_bj v_evicted(j)[t] on fp16
 // MFMA with hi/lo splits (C[b][t]; each lane holds rows hf*32 .. +31 of its
-// E row, so its prefix is a register loop, and k-step st takes rows
-// 32 hf + 8 st .. +7).  E is scaled by 2^12 and the values by the pass's
+// E row, and k-step st takes rows 32 hf + 8 st .. +7).  E is scaled by 2^12 and the values by the pass's
 // power of two (value_exp) before the split, so that the fp16 remainders of
 // small values stay far above their absolute floor and large values stay in
 // fp16 range; the result is scaled back exactly.  The evicted values are
@@ -464,40 +473,21 @@ __global__ __launch_bounds__(256) void k_dtheta(KParams p)
         float e[32];
         {
             float* Lr = p.E + (row0 + min(hb, hm - 1)) * SUB + hf * 32;
-            // P is stored per (sub-chunk, head, row j) with the landmarks
-            // contiguous: PT[s][gh][j][64], b < m
-            const int hbc = min(hb, hm - 1);
-            float* Pt = p.P + (((int64_t)s * p.nh + g * p.H + hbc / p.m) * SUB + hf * 32) * 64 + hbc % p.m;
             const float Mn = p.Ms[row0 + min(hb, hm - 1)];
-            const float base = p.Rs[row0 + min(hb, hm - 1)] * p.TZ[row0 + min(hb, hm - 1)];
 #pragma unroll
             for (int k = 0; k < 32; k += 4) {
                 const float4 x = *reinterpret_cast<const float4*>(Lr + k);
                 e[k] = x.x; e[k + 1] = x.y; e[k + 2] = x.z; e[k + 3] = x.w;
             }
-            float run = 0.f;
 #pragma unroll
-            for (int k = 0; k < 32; ++k) {
-                e[k] = (rv && e[k] != -INFINITY) ? expf(e[k] - Mn) : 0.f;
-                run += e[k];
-            }
-            // the second half's prefix starts after the first half's total
-            const float first = __shfl(run, ln, 64);
-            float pre = base + (hf ? first : 0.f);
+            for (int k = 0; k < 32; ++k) e[k] = (rv && e[k] != -INFINITY) ? expf(e[k] - Mn) : 0.f;
+            // E replaces the scores in the plane: the attention epilogue reads it
             if (rv) {
 #pragma unroll
                 for (int k = 0; k < 32; k += 4) {
-                    float4 pe, pp;
+                    float4 pe;
                     pe.x = e[k]; pe.y = e[k + 1]; pe.z = e[k + 2]; pe.w = e[k + 3];
-                    pre += e[k]; pp.x = pre;
-                    pre += e[k + 1]; pp.y = pre;
-                    pre += e[k + 2]; pp.z = pre;
-                    pre += e[k + 3]; pp.w = pre;
                     *reinterpret_cast<float4*>(Lr + k) = pe;
-                    Pt[(k + 0) * 64] = pp.x;
-                    Pt[(k + 1) * 64] = pp.y;
-                    Pt[(k + 2) * 64] = pp.z;
-                    Pt[(k + 3) * 64] = pp.w;
                 }
             }
         }

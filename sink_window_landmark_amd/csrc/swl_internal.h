@@ -38,8 +38,7 @@ struct KParams {
     int T;   // rows (<= PASS_SUBS * SUB)
     int S;   // sub-chunks, ceil(T / SUB)
     // scratch planes (see scratch_layout)
-    float* E;    // [S][nh*m][SUB]  scores, then exp mass against the post-sub-chunk max
-    float* P;    // [S][nh][SUB][64] far mass prefix R*Z + sum_{j'<=j} E of row j, landmark b < m
+    float* E;    // [S][nh*m][SUB]  scores of the evicted keys (-inf: no eviction), then exp against the post-sub-chunk max
     float* Ms;   // [S][nh*m]       local max of the scores, then the post-sub-chunk max
     float* Rs;   // [S][nh*m]       local mass of the scores, then the rescale of the old mass
     float* TZ;   // [S+1][nh*m]     mass before each sub-chunk, then after the last
@@ -162,6 +161,33 @@ __host__ __device__ inline int value_exp_of(float vmax)
     int ex;
     frexpf(vmax, &ex);   // vmax = f 2^ex, 0.5 <= f < 1
     return 14 - ex;
+}
+
+// Work item (s, gi, sp) at position pos of an order that splits the S
+// sub-chunks into 8 contiguous ranges, one per XCD (xcd_work_item deals
+// positions to XCDs in contiguous runs), then takes the NG groups (or
+// (head group, group) pairs) of a range one after the other, then the
+// sub-chunks of the range, then nsp splits of each.  Each XCD then runs an
+// equal share of every group's sub-chunks, whatever the groups' windows,
+// while the blocks it runs together still cover consecutive sub-chunks of
+// one group (which share their key band in its L2).
+__device__ __forceinline__ void range_item(int pos, int S, int NG, int nsp, int& s, int& gi, int& sp)
+{
+    const int per_s = NG * nsp, q = S >> 3, rem = S & 7;
+    int lo = 0;
+    s = gi = sp = 0;
+    for (int r = 0; r < 8; ++r) {
+        const int len = q + (r < rem ? 1 : 0);
+        if (pos < (lo + len) * per_s) {
+            const int local = pos - lo * per_s;
+            sp = local % nsp;
+            const int t = local / nsp;   // gi * len + (s - lo)
+            s = lo + t % len;
+            gi = t / len;
+            return;
+        }
+        lo += len;
+    }
 }
 
 // Launchers (each returns the launch's hipGetLastError).
