@@ -146,9 +146,12 @@ int swl_prefill(const swl_geom* geom, const swl_state* st,
                 const float* q, const float* k, const float* v, int64_t rows,
                 float* out, void* scratch, size_t scratch_bytes, void* stream);
 
-/* Stages of a call, as reported to a swl_stage_fn.  Launch order: value
- * scale, far score, far scan, dtheta, theta scan, kv split, attend, ring,
- * meta. */
+/* Stages of a call, as reported to a swl_stage_fn.  A prefill pass makes
+ * six launches, reported in this order: far score (which also takes the
+ * values' scale), far scan, dtheta, theta scan (which also splits the key
+ * tiles), attend, ring (which also updates meta).  SWL_STAGE_META,
+ * SWL_STAGE_KV_SPLIT and SWL_STAGE_VALUE_SCALE name parts of those
+ * launches and are not reported on their own. */
 enum swl_stage {
     SWL_STAGE_FAR_SCORE = 0,  /* evicted key x landmark scores */
     SWL_STAGE_FAR_SCAN = 1,   /* post-sub-chunk max, rescale and incoming mass */

@@ -80,7 +80,7 @@ static bool state_ok(const swl_geom* g, const swl_state* st)
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Carve {
-    size_t tok, apart, vm, e, ms, rs, tz, th, kv, total;
+    size_t tok, apart, mc, vm, e, ms, rs, tz, th, kv, total;
 };
 
 static Carve carve(const swl_geom* g, int S)
@@ -91,7 +91,8 @@ static Carve carve(const swl_geom* g, int S)
     // the decode plane comes first, at an offset that does not depend on S
     c.tok = off; off += align256(sizeof(float) * tok_part_floats(g->G, g->H, g->dv, g->ns, g->W));
     c.apart = off; off += align256(sizeof(float) * attend_part_floats(g->d));
-    c.vm = off; off += align256(sizeof(float) * (size_t)g->G * VM_BLOCKS);
+    c.mc = off; off += align256(sizeof(uint32_t) * 4 * (size_t)g->G);
+    c.vm = off; off += align256(sizeof(float) * (size_t)g->G * VM_SLOTS);
     c.e = off;  off += align256(sizeof(float) * (size_t)S * nhm * SUB);
     c.ms = off; off += align256(sizeof(float) * (size_t)S * nhm);
     c.rs = off; off += align256(sizeof(float) * (size_t)S * nhm);
@@ -117,7 +118,7 @@ static KParams make_params(const swl_geom* g, const swl_state* st)
     p.G = g->G; p.H = g->H; p.m = g->m; p.W = g->W; p.ns = g->ns;
     p.d = g->d; p.dv = g->dv; p.nh = g->G * g->H; p.rect = g->rect;
     p.scale = g->scale;
-    p.meta = st->meta; p.ring_k = st->ring_k; p.ring_v = st->ring_v;
+    p.meta = st->meta; p.meta_out = st->meta; p.ring_k = st->ring_k; p.ring_v = st->ring_v;
     p.sink_k = st->sink_k; p.sink_v = st->sink_v; p.k_tilde = st->k_tilde;
     p.q_tilde = st->q_tilde; p.mu = st->mu; p.mz = st->mz; p.theta = st->theta;
     return p;
@@ -134,6 +135,8 @@ static void set_scratch(KParams& p, const swl_geom* g, void* scratch, int S)
     p.TH = reinterpret_cast<float*>(b + c.th);
     p.apart = reinterpret_cast<float*>(b + c.apart);
     p.vmax = reinterpret_cast<float*>(b + c.vm);
+    p.vm_n = fs_blocks_per_group(S, g->G);
+    p.meta_copy = reinterpret_cast<uint32_t*>(b + c.mc);
     p.kvs = reinterpret_cast<unsigned short*>(b + c.kv);
     p.kv_tiles = kv_tiles(g->ns, g->W, S);
 }
@@ -154,26 +157,35 @@ static void set_fuse(KParams& p, const swl_fuse* f, int64_t row0)
         if ((x) != hipSuccess) return SWL_EHIP; \
     } while (0)
 
-// The values' scale, far_e (scores, scan, E/P and the accumulator
-// increment) + attention (near part and far readout) of one call; the state
-// is unchanged.
+// The launches after a call's first one read the call-start meta from its
+// copy in scratch (far_score wrote it), so that the last one can update the
+// state's meta while others read the old.
+static KParams after_first(const KParams& p)
+{
+    KParams q = p;
+    q.meta = p.meta_copy;
+    return q;
+}
+
+// far_e (the values' scale, scores, scan, E and the accumulator increment)
+// + attention (near part and far readout) of one call; the state is
+// unchanged.
 static int run_attend(const KParams& p, hipStream_t st)
 {
-    SWL_TRY(launch_vmax(p, st));
     SWL_TRY(launch_far_score(p, st));
-    SWL_TRY(launch_far_scan(p, st));
-    SWL_TRY(launch_dtheta(p, st));
-    SWL_TRY(launch_kv_split(p, st));
-    SWL_TRY(launch_attend(p, st));
+    const KParams q = after_first(p);
+    SWL_TRY(launch_far_scan(q, st));
+    SWL_TRY(launch_dtheta(q, st));
+    SWL_TRY(launch_theta_kv(q, false, true, st));
+    SWL_TRY(launch_attend(q, st));
     return SWL_OK;
 }
 
-// far commit + ring commit + meta of one call (after run_attend on its rows).
+// far commit + ring commit + meta of one call (after run_attend on its rows,
+// whose scratch holds the call-start meta), in one launch.
 static int run_commit(const KParams& p, hipStream_t st)
 {
-    SWL_TRY(launch_theta_scan(p, true, st));
-    SWL_TRY(launch_ring_commit(p, st));
-    SWL_TRY(launch_meta(p, st));
+    SWL_TRY(launch_commit(after_first(p), true, st));
     return SWL_OK;
 }
 
@@ -252,7 +264,8 @@ int swl_commit(const swl_geom* geom, const swl_state* st, const float* k, const 
 
 // Consecutive 64-row sub-chunks of `rows` rows, batched into passes of up
 // to PASS_SUBS sub-chunks: far_e, far commit, (attention,) ring commit and
-// meta of each pass.  Without `attend`, q and out are not used.
+// meta of each pass, in six launches (four without `attend`, where q and
+// out are not used).
 static int run_rows(const swl_geom* geom, const swl_state* st, const float* q, const float* k,
                     const float* v, int64_t rows, const swl_fuse* fuse, float* out, void* scratch,
                     size_t scratch_bytes, void* stream, swl_stage_fn fn, void* user, bool attend)
@@ -288,17 +301,17 @@ static int run_rows(const swl_geom* geom, const swl_state* st, const float* q, c
         set_scratch(p, geom, scratch, S_max);
         p.theta_prev = p.TH;
         p.theta_prev_stride = (int64_t)nh * geom->m * geom->dv;
-        SWL_STAGE(SWL_STAGE_VALUE_SCALE, launch_vmax(p, hs));
-        SWL_STAGE(SWL_STAGE_FAR_SCORE, launch_far_score(p, hs));
-        SWL_STAGE(SWL_STAGE_FAR_SCAN, launch_far_scan(p, hs));
-        SWL_STAGE(SWL_STAGE_DTHETA, launch_dtheta(p, hs));
-        SWL_STAGE(SWL_STAGE_THETA_SCAN, launch_theta_scan(p, true, hs));
+        SWL_STAGE(SWL_STAGE_FAR_SCORE, launch_far_score(p, hs));   // with the values' scale
+        const KParams q = after_first(p);
+        SWL_STAGE(SWL_STAGE_FAR_SCAN, launch_far_scan(q, hs));
+        SWL_STAGE(SWL_STAGE_DTHETA, launch_dtheta(q, hs));
         if (attend) {
-            SWL_STAGE(SWL_STAGE_KV_SPLIT, launch_kv_split(p, hs));
-            SWL_STAGE(SWL_STAGE_ATTEND, launch_attend(p, hs));
+            SWL_STAGE(SWL_STAGE_THETA_SCAN, launch_theta_kv(q, true, true, hs));   // with the key tiles
+            SWL_STAGE(SWL_STAGE_ATTEND, launch_attend(q, hs));
+            SWL_STAGE(SWL_STAGE_RING, launch_commit(q, false, hs));   // with the meta
+        } else {
+            SWL_STAGE(SWL_STAGE_THETA_SCAN, launch_commit(q, true, hs));   // with ring and meta
         }
-        SWL_STAGE(SWL_STAGE_RING, launch_ring_commit(p, hs));
-        SWL_STAGE(SWL_STAGE_META, launch_meta(p, hs));
         done += T;
     }
 #undef SWL_STAGE

@@ -69,6 +69,7 @@
 // Softmax runs online in base 2 (q is pre-scaled by scale*log2 e).
 #include "swl_internal.h"
 #include "lanes.h"
+#include "stages.h"
 
 namespace swl {
 
@@ -232,12 +233,12 @@ __device__ __forceinline__ void pv_step(floatx16 (&O)[NB], const float* row, int
 // attention takes back out of its value sums.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void k_kv_split(KParams p)
+__device__ __forceinline__ void kv_split_body(const KParams& p, int64_t bid)
 {
     using L = KvTile<D>;
     __shared__ float kf[KT][D + 1];
     __shared__ float vf[KT][D + 1];
-    const int t = blockIdx.x % p.kv_tiles, g = blockIdx.x / p.kv_tiles;
+    const int t = (int)(bid % p.kv_tiles), g = (int)(bid / p.kv_tiles);
     const int nst = (p.ns + KT - 1) / KT;
     const GMeta c = load_gmeta(p.meta, g, p.W);
     const int last = c.len0 + p.T - 1;   // last window position of the pass
@@ -288,6 +289,16 @@ __global__ __launch_bounds__(256) void k_kv_split(KParams p)
         *reinterpret_cast<u32x4*>(vo + dst) = u32x4{s0.hi, s1.hi, s2.hi, s3.hi};
         *reinterpret_cast<u32x4*>(vo + L::VH + dst) = u32x4{s0.lo, s1.lo, s2.lo, s3.lo};
     }
+}
+
+// The accumulator scan (stages.h; with its commit of Theta, M and Z) and
+// the key tiles of a pass in one launch: blocks [0, nth) scan, the rest
+// split tiles.  The two do not depend on each other.
+template <int D>
+__global__ __launch_bounds__(256) void k_theta_kv(KParams p, int nth)
+{
+    if ((int)blockIdx.x < nth) theta_scan_body(p, true, blockIdx.x);
+    else kv_split_body<D>(p, (int64_t)blockIdx.x - nth);
 }
 
 // MODE: AT_FULL, one block per (sub-chunk, group, head group) over all of its
@@ -878,21 +889,24 @@ int kv_tiles(int ns, int W, int S)
 size_t kv_tile_bytes(int d) { return (size_t)128 * ((d < 16 ? 16 : d) + d); }
 
 template <int D>
-static hipError_t launch_split_d(const KParams& p, hipStream_t st)
+static hipError_t launch_theta_kv_d(const KParams& p, bool theta, bool kv, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_kv_split<D>, dim3(p.G * p.kv_tiles), dim3(256), 0, st, p);
+    const int64_t nth = theta ? theta_blocks(p) : 0;
+    const int64_t nkv = kv ? (int64_t)p.G * p.kv_tiles : 0;
+    if (nth + nkv == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_theta_kv<D>, dim3((unsigned)(nth + nkv)), dim3(256), 0, st, p, (int)nth);
     return hipGetLastError();
 }
 
-hipError_t launch_kv_split(const KParams& p, hipStream_t st)
+hipError_t launch_theta_kv(const KParams& p, bool theta, bool kv, hipStream_t st)
 {
     switch (p.d) {
-    case 8: return launch_split_d<8>(p, st);
-    case 16: return launch_split_d<16>(p, st);
-    case 32: return launch_split_d<32>(p, st);
-    case 64: return launch_split_d<64>(p, st);
-    case 128: return launch_split_d<128>(p, st);
-    case 256: return launch_split_d<256>(p, st);
+    case 8: return launch_theta_kv_d<8>(p, theta, kv, st);
+    case 16: return launch_theta_kv_d<16>(p, theta, kv, st);
+    case 32: return launch_theta_kv_d<32>(p, theta, kv, st);
+    case 64: return launch_theta_kv_d<64>(p, theta, kv, st);
+    case 128: return launch_theta_kv_d<128>(p, theta, kv, st);
+    case 256: return launch_theta_kv_d<256>(p, theta, kv, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -66,50 +66,6 @@ __device__ __forceinline__ int kswz(int r, int c)
 }
 
 // ---------------------------------------------------------------------------
-// vmax: the largest |value| of each group's pass inputs -- its sinks, the
-// window at the start of the call and the pass's rows -- as VM_BLOCKS block
-// maxima per group (value_exp reduces them): the value products of the
-// pass (key tiles, accumulator increments) scale their fp16 splits by it.
-// Block b of group g takes rows b, b + VM_BLOCKS, ... of that list, DV/4
-// lanes per row.
-// ---------------------------------------------------------------------------
-template <int DV>
-__global__ __launch_bounds__(256) void k_vmax(KParams p)
-{
-    constexpr int LPR = DV / 4 < 64 ? DV / 4 : 64;   // lanes per row (64 at dv = 256: two float4 each)
-    constexpr int RPB = 256 / LPR;                    // rows per block step
-    __shared__ float red[4];
-    const int g = blockIdx.x / VM_BLOCKS, b = blockIdx.x % VM_BLOCKS;
-    const GMeta c = load_gmeta(p.meta, g, p.W);
-    const int n = p.ns + c.len0 + p.T;
-    const int li = threadIdx.x % LPR, rb = threadIdx.x / LPR;
-    constexpr int U = 8;   // rows whose loads are in flight together
-    float mx = 0.f;
-    for (int r0 = b * RPB + rb; r0 < n; r0 += U * VM_BLOCKS * RPB) {
-        float4 x[U][DV / (4 * LPR)];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int r = min(r0 + u * VM_BLOCKS * RPB, n - 1);   // clamped: rows past n repeat row n-1
-            const float* row = r < p.ns ? p.sink_v + ((int64_t)g * p.ns + r) * DV : val_row(p, c, g, r - p.ns);
-#pragma unroll
-            for (int k = 0; k < DV / (4 * LPR); ++k)
-                x[u][k] = *reinterpret_cast<const float4*>(row + 4 * li + 4 * LPR * k);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int k = 0; k < DV / (4 * LPR); ++k)
-                mx = fmaxf(mx, fmaxf(fmaxf(fabsf(x[u][k].x), fabsf(x[u][k].y)),
-                                     fmaxf(fabsf(x[u][k].z), fabsf(x[u][k].w))));
-    }
-    mx = wmax(mx);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
-    __syncthreads();
-    if (threadIdx.x == 0)
-        p.vmax[(int64_t)g * VM_BLOCKS + b] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-}
-
-// ---------------------------------------------------------------------------
 // far_score: L[s][gh*m+b][j] = scale <q~_{gh,b}, key evicted by row j>, -inf
 // for rows that do not evict, and per landmark row the local max mx and mass
 // zl = sum_j exp(l_j - mx) of the sub-chunk.  One block per (group, run of
@@ -120,16 +76,15 @@ __global__ __launch_bounds__(256) void k_vmax(KParams p)
 // the next sub-chunk are in flight while the current one is multiplied.
 // MFMA C[hb][j] = Q~ K_e^T on v_mfma_f32_32x32x16_f16 (three split products
 // per k-step; lane (row, hf) holds columns 16 st + 8 hf .. +7 of its row).
+//
+// As the first launch of a call it also (a) copies the call-start meta to
+// p.meta_copy (block 0), which the later launches read, so that the last one
+// can write the new meta, and (b) takes the largest |value| of an equal share
+// of its group's value rows -- the sinks, the window at the call's start and
+// the call's rows -- into p.vmax[g][run]: the value products of the call
+// (key tiles, accumulator increments) scale their fp16 splits by the
+// group's maximum (value_exp).
 // ---------------------------------------------------------------------------
-constexpr int FS_RUN = 4;
-// sub-chunks per block: FS_RUN while the launch keeps at least 256 blocks,
-// fewer for short calls
-__host__ __device__ inline int fs_run(int S, int G)
-{
-    int rl = FS_RUN;
-    while (rl > 1 && ((S + rl - 1) / rl) * G < 256) rl >>= 1;
-    return rl;
-}
 // eight waves; four at d = 256, where the query halves alone take 128 registers
 template <int D>
 constexpr int fs_threads() { return D > 128 ? 256 : 512; }
@@ -151,10 +106,11 @@ __global__ __launch_bounds__(fs_threads<D>()) void k_far_score(KParams p)
     constexpr int PT = (N + FS_THREADS - 1) / FS_THREADS;
 
     const int rl = fs_run(p.S, p.G);
-    const int nrun = (p.S + rl - 1) / rl;
-    const int w = xcd_work_item(blockIdx.x, nrun * p.G);
-    const int run = w % nrun, g = w / nrun;
-    const int s_lo = run * rl, s_hi = min(p.S, s_lo + rl);
+    const int nrun = fs_runs(p.S, p.G);
+    const int nblk = fs_blocks_per_group(p.S, p.G);   // nrun, or more for short calls
+    const int w = xcd_work_item(blockIdx.x, nblk * p.G);
+    const int run = w % nblk, g = w / nblk;
+    const int s_lo = min(run, nrun - 1) * rl, s_hi = min(p.S, s_lo + rl);
     const GMeta c = load_gmeta(p.meta, g, p.W);
     const int hm = p.H * p.m;
     const int64_t nhm = (int64_t)p.nh * p.m;
@@ -222,9 +178,44 @@ __global__ __launch_bounds__(fs_threads<D>()) void k_far_score(KParams p)
         }
     };
 
+    if (blockIdx.x == 0 && tid < 4 * p.G) p.meta_copy[tid] = p.meta[tid];
     {
         v4 x[PT];
         load_keys(s_lo, x);
+        // the largest |value| of this block's share of the group's value rows
+        // (its loads go out beside the first sub-chunk's keys)
+        {
+            constexpr int LPR = D / 4 < 64 ? D / 4 : 64;   // lanes per row (d <= 256: one float4 each)
+            constexpr int RPB = FS_THREADS / LPR;           // rows per step
+            constexpr int U = 4;                            // steps in flight
+            const int64_t n = (int64_t)p.ns + c.len0 + p.T;
+            const int r_lo = (int)(n * run / nblk), r_hi = (int)(n * (run + 1) / nblk);
+            const int li = tid % LPR, rb = tid / LPR;
+            float mx = 0.f;
+            for (int r0 = r_lo + rb; r0 < r_hi; r0 += U * RPB) {
+                float4 v[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int r = min(r0 + u * RPB, r_hi - 1);   // clamped: repeats a row of the share
+                    const float* row = r < p.ns ? p.sink_v + ((int64_t)g * p.ns + r) * D : val_row(p, c, g, r - p.ns);
+                    v[u] = *reinterpret_cast<const float4*>(row + 4 * li);
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w))));
+            }
+            mx = wmax(mx);
+            __shared__ float vred[FS_THREADS / 64];
+            if (lane == 0) vred[wave] = mx;
+            __syncthreads();
+            if (tid == 0) {
+                float b = 0.f;
+#pragma unroll
+                for (int w2 = 0; w2 < FS_THREADS / 64; ++w2) b = fmaxf(b, vred[w2]);
+                p.vmax[(int64_t)g * VM_SLOTS + run] = b;
+            }
+        }
+        if (run >= nrun) return;   // a block for the value maxima only (uniform over the block)
         store_keys(s_lo, x, ek[0]);
     }
     if (resident && wave < nht) load_q(wave);
@@ -323,8 +314,6 @@ __global__ __launch_bounds__(fs_threads<D>()) void k_far_score(KParams p)
 // sum_j E_sj, up to rounding), and the final mass into TZ[S].  Reads the local
 // (mx, zl) that far_score left in Ms/Rs and replaces them with M'_s and R_s.
 // ---------------------------------------------------------------------------
-constexpr int SCAN_AHEAD = 32;  // theta_scan's prefetch depth
-
 // (M, Z) of a run of sub-chunks: the max and the mass against it; a run
 // with no evictions is (-inf, 0).  Runs a then b combine to the pair of the
 // concatenation: the online-softmax merge, an associative operation.
@@ -550,81 +539,11 @@ __global__ __launch_bounds__(256) void k_dtheta(KParams p)
 }
 
 // ---------------------------------------------------------------------------
-// theta_scan: one thread per (gh, b, t), walking the sub-chunks in order:
-// TH[s] <- Theta (the value before sub-chunk s, which the readout of s uses),
-// Theta <- R_s Theta + dTheta_s.  With `commit` the final Theta, M and Z go
-// to the state (o1b_far_commit: M <- M', Z <- the mass after the rows).
-//
-// Theta is carried as an unevaluated sum th + tc of two fp32 numbers
-// (compensated summation): the rounding error of each product R_s th (an
-// fma gives it exactly) and of each sum (Knuth's two-sum) goes into tc, so
-// the running value keeps about twice fp32's precision over the hundreds of
-// sub-chunks of a pass, and only its final rounding to one fp32 number
-// (and each TH[s]) is left.  The element of an accumulator that sums tens
-// of thousands of signed terms can cancel to a value far below the terms'
-// scale; plain fp32 accumulation would leave there an error of order
-// 2^-24 times the partial sums' magnitude per sub-chunk.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void two_sum(float a, float b, float& s, float& e)
-{
-#pragma clang fp contract(off)
-    s = a + b;
-    const float bv = s - a;
-    e = (a - (s - bv)) + (b - bv);
-}
-
-__global__ __launch_bounds__(256) void k_theta_scan(KParams p, int commit)
-{
-    // every product and sum below rounds on its own: a product fused into a
-    // later sum would no longer be the value whose error the fma takes
-#pragma clang fp contract(off)
-    const int64_t nhm = (int64_t)p.nh * p.m;
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= nhm * p.dv) return;
-    const int64_t ghb = idx / p.dv;
-    const int64_t stride = nhm * p.dv;
-    float th = p.theta[idx], tc = 0.f;
-    for (int s0 = 0; s0 < p.S; s0 += SCAN_AHEAD) {
-        float dth[SCAN_AHEAD], rs[SCAN_AHEAD];
-#pragma unroll
-        for (int k = 0; k < SCAN_AHEAD; ++k) {
-            const int s = min(s0 + k, p.S - 1);
-            dth[k] = p.TH[(int64_t)s * stride + idx];
-            rs[k] = p.Rs[(int64_t)s * nhm + ghb];
-        }
-#pragma unroll
-        for (int k = 0; k < SCAN_AHEAD; ++k) {
-            const int s = s0 + k;
-            if (s < p.S) {
-                p.TH[(int64_t)s * stride + idx] = th;
-                // (th + tc) R + d, with the errors of R th and of the sum kept
-                const float pr = rs[k] * th;
-                const float pe = fmaf(rs[k], th, -pr);
-                float sm, se;
-                two_sum(pr, dth[k], sm, se);
-                const float lo = fmaf(rs[k], tc, pe + se);
-                two_sum(sm, lo, th, tc);
-            }
-        }
-    }
-    if (commit) {
-        p.theta[idx] = th;
-        if (idx % p.dv == 0) {
-            const int64_t gh = ghb / p.m, b = ghb % p.m;
-            const int64_t last = (int64_t)(p.S - 1) * nhm + ghb;
-            p.mz[gh * 2 * p.m + b] = p.Ms[last];
-            p.mz[gh * 2 * p.m + p.m + b] = p.TZ[(int64_t)p.S * nhm + ghb];
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
 template <int D>
 static void launch_fs(const KParams& p, hipStream_t st)
 {
-    const int rl = fs_run(p.S, p.G);
-    const int nrun = (p.S + rl - 1) / rl;
-    hipLaunchKernelGGL(k_far_score<D>, dim3(nrun * p.G), dim3(fs_threads<D>()), 0, st, p);
+    hipLaunchKernelGGL(k_far_score<D>, dim3(fs_blocks_per_group(p.S, p.G) * p.G), dim3(fs_threads<D>()), 0, st,
+                       p);
 }
 
 hipError_t launch_far_score(const KParams& p, hipStream_t st)
@@ -649,26 +568,6 @@ hipError_t launch_far_scan(const KParams& p, hipStream_t st)
 }
 
 template <int DV>
-static void launch_vm(const KParams& p, hipStream_t st)
-{
-    hipLaunchKernelGGL(k_vmax<DV>, dim3(p.G * VM_BLOCKS), dim3(256), 0, st, p);
-}
-
-hipError_t launch_vmax(const KParams& p, hipStream_t st)
-{
-    switch (p.dv) {
-    case 8: launch_vm<8>(p, st); break;
-    case 16: launch_vm<16>(p, st); break;
-    case 32: launch_vm<32>(p, st); break;
-    case 64: launch_vm<64>(p, st); break;
-    case 128: launch_vm<128>(p, st); break;
-    case 256: launch_vm<256>(p, st); break;
-    default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-}
-
-template <int DV>
 static void launch_dt(const KParams& p, hipStream_t st)
 {
     hipLaunchKernelGGL(k_dtheta<DV>, dim3(p.S * p.G), dim3(256), 0, st, p);
@@ -685,14 +584,6 @@ hipError_t launch_dtheta(const KParams& p, hipStream_t st)
     case 256: launch_dt<256>(p, st); break;
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
-}
-
-hipError_t launch_theta_scan(const KParams& p, bool commit, hipStream_t st)
-{
-    int64_t n = (int64_t)p.nh * p.m * p.dv;
-    hipLaunchKernelGGL(k_theta_scan, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p,
-                       commit ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -149,12 +149,13 @@ __device__ __forceinline__ float max32(float x)
     return pair_max<4>(x);
 }
 
-// value_exp_of over group g's block maxima (k_vmax), evaluated by every
+// value_exp_of over group g's block maxima (far_score), evaluated by every
 // lane of the calling wave (all 64 lanes must call it).
 __device__ __forceinline__ int value_exp(const KParams& p, int g)
 {
-    static_assert(VM_BLOCKS == 64, "one block maximum per lane");
-    const float x = wmax(p.vmax[(int64_t)g * VM_BLOCKS + (threadIdx.x & 63)]);
+    float x = 0.f;
+    for (int i = threadIdx.x & 63; i < p.vm_n; i += 64) x = fmaxf(x, p.vmax[(int64_t)g * VM_SLOTS + i]);
+    x = wmax(x);
     return __builtin_amdgcn_readfirstlane(value_exp_of(x));   // the same in every lane
 }
 

@@ -1,7 +1,9 @@
-// State kernels: the empty state, the ring commit and the ring bookkeeping.
-// cortiq-engine 0.8.51 src/gpu_wgpu/o1_batch.rs, o1b_ring_commit and
-// o1b_meta, applied to all rows of a call at once.
+// State kernels: the empty state, the end of a call (accumulator scan, ring
+// commit, meta) and the rewind of one push.  cortiq-engine 0.8.51
+// src/gpu_wgpu/o1_batch.rs, o1b_far_commit, o1b_ring_commit and o1b_meta,
+// applied to all rows of a call at once.
 #include "swl_internal.h"
+#include "stages.h"
 
 namespace swl {
 
@@ -23,44 +25,19 @@ __global__ void k_init(KParams p, Windows win)
     }
 }
 
-// Chunk row r of the call lands in slot (head0 + len0 + r) mod w_g, the
-// slot its own eviction freed (o1b_ring_commit).  Only the last w_g rows of
-// the call survive in the ring, so only they are written: that keeps the
-// writes of a call whose rows outnumber the window free of collisions.
-// One block per (row, group), rows counted back from the end of the call.
-__global__ __launch_bounds__(256) void k_ring_commit(KParams p)
+// The end of a call in one launch: (with `nth` > 0) the accumulator scan
+// with its commit, the ring commit, and the meta update (stages.h).  Blocks
+// [0, nth) scan, the next ring_blocks(p) commit rows, and the last one
+// writes the meta.  None depends on another: every reader of the old ring
+// rows and meta ran in earlier launches, and these read the call-start meta
+// from its copy (p.meta).
+__global__ __launch_bounds__(256) void k_commit(KParams p, int nth)
 {
-    const int g = blockIdx.y;
-    const GMeta c = load_gmeta(p.meta, g, p.W);
-    const int r = p.T - 1 - (int)blockIdx.x;
-    if (r < 0 || r < p.T - c.wg) return;
-    const int slot = (int)(((int64_t)c.head0 + c.len0 + r) % c.wg);
-    const float* ks = p.k + ((int64_t)r * p.G + g) * p.d;
-    const float* vs = p.v + ((int64_t)r * p.G + g) * p.dv;
-    float* kd = p.ring_k + ((int64_t)g * p.W + slot) * p.d;
-    float* vd = p.ring_v + ((int64_t)g * p.W + slot) * p.dv;
-    const float* kt = p.rope ? p.rope + (int64_t)r * p.d : nullptr;   // the ring holds turned keys
-    for (int t = threadIdx.x; t < p.d / 4; t += 256)
-        reinterpret_cast<float4*>(kd)[t] = rope4(ks, kt, 4 * t, p.d);
-    for (int t = threadIdx.x; t < p.dv / 4; t += 256)
-        reinterpret_cast<float4*>(vd)[t] = reinterpret_cast<const float4*>(vs)[t];
-}
-
-// len, head and nfar after T pushes (o1b_meta with k = T).
-__global__ void k_meta(KParams p)
-{
-    const int g = blockIdx.x * blockDim.x + threadIdx.x;
-    if (g >= p.G) return;
-    const GMeta c = load_gmeta(p.meta, g, p.W);
-    const int64_t tot = (int64_t)c.len0 + p.T;
-    if (tot <= c.wg) {
-        p.meta[4 * g + 0] = (uint32_t)tot;
-    } else {
-        const int64_t ev = tot - c.wg;
-        p.meta[4 * g + 0] = (uint32_t)c.wg;
-        p.meta[4 * g + 1] = (uint32_t)((c.head0 + ev) % c.wg);
-        p.meta[4 * g + 2] = (uint32_t)(c.nfar0 + ev);
-    }
+    const int64_t b = blockIdx.x;
+    const int64_t nring = ring_blocks(p);
+    if (b < nth) theta_scan_body(p, true, b);
+    else if (b < nth + nring) ring_body(p, b - nth);
+    else meta_body(p);
 }
 
 hipError_t launch_init(const KParams& p, const uint32_t* windows, hipStream_t st)
@@ -75,16 +52,10 @@ hipError_t launch_init(const KParams& p, const uint32_t* windows, hipStream_t st
     return hipGetLastError();
 }
 
-hipError_t launch_ring_commit(const KParams& p, hipStream_t st)
+hipError_t launch_commit(const KParams& p, bool theta, hipStream_t st)
 {
-    const int rows = p.T < p.W ? p.T : p.W;
-    hipLaunchKernelGGL(k_ring_commit, dim3(rows, p.G), dim3(256), 0, st, p);
-    return hipGetLastError();
-}
-
-hipError_t launch_meta(const KParams& p, hipStream_t st)
-{
-    hipLaunchKernelGGL(k_meta, dim3((p.G + 63) / 64), dim3(64), 0, st, p);
+    const int64_t nth = theta ? theta_blocks(p) : 0;
+    hipLaunchKernelGGL(k_commit, dim3((unsigned)(nth + ring_blocks(p) + 1)), dim3(256), 0, st, p, (int)nth);
     return hipGetLastError();
 }
 

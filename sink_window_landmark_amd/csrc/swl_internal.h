@@ -12,15 +12,19 @@ namespace swl {
 
 constexpr int SUB = SWL_SUB;           // rows of a sub-chunk
 constexpr int PASS_SUBS = 512;         // sub-chunks per prefill pass (32768 rows)
-constexpr int VM_BLOCKS = 64;          // blocks per group of the value-range pass (one wave's lanes)
+constexpr int VM_SLOTS = PASS_SUBS;     // value maxima per group (one per far_score block, <= 512)
 
 // Everything a kernel of one call (or one prefill pass) needs, passed by value.
 struct KParams {
     // geometry
     int G, H, m, W, ns, d, dv, nh, rect;
     float scale;
-    // state
+    // state (meta: the call-start bookkeeping; after a call's first launch it
+    // points to the copy in scratch, meta_copy, so that the last launch can
+    // write the new one to meta_out while others read the old)
     uint32_t* meta;
+    uint32_t* meta_copy;      // [G][4] scratch copy of the call-start meta (written by far_score)
+    uint32_t* meta_out;       // the state's meta (written by the meta update)
     float* ring_k;
     float* ring_v;
     const float* sink_k;
@@ -47,7 +51,8 @@ struct KParams {
     int64_t theta_prev_stride;
     float* apart;             // split-window attention partials (attend_part_floats())
     int nsp;                  // splits of the window per attention work item (set by launch_attend)
-    float* vmax;              // [G][VM_BLOCKS] largest |value| seen by each block of k_vmax
+    float* vmax;              // [G][VM_SLOTS] largest |value| seen by each far_score block of the group
+    int vm_n;                 // far_score blocks per group (slots of vmax in use)
     unsigned short* kvs;      // [G][kv_tiles] fp16 key tiles of the pass (k_kv_split)
     int kv_tiles;             // tiles per group: the sinks, then the aligned window tiles
     // fused ingest and output steps (null: off)
@@ -190,14 +195,38 @@ __device__ __forceinline__ void range_item(int pos, int S, int NG, int nsp, int&
     }
 }
 
+// far_score: sub-chunks per block (FS_RUN while the launch keeps at least
+// 256 blocks, fewer for short calls) and blocks per group
+constexpr int FS_RUN = 4;
+__host__ __device__ inline int fs_run(int S, int G)
+{
+    int rl = FS_RUN;
+    while (rl > 1 && ((S + rl - 1) / rl) * G < 256) rl >>= 1;
+    return rl;
+}
+// blocks per group of runs of sub-chunks
+__host__ __device__ inline int fs_runs(int S, int G)
+{
+    const int rl = fs_run(S, G);
+    return (S + rl - 1) / rl;
+}
+// blocks per group of the launch: one per run, and at least 32, so that the
+// value maxima of a short call still spread over many blocks (the blocks
+// past the runs take only their share of the values)
+constexpr int FS_MIN_BLOCKS = 32;
+__host__ __device__ inline int fs_blocks_per_group(int S, int G)
+{
+    const int n = fs_runs(S, G);
+    return n > FS_MIN_BLOCKS ? n : FS_MIN_BLOCKS;
+}
+
 // Launchers (each returns the launch's hipGetLastError).
 hipError_t launch_init(const KParams& p, const uint32_t* windows, hipStream_t st);
-hipError_t launch_vmax(const KParams& p, hipStream_t st);
 hipError_t launch_far_score(const KParams& p, hipStream_t st);
 hipError_t launch_far_scan(const KParams& p, hipStream_t st);
 hipError_t launch_dtheta(const KParams& p, hipStream_t st);
-hipError_t launch_theta_scan(const KParams& p, bool commit, hipStream_t st);
-hipError_t launch_kv_split(const KParams& p, hipStream_t st);
+// the accumulator scan (commit) and the key tiles in one launch (either may be off)
+hipError_t launch_theta_kv(const KParams& p, bool theta, bool kv, hipStream_t st);
 hipError_t launch_attend(const KParams& p, hipStream_t st);
 // tiles per group and bytes per tile of the fp16 key tiles
 int kv_tiles(int ns, int W, int S);
@@ -205,8 +234,8 @@ size_t kv_tile_bytes(int d);
 // floats of the split-window attention partials (a plane of fixed size: at
 // most 256 (block, split) pairs of one launch)
 size_t attend_part_floats(int d);
-hipError_t launch_ring_commit(const KParams& p, hipStream_t st);
-hipError_t launch_meta(const KParams& p, hipStream_t st);
+// the ring commit and the meta update, after the accumulator scan when `theta`
+hipError_t launch_commit(const KParams& p, bool theta, hipStream_t st);
 hipError_t launch_rewind(const KParams& p, hipStream_t st);
 // one-row decode: partials, then merge + commit; `part` holds tok_part_floats()
 hipError_t launch_token(const KParams& p, float* part, hipStream_t st);
