@@ -80,7 +80,7 @@ static bool state_ok(const swl_geom* g, const swl_state* st)
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Carve {
-    size_t tok, apart, mc, vm, e, ms, rs, tz, th, kv, total;
+    size_t tok, apart, mc, vm, e, fac, ms, rs, tz, th, kv, total;
 };
 
 static Carve carve(const swl_geom* g, int S)
@@ -94,6 +94,7 @@ static Carve carve(const swl_geom* g, int S)
     c.mc = off; off += align256(sizeof(uint32_t) * 4 * (size_t)g->G);
     c.vm = off; off += align256(sizeof(float) * (size_t)g->G * VM_SLOTS);
     c.e = off;  off += align256(sizeof(float) * (size_t)S * nhm * SUB);
+    c.fac = off; off += align256(sizeof(float) * (size_t)S * nhm);
     c.ms = off; off += align256(sizeof(float) * (size_t)S * nhm);
     c.rs = off; off += align256(sizeof(float) * (size_t)S * nhm);
     c.tz = off; off += align256(sizeof(float) * (size_t)(S + 1) * nhm);
@@ -129,6 +130,7 @@ static void set_scratch(KParams& p, const swl_geom* g, void* scratch, int S)
     Carve c = carve(g, S);
     char* b = static_cast<char*>(scratch);
     p.E = reinterpret_cast<float*>(b + c.e);
+    p.FAC = reinterpret_cast<float*>(b + c.fac);
     p.Ms = reinterpret_cast<float*>(b + c.ms);
     p.Rs = reinterpret_cast<float*>(b + c.rs);
     p.TZ = reinterpret_cast<float*>(b + c.tz);
@@ -174,8 +176,7 @@ static int run_attend(const KParams& p, hipStream_t st)
 {
     SWL_TRY(launch_far_score(p, st));
     const KParams q = after_first(p);
-    SWL_TRY(launch_far_scan(q, st));
-    SWL_TRY(launch_dtheta(q, st));
+    SWL_TRY(launch_scan_dtheta(q, st));
     SWL_TRY(launch_theta_kv(q, false, true, st));
     SWL_TRY(launch_attend(q, st));
     return SWL_OK;
@@ -264,7 +265,7 @@ int swl_commit(const swl_geom* geom, const swl_state* st, const float* k, const 
 
 // Consecutive 64-row sub-chunks of `rows` rows, batched into passes of up
 // to PASS_SUBS sub-chunks: far_e, far commit, (attention,) ring commit and
-// meta of each pass, in six launches (four without `attend`, where q and
+// meta of each pass, in five launches (three without `attend`, where q and
 // out are not used).
 static int run_rows(const swl_geom* geom, const swl_state* st, const float* q, const float* k,
                     const float* v, int64_t rows, const swl_fuse* fuse, float* out, void* scratch,
@@ -303,8 +304,7 @@ static int run_rows(const swl_geom* geom, const swl_state* st, const float* q, c
         p.theta_prev_stride = (int64_t)nh * geom->m * geom->dv;
         SWL_STAGE(SWL_STAGE_FAR_SCORE, launch_far_score(p, hs));   // with the values' scale
         const KParams q = after_first(p);
-        SWL_STAGE(SWL_STAGE_FAR_SCAN, launch_far_scan(q, hs));
-        SWL_STAGE(SWL_STAGE_DTHETA, launch_dtheta(q, hs));
+        SWL_STAGE(SWL_STAGE_FAR_SCAN, launch_scan_dtheta(q, hs));   // with the increments
         if (attend) {
             SWL_STAGE(SWL_STAGE_THETA_SCAN, launch_theta_kv(q, true, true, hs));   // with the key tiles
             SWL_STAGE(SWL_STAGE_ATTEND, launch_attend(q, hs));

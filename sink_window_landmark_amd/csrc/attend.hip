@@ -14,9 +14,10 @@
 //   is the far mass prefix, so D_far = sum_b gain_b R_b Z_b +
 //   sum_{j0<=j<=i} cf_j, which is how it is formed here;
 //   out = (N_far + sum p v) / max(D_far + sum p, 1e-30), p = e^{s-c}.
-// M', R, the incoming mass Z (far_scan), E (dtheta) and Theta before the
-// sub-chunk (theta_scan, or the state for a single sub-chunk) are ready
-// before this kernel runs.
+// M', R, the incoming mass Z and fac = exp(mx - M') (far_scan), E against
+// the sub-chunk's own max mx (far_score) and Theta before the sub-chunk
+// (theta_scan, or the state for a single sub-chunk) are ready before this
+// kernel runs.
 //
 // The near part never depends on the far field, so every sub-chunk of a call
 // is computed in one launch: one block per (sub-chunk, KV group, group of up
@@ -335,7 +336,7 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
     constexpr int LDF = D + 4;                // fp32 row stride of the epilogue's tiles
     constexpr int NEAR_BYTES = 2 * L::BYTES;
     constexpr int KTB = 2 * 2 * L::KH * 2;     // landmark keys as two fp16 hi/lo K tiles
-    constexpr int FAR_BYTES = KTB + 2 * KT * LDF * 4 + HPB * 3 * 64 * 4;
+    constexpr int FAR_BYTES = KTB + 2 * KT * LDF * 4 + HPB * 4 * 64 * 4;
     constexpr int SMEM = NEAR_BYTES > FAR_BYTES ? NEAR_BYTES : FAR_BYTES;
     constexpr float LOG2E = 1.4426950408889634f;
     __shared__ __align__(16) unsigned char smem[SMEM];
@@ -344,9 +345,9 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
     // hi/lo K tiles and the sub-chunk's evicted values (64 rows) in fp32
     unsigned short* const Kt = reinterpret_cast<unsigned short*>(smem);
     float(*const Vs)[LDF] = reinterpret_cast<float(*)[LDF]>(smem + KTB);
-    // and the post-sub-chunk max M', rescale R and incoming mass Z of each
-    // head's landmarks
-    float(*const MR)[3][64] = reinterpret_cast<float(*)[3][64]>(smem + KTB + 2 * KT * LDF * 4);
+    // and the post-sub-chunk max M', rescale R, incoming mass Z and E's
+    // factor of each head's landmarks
+    float(*const MR)[4][64] = reinterpret_cast<float(*)[4][64]>(smem + KTB + 2 * KT * LDF * 4);
 
     // work item = (sub-chunk, group, head group), dealt to XCDs as ranges of
     // sub-chunks (range_item)
@@ -644,10 +645,10 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
             *reinterpret_cast<u32x2*>(t) = u32x2{s0.hi, s1.hi};
             *reinterpret_cast<u32x2*>(t + L::KH) = u32x2{s0.lo, s1.lo};
         }
-        for (int e = tid; e < HPB * 3 * 64; e += AT_THREADS) {
-            const int hh = e / 192, which = (e / 64) % 3, b = e & 63;
+        for (int e = tid; e < HPB * 4 * 64; e += AT_THREADS) {
+            const int hh = e >> 8, which = (e >> 6) & 3, b = e & 63;
             const int ghh = g * p.H + min(hgrp * HPB + hh, p.H - 1);
-            const float* src = which == 0 ? p.Ms : which == 1 ? p.Rs : p.TZ;
+            const float* src = which == 0 ? p.Ms : which == 1 ? p.Rs : which == 2 ? p.TZ : p.FAC;
             MR[hh][which][b] = src[((int64_t)s * p.nh + ghh) * m + min(b, m - 1)];
         }
         __syncthreads();
@@ -660,7 +661,8 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
             const float* Ms = MR[wave >> 1][0];   // (b < 64: entries past m are not used)
             const float* Rs = MR[wave >> 1][1];
             const float* Zs = MR[wave >> 1][2];
-            const float* Eb = p.E + ghb0 * SUB;   // [b][j] exp(l - M'), 0 where row j evicts nothing
+            const float* Fs = MR[wave >> 1][3];
+            const float* Eb = p.E + ghb0 * SUB;   // [b][j] exp(l - mx), 0 where row j evicts nothing
             const float* Th = p.theta_prev + (int64_t)s * p.theta_prev_stride + (int64_t)gh * m * D;
 
             // f^T = K~ Q^T (log2 units) from the near part's Q^T halves, three
@@ -746,6 +748,7 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
                     dfar += lane_far & (b < m) ? gain * (Rs[b] * Zs[b]) : 0.f;
                 }
             // in-chunk coefficients cf^T = E^T g^T over rows j0 <= j <= i
+            // (E against the post-sub-chunk max is the stored one times fac_b)
             floatx16 cf[2];
 #pragma unroll
             for (int jt = 0; jt < 2; ++jt) {
@@ -760,7 +763,10 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
                         av[t] = b < m ? Eb[(int64_t)b * SUB + j] : 0.f;
                     }
 #pragma unroll
-                    for (int t = 0; t < 16; ++t) cf[jt] = mfma32(av[t], gn[bt][t], cf[jt]);
+                    for (int t = 0; t < 16; ++t) {
+                        const int b = min(bt * 32 + kap(t, hf), 63);
+                        cf[jt] = mfma32(av[t], gn[bt][t] * Fs[b], cf[jt]);
+                    }
                 }
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {

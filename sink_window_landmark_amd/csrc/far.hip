@@ -66,9 +66,12 @@ __device__ __forceinline__ int kswz(int r, int c)
 }
 
 // ---------------------------------------------------------------------------
-// far_score: L[s][gh*m+b][j] = scale <q~_{gh,b}, key evicted by row j>, -inf
-// for rows that do not evict, and per landmark row the local max mx and mass
-// zl = sum_j exp(l_j - mx) of the sub-chunk.  One block per (group, run of
+// far_score: with l_j = scale <q~_{gh,b}, key evicted by row j>, per landmark
+// row the local max mx = max_j l_j and E[s][gh*m+b][j] = exp(l_j - mx) (0
+// for rows that do not evict) and the local mass zl = sum_j E_j of the
+// sub-chunk.  Against the post-sub-chunk max M' every E_j is that times one
+// factor, exp(mx - M') (far_scan), which the accumulator scan and the
+// attention epilogue apply.  One block per (group, run of
 // `rl` consecutive sub-chunks, up to FS_RUN); wave w of the block's NWV takes
 // landmark-row tiles w, w + NWV, ..., and when a group has at most NWV of
 // them its tile's query halves stay in registers for the whole run.  The evicted keys of a
@@ -288,9 +291,11 @@ __global__ __launch_bounds__(fs_threads<D>()) void k_far_score(KParams p)
             for (int v = 0; v < 16; ++v) {
                 const int hb = ht * 32 + fkap(v, hf);
                 float z = 0.f;
-                if (mx[v] != -INFINITY) {
 #pragma unroll
-                    for (int jt = 0; jt < 2; ++jt) z += expf(acc[jt][v] - mx[v]);
+                for (int jt = 0; jt < 2; ++jt) {
+                    // exp(l - mx): 0 for rows that do not evict (and when none does)
+                    acc[jt][v] = mx[v] == -INFINITY ? 0.f : expf(acc[jt][v] - mx[v]);
+                    z += acc[jt][v];
                 }
                 z = sum32(z);
                 if (hb < hm) {
@@ -309,10 +314,11 @@ __global__ __launch_bounds__(fs_threads<D>()) void k_far_score(KParams p)
 
 // ---------------------------------------------------------------------------
 // mz_scan: one thread per landmark row (gh, b), walking the sub-chunks in
-// order on scalars: M'_s, R_s and the incoming mass Z_{s-1} (into TZ[s]),
-// with Z_s = R_s Z_{s-1} + zl_s exp(mx_s - M'_s) (the sub-chunk's mass
-// sum_j E_sj, up to rounding), and the final mass into TZ[S].  Reads the local
-// (mx, zl) that far_score left in Ms/Rs and replaces them with M'_s and R_s.
+// order on scalars: M'_s, R_s, the factor fac_s = exp(mx_s - M'_s) that
+// brings the sub-chunk's E to the post-sub-chunk max, and the incoming mass
+// Z_{s-1} (into TZ[s]), with Z_s = R_s Z_{s-1} + zl_s fac_s, and the final
+// mass into TZ[S].  Reads the local (mx, zl) that far_score left in Ms/Rs
+// and replaces them with M'_s and R_s.
 // ---------------------------------------------------------------------------
 // (M, Z) of a run of sub-chunks: the max and the mass against it; a run
 // with no evictions is (-inf, 0).  Runs a then b combine to the pair of the
@@ -336,11 +342,11 @@ __device__ __forceinline__ MZ mz_merge(MZ a, MZ b)
 // differs from the serial sum only in rounding order).
 constexpr int MZ_PER = PASS_SUBS / 64;
 
-__global__ __launch_bounds__(256) void k_mz_scan(KParams p)
+__device__ __forceinline__ void mz_scan_body(const KParams& p, int64_t bid)
 {
     const int64_t nhm = (int64_t)p.nh * p.m;
     const int lane = threadIdx.x & 63;
-    const int64_t ghb = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t ghb = bid * 4 + (threadIdx.x >> 6);
     if (ghb >= nhm) return;   // (uniform over the wave)
     const int64_t gh = ghb / p.m, b = ghb % p.m;
     float mx[MZ_PER], zl[MZ_PER];
@@ -372,10 +378,12 @@ __global__ __launch_bounds__(256) void k_mz_scan(KParams p)
             const float Mn = fmaxf(M, mx[k]);
             const float R = (Mn == M) ? 1.0f : expf(M - Mn);
             const int64_t at = (int64_t)s * nhm + ghb;
+            const float fac = mx[k] == -INFINITY ? 0.f : expf(mx[k] - Mn);
             p.Ms[at] = Mn;
             p.Rs[at] = R;
             p.TZ[at] = Z;
-            Z = R * Z + (mx[k] == -INFINITY ? 0.f : zl[k] * expf(mx[k] - Mn));
+            p.FAC[at] = fac;
+            Z = R * Z + zl[k] * fac;
             M = Mn;
             // the mass after the last sub-chunk, which a commit stores: a call
             // that resumes from the committed state then carries this value
@@ -385,18 +393,18 @@ __global__ __launch_bounds__(256) void k_mz_scan(KParams p)
 }
 
 // ---------------------------------------------------------------------------
-// dtheta: per (sub-chunk, group): E = exp(l - M'_s) for every landmark row
-// (written over the scores, for the attention epilogue), and
-// TH[s][gh*m+b][t] = sum_j E_bj v_evicted(j)[t] on fp16
-// MFMA with hi/lo splits (C[b][t]; each lane holds rows hf*32 .. +31 of its
-// E row, and k-step st takes rows 32 hf + 8 st .. +7).  E is scaled by 2^12 and the values by the pass's
+// dtheta: per (sub-chunk, group): TH[s][gh*m+b][t] = sum_j E_bj
+// v_evicted(j)[t] with far_score's E (against the sub-chunk's own max, so
+// it needs nothing from the far scan; the accumulator scan applies fac_s)
+// on fp16 MFMA with hi/lo splits (C[b][t]; each lane holds rows hf*32 .. +31
+// of its E row, and k-step st takes rows 32 hf + 8 st .. +7).  E is scaled by 2^12 and the values by the pass's
 // power of two (value_exp) before the split, so that the fp16 remainders of
 // small values stay far above their absolute floor and large values stay in
 // fp16 range; the result is scaled back exactly.  The evicted values are
 // staged in LDS transposed.
 // ---------------------------------------------------------------------------
 template <int DV>
-__global__ __launch_bounds__(256) void k_dtheta(KParams p)
+__device__ __forceinline__ void dtheta_body(const KParams& p, int64_t bid)
 {
     constexpr int NT = DV >= 32 ? DV / 32 : 1;   // 32-column output tiles
     // the evicted values transposed, fp16 hi/lo: row t holds the 64 rows j
@@ -404,7 +412,7 @@ __global__ __launch_bounds__(256) void k_dtheta(KParams p)
     // that do not evict
     constexpr int VH = DV * SUB;
     __shared__ __align__(16) unsigned short vt[2 * VH];
-    const int w = xcd_work_item(blockIdx.x, p.S * p.G);
+    const int w = (int)bid;
     const int s = w % p.S, g = w / p.S;
     const int r0 = s * SUB;
     const int ks = min(SUB, p.T - r0);
@@ -461,23 +469,12 @@ __global__ __launch_bounds__(256) void k_dtheta(KParams p)
         const bool rv = hb < hm;
         float e[32];
         {
-            float* Lr = p.E + (row0 + min(hb, hm - 1)) * SUB + hf * 32;
-            const float Mn = p.Ms[row0 + min(hb, hm - 1)];
+            const float* Lr = p.E + (row0 + min(hb, hm - 1)) * SUB + hf * 32;
 #pragma unroll
             for (int k = 0; k < 32; k += 4) {
                 const float4 x = *reinterpret_cast<const float4*>(Lr + k);
-                e[k] = x.x; e[k + 1] = x.y; e[k + 2] = x.z; e[k + 3] = x.w;
-            }
-#pragma unroll
-            for (int k = 0; k < 32; ++k) e[k] = (rv && e[k] != -INFINITY) ? expf(e[k] - Mn) : 0.f;
-            // E replaces the scores in the plane: the attention epilogue reads it
-            if (rv) {
-#pragma unroll
-                for (int k = 0; k < 32; k += 4) {
-                    float4 pe;
-                    pe.x = e[k]; pe.y = e[k + 1]; pe.z = e[k + 2]; pe.w = e[k + 3];
-                    *reinterpret_cast<float4*>(Lr + k) = pe;
-                }
+                e[k] = rv ? x.x : 0.f; e[k + 1] = rv ? x.y : 0.f;
+                e[k + 2] = rv ? x.z : 0.f; e[k + 3] = rv ? x.w : 0.f;
             }
         }
         // E * 2^12 as fp16 halves: k-step st takes rows j = 32 hf + 8 st + e
@@ -560,28 +557,33 @@ hipError_t launch_far_score(const KParams& p, hipStream_t st)
     return hipGetLastError();
 }
 
-hipError_t launch_far_scan(const KParams& p, hipStream_t st)
+// The far scan (one wave per landmark row, four per block) and the
+// accumulator increments (one block per (sub-chunk, group), XCD-ordered) in
+// one launch: the increments take far_score's E as it is, so neither waits
+// for the other.
+template <int DV>
+__global__ __launch_bounds__(256) void k_scan_dtheta(KParams p, int nmz)
 {
-    const int64_t nhm = (int64_t)p.nh * p.m;
-    hipLaunchKernelGGL(k_mz_scan, dim3((unsigned)((nhm + 3) / 4)), dim3(256), 0, st, p);
-    return hipGetLastError();
+    if ((int)blockIdx.x < nmz) mz_scan_body(p, blockIdx.x);
+    else dtheta_body<DV>(p, xcd_work_item((int)blockIdx.x - nmz, p.S * p.G));
 }
 
 template <int DV>
-static void launch_dt(const KParams& p, hipStream_t st)
+static void launch_sd(const KParams& p, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_dtheta<DV>, dim3(p.S * p.G), dim3(256), 0, st, p);
+    const int nmz = (int)(((int64_t)p.nh * p.m + 3) / 4);
+    hipLaunchKernelGGL(k_scan_dtheta<DV>, dim3(nmz + p.S * p.G), dim3(256), 0, st, p, nmz);
 }
 
-hipError_t launch_dtheta(const KParams& p, hipStream_t st)
+hipError_t launch_scan_dtheta(const KParams& p, hipStream_t st)
 {
     switch (p.dv) {
-    case 8: launch_dt<8>(p, st); break;
-    case 16: launch_dt<16>(p, st); break;
-    case 32: launch_dt<32>(p, st); break;
-    case 64: launch_dt<64>(p, st); break;
-    case 128: launch_dt<128>(p, st); break;
-    case 256: launch_dt<256>(p, st); break;
+    case 8: launch_sd<8>(p, st); break;
+    case 16: launch_sd<16>(p, st); break;
+    case 32: launch_sd<32>(p, st); break;
+    case 64: launch_sd<64>(p, st); break;
+    case 128: launch_sd<128>(p, st); break;
+    case 256: launch_sd<256>(p, st); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -27,7 +27,9 @@ __host__ __device__ inline int64_t theta_blocks(const KParams& p)
 
 // theta_scan, block `bid` of theta_blocks(p): one thread per (gh, b, t),
 // walking the sub-chunks in order: TH[s] <- Theta (the value before
-// sub-chunk s, which the readout of s uses), Theta <- R_s Theta + dTheta_s.
+// sub-chunk s, which the readout of s uses), Theta <- R_s Theta +
+// fac_s dTheta_s (dtheta's increment is against the sub-chunk's own max;
+// fac_s brings it to the post-sub-chunk max).
 // With `commit` the final Theta, M and Z go to the state (o1b_far_commit:
 // M <- M', Z <- the mass after the rows).
 //
@@ -52,24 +54,28 @@ __device__ __forceinline__ void theta_scan_body(const KParams& p, bool commit, i
     const int64_t stride = nhm * p.dv;
     float th = p.theta[idx], tc = 0.f;
     for (int s0 = 0; s0 < p.S; s0 += SCAN_AHEAD) {
-        float dth[SCAN_AHEAD], rs[SCAN_AHEAD];
+        float dth[SCAN_AHEAD], rs[SCAN_AHEAD], fs[SCAN_AHEAD];
 #pragma unroll
         for (int k = 0; k < SCAN_AHEAD; ++k) {
             const int s = min(s0 + k, p.S - 1);
             dth[k] = p.TH[(int64_t)s * stride + idx];
             rs[k] = p.Rs[(int64_t)s * nhm + ghb];
+            fs[k] = p.FAC[(int64_t)s * nhm + ghb];
         }
 #pragma unroll
         for (int k = 0; k < SCAN_AHEAD; ++k) {
             const int s = s0 + k;
             if (s < p.S) {
                 p.TH[(int64_t)s * stride + idx] = th;
-                // (th + tc) R + d, with the errors of R th and of the sum kept
+                // (th + tc) R + fac d, with the errors of both products and
+                // of the sum kept
                 const float pr = rs[k] * th;
                 const float pe = fmaf(rs[k], th, -pr);
+                const float pd = fs[k] * dth[k];
+                const float pde = fmaf(fs[k], dth[k], -pd);
                 float sm, se;
-                two_sum(pr, dth[k], sm, se);
-                const float lo = fmaf(rs[k], tc, pe + se);
+                two_sum(pr, pd, sm, se);
+                const float lo = fmaf(rs[k], tc, (pe + pde) + se);
                 two_sum(sm, lo, th, tc);
             }
         }

@@ -42,7 +42,8 @@ struct KParams {
     int T;   // rows (<= PASS_SUBS * SUB)
     int S;   // sub-chunks, ceil(T / SUB)
     // scratch planes (see scratch_layout)
-    float* E;    // [S][nh*m][SUB]  scores of the evicted keys (-inf: no eviction), then exp against the post-sub-chunk max
+    float* E;    // [S][nh*m][SUB]  exp(l - mx_s) of the evicted keys' scores against the sub-chunk's own max (0: no eviction)
+    float* FAC;  // [S][nh*m]       exp(mx_s - M'_s): E's factor to the post-sub-chunk max
     float* Ms;   // [S][nh*m]       local max of the scores, then the post-sub-chunk max
     float* Rs;   // [S][nh*m]       local mass of the scores, then the rescale of the old mass
     float* TZ;   // [S+1][nh*m]     mass before each sub-chunk, then after the last
@@ -223,8 +224,8 @@ __host__ __device__ inline int fs_blocks_per_group(int S, int G)
 // Launchers (each returns the launch's hipGetLastError).
 hipError_t launch_init(const KParams& p, const uint32_t* windows, hipStream_t st);
 hipError_t launch_far_score(const KParams& p, hipStream_t st);
-hipError_t launch_far_scan(const KParams& p, hipStream_t st);
-hipError_t launch_dtheta(const KParams& p, hipStream_t st);
+// the far scan and the accumulator increments in one launch
+hipError_t launch_scan_dtheta(const KParams& p, hipStream_t st);
 // the accumulator scan (commit) and the key tiles in one launch (either may be off)
 hipError_t launch_theta_kv(const KParams& p, bool theta, bool kv, hipStream_t st);
 hipError_t launch_attend(const KParams& p, hipStream_t st);
