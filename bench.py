@@ -10,9 +10,11 @@ in HBM when the timed region starts.
 
 Prints one JSON line: prefill rows/s (whole job, one GPU), the near
 kernel's achieved TFLOP/s against its matrix-core roofline (timed live with
-HIP events around its launches): the near products run as three fp16
-products of hi/lo splits (2.5 PFLOP/s / 3 of fp32-accurate work), the far
-readout's on fp32 MFMA (157.3 TFLOP/s), the decode path's us/token after the
+HIP events around its launches): the near products, the far readout's
+landmark scores and its far numerator run as three fp16 products of hi/lo
+splits (2.5 PFLOP/s / 3 of fp32-accurate work), the far readout's u and
+in-chunk coefficients on fp32 MFMA (157.3 TFLOP/s), the decode path's
+us/token after the
 32768-row prompt, the per-sub-chunk API's rate, an exact-attention timing
 for context, and the CPU oracle timed on a bounded sample.
 
@@ -55,7 +57,9 @@ def far_flops(cfg, T, len0=0, nfar0=0, split=False):
     updates (2 d m H and 2 dv m H per evicted key and group), and per row and
     head with a non-empty far field: f (2 m d), u (2 m m), N (2 m dv) and the
     in-chunk terms (2 n (m + dv), n = rows of the sub-chunk evicted so far).
-    With split=True the readout figure comes as (f part, the rest)."""
+    With split=True the readout figure comes as (the part on fp16 splits:
+    f, N and the in-chunk value terms 2 n dv; the part on fp32 MFMA: u and
+    the in-chunk coefficients 2 n m)."""
     m, d, dv, H = cfg.m, cfg.d, cfg.dv, cfg.H
     fe = fc = ro = rf = 0
     for g in range(cfg.G):
@@ -71,7 +75,7 @@ def far_flops(cfg, T, len0=0, nfar0=0, split=False):
                 n_in = max(0, i - max(j0, 0) + 1) if i >= j0 else 0
                 if nf + n_in > 0:
                     ro += H * (2 * m * d + 2 * m * m + 2 * m * dv + 2 * n_in * (m + dv))
-                    rf += H * 2 * m * d
+                    rf += H * (2 * m * d + 2 * m * dv + 2 * n_in * dv)
             tot = ln + k
             if tot > w:
                 nf += tot - w
@@ -225,10 +229,11 @@ def run_gpu(args, cfg):
     # the attend kernel computes the near part and the far readout
     near_flops_per_launch = (near_step_flops + ro) / launches_per_step
     achieved = near_flops_per_launch / (near_launch_ms * 1e-3) / 1e12
-    # the kernel's peak for its own mix: the near products and the landmark
-    # scores at the split rate, the rest of the far readout at the fp32 rate
-    _, _, (ro_f, ro_rest) = far_flops(cfg, T, split=True)
-    t_peak = ((near_step_flops + ro_f) / MFMA_SPLIT_PEAK_TFLOPS + ro_rest / MFMA_FP32_PEAK_TFLOPS) / launches_per_step
+    # the kernel's peak for its own mix: the near products and the readout's
+    # split parts at the split rate, its u and in-chunk coefficients at the
+    # fp32 rate
+    _, _, (ro_s, ro_32) = far_flops(cfg, T, split=True)
+    t_peak = ((near_step_flops + ro_s) / MFMA_SPLIT_PEAK_TFLOPS + ro_32 / MFMA_FP32_PEAK_TFLOPS) / launches_per_step
     peak = near_flops_per_launch / t_peak
     near_bytes_per_launch = attend_bytes(cfg, T) / launches_per_step
     step_flops = near_step_flops + fe + fc + ro
@@ -656,7 +661,8 @@ def main():
         "dtype": "f32",
         "mfma_dtype": "f16 hi/lo splits (three products per fp32-accurate product, f32 accumulation) "
                       "for the near part, the landmark and evicted-key scores and the accumulator "
-                      "increments; f32 for the far readout's u, accumulator and in-chunk products",
+                      "increments, the far readout's landmark scores and far numerator; f32 for the far "
+                      "readout's u and in-chunk coefficients",
         "data": "synthetic",
         "config": {"workload": "max-window layer: 4 KV groups x 4 query heads, d=dv=128, 4 sinks, "
                                "w=2048, m=64 landmarks, 32768-row prompt from the empty state as "
@@ -665,9 +671,9 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "k_attend<128,2> (near attention + far readout)",
                      "achieved": near["achieved_tflops"], "peak": near["peak_tflops"],
                      "unit": "TFLOP/s", "frac": near["achieved_tflops"] / near["peak_tflops"],
-                     "peak_basis": "near flops and the far readout's landmark scores at 2500/3 TFLOP/s "
-                                   "(fp16 MFMA, three split products per fp32-accurate product), the rest "
-                                   "of the far readout at 157.3 TFLOP/s (fp32 MFMA)",
+                     "peak_basis": "near flops and the far readout's landmark scores and far numerator "
+                                   "at 2500/3 TFLOP/s (fp16 MFMA, three split products per fp32-accurate "
+                                   "product), its u and in-chunk coefficients at 157.3 TFLOP/s (fp32 MFMA)",
                      "near_flops_per_launch": near["near_flops_per_launch"],
                      "readout_flops_per_launch": near["readout_flops_per_launch"],
                      "traffic": None,

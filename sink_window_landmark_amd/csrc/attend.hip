@@ -63,10 +63,12 @@
 // XOR-swizzled so that the MFMA operand reads are free of bank conflicts;
 // attention then stages a tile with plain global-to-LDS copies
 // (global_load_lds_dwordx4), with no arithmetic and no registers.
-//   The far epilogue runs on v_mfma_f32_32x32x2f32 with the same shapes:
-//   landmarks (a or b) or in-chunk rows j take the place of keys, and a
-//   C-layout accumulator tile is always directly the B operand of the next
-//   product.
+//   The far epilogue chains more products in the same shapes: landmarks
+//   (a or b) or in-chunk rows j take the place of keys, and a C-layout
+//   accumulator tile is always directly the B operand of the next product.
+//   The landmark scores and the far numerator run on split fp16 (the
+//   numerator's operands scaled by powers of two, far_numerator), u and the
+//   in-chunk coefficients on v_mfma_f32_32x32x2f32.
 // Softmax runs online in base 2 (q is pre-scaled by scale*log2 e).
 #include "swl_internal.h"
 #include "lanes.h"
@@ -215,14 +217,149 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base)
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 
-// O^T[blk] += A_row^T B for one fp32 MFMA step of the epilogue: `row` is the
-// value row of this lane's k index (value column 32 blk + n is A for block
-// blk).
-template <int D, int NB>
-__device__ __forceinline__ void pv_step(floatx16 (&O)[NB], const float* row, int ln, float b)
+// n floats from p (the same p in every lane of the wave) read by 32-bit
+// element index through a buffer resource: one VGPR offset per load in place
+// of 64-bit address arithmetic.  Word 3 of the resource is the raw 32-bit
+// format of gfx9 targets.  Callers keep their indexes inside [0, n).
+struct FView {
+    __amdgpu_buffer_rsrc_t r;
+    __device__ __forceinline__ FView(const float* p, int n)
+    {
+        // (readfirstlane returns a signed int: each half goes through
+        // unsigned, so that the low half does not sign-extend into the high)
+        const uint64_t a = reinterpret_cast<uint64_t>(p);
+        const uint64_t lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)a);
+        const uint64_t hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+        r = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(hi << 32 | lo), (short)0, n * 4, 0x00020000);
+    }
+    __device__ __forceinline__ float operator[](int i) const
+    {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, i * 4, 0, 0));
+    }
+};
+
+// Split fp16 halves of 8 values times 2^ex (the scaling is exact): an A
+// operand, or the B operand of k-step q of a C-layout tile x (its values
+// 8q .. 8q+7 in this lane).
+__device__ __forceinline__ void split8(const float (&a)[8], int ex, u32x4& hi, u32x4& lo)
 {
+    unsigned h[4], l[4];
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk) O[blk] = mfma32(row[min(blk * 32 + ln, D - 1)], b, O[blk]);
+    for (int k = 0; k < 4; ++k) {
+        const Split<false> s(ldexpf(a[2 * k], ex), ldexpf(a[2 * k + 1], ex));
+        h[k] = s.hi;
+        l[k] = s.lo;
+    }
+    hi = u32x4{h[0], h[1], h[2], h[3]};
+    lo = u32x4{l[0], l[1], l[2], l[3]};
+}
+__device__ __forceinline__ void split_b(const floatx16& x, int q, int ex, u32x4& hi, u32x4& lo)
+{
+    float a[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = x[8 * q + e];
+    split8(a, ex, hi, lo);
+}
+
+// The far numerator, O^T += Theta^T (g R)^T + V_ev^T cf^T, on fp16 matrix
+// cores with three split products per k-step as in the near part.  Every
+// operand enters its split times a power of two that puts it in fp16 range
+// with its remainder far above fp16's floor: the gains and the in-chunk
+// coefficients per query by their largest magnitude, the evicted values by
+// the pass's value exponent, Theta per 32-column block by that block's
+// largest magnitude (taken from the loaded values).  Each chain accumulates
+// on its own and is scaled back (exactly) as it is added to O.  K-step st of
+// tile bt = st / 2 takes, in this lane, rows 32 bt + 16 (st % 2) + 4 hf +
+// 8 (e / 4) + e % 4 (e = 0..7): the C-layout rows of the lane's values
+// 8 (st % 2) .. + 7, so that the gains and coefficients are B operands as
+// they stand.  Theta's loads for a block go out as soon as the block before
+// it is split (the first block's before the evicted-value chain, whose
+// operands come from LDS).
+template <int D, int NB, int MT, int LDF>
+__device__ __forceinline__ void far_numerator(floatx16 (&O)[NB], const floatx16 (&gn)[MT], const floatx16 (&cf)[2],
+                                              const FView& Th, const float (*Vs)[LDF], int vexp, int m, int ln,
+                                              int hf)
+{
+    constexpr int ST = 2 * MT;   // k-steps of the Theta chain
+    auto krow = [&](int st, int e) { return (st >> 1) * 32 + (st & 1) * 16 + 4 * hf + (e >> 2) * 8 + (e & 3); };
+    float th[ST][8];
+    auto load = [&](int blk) {
+        const int col = min(blk * 32 + ln, D - 1);
+#pragma unroll
+        for (int st = 0; st < ST; ++st)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) th[st][e] = Th[min(krow(st, e), m - 1) * D + col];   // rows >= m: 0 below
+    };
+
+    float gmax = 0.f, cmax = 0.f;
+#pragma unroll
+    for (int bt = 0; bt < MT; ++bt)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) gmax = fmaxf(gmax, fabsf(gn[bt][t]));
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) cmax = fmaxf(cmax, fabsf(cf[jt][t]));
+    gmax = pair_max<5>(gmax);   // a query's two lane halves
+    cmax = pair_max<5>(cmax);
+    const int eg = value_exp_of(gmax), ecf = value_exp_of(cmax);
+
+    if (__any(cmax > 0.f)) {
+        u32x4 bh[4], bl[4];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) split_b(cf[st >> 1], st & 1, ecf, bh[st], bl[st]);
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+            const int col = min(blk * 32 + ln, D - 1);
+            floatx16 acc;
+            zero16(acc);
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                float a[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a[e] = Vs[krow(st, e)][col];
+                u32x4 ah, al;
+                split8(a, vexp, ah, al);
+                acc = mfma16(ah, bh[st], acc);
+                acc = mfma16(ah, bl[st], acc);
+                acc = mfma16(al, bh[st], acc);
+            }
+#pragma unroll
+            for (int v = 0; v < 16; ++v) O[blk][v] += ldexpf(acc[v], -(vexp + ecf));
+        }
+    }
+    if (__any(gmax > 0.f)) {
+        load(0);
+        u32x4 bh[ST], bl[ST];
+#pragma unroll
+        for (int st = 0; st < ST; ++st) split_b(gn[st >> 1], st & 1, eg, bh[st], bl[st]);
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+            float tm = 0.f;
+#pragma unroll
+            for (int st = 0; st < ST; ++st)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    if (krow(st, e) >= m) th[st][e] = 0.f;
+                    tm = fmaxf(tm, fabsf(th[st][e]));
+                }
+            const int et = __builtin_amdgcn_readfirstlane(value_exp_of(wmax(tm)));
+            u32x4 ah[ST], al[ST];
+#pragma unroll
+            for (int st = 0; st < ST; ++st) split8(th[st], et, ah[st], al[st]);
+            if (blk + 1 < NB) load(blk + 1);
+            floatx16 acc;
+            zero16(acc);
+#pragma unroll
+            for (int st = 0; st < ST; ++st) {
+                acc = mfma16(ah[st], bh[st], acc);
+                acc = mfma16(ah[st], bl[st], acc);
+                acc = mfma16(al[st], bh[st], acc);
+            }
+#pragma unroll
+            for (int v = 0; v < 16; ++v) O[blk][v] += ldexpf(acc[v], -(et + eg));
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -663,7 +800,7 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
             const float* Zs = MR[wave >> 1][2];
             const float* Fs = MR[wave >> 1][3];
             const float* Eb = p.E + ghb0 * SUB;   // [b][j] exp(l - mx), 0 where row j evicts nothing
-            const float* Th = p.theta_prev + (int64_t)s * p.theta_prev_stride + (int64_t)gh * m * D;
+            const FView Th(p.theta_prev + (int64_t)s * p.theta_prev_stride + (int64_t)gh * m * D, m * D);
 
             // f^T = K~ Q^T (log2 units) from the near part's Q^T halves, three
             // split products per k-step; e = exp2(f - fmax)
@@ -794,23 +931,14 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
                 for (int v = 0; v < 16; ++v) O[b][v] *= wo;
             den = den * wn + dfar;
 #pragma unroll
-            for (int bt = 0; bt < MT; ++bt) {
+            for (int bt = 0; bt < MT; ++bt)
 #pragma unroll
                 for (int t = 0; t < 16; ++t) {
                     const int b = bt * 32 + kap(t, hf);
                     const float r = b < m ? Rs[b] : 0.f;
                     gn[bt][t] *= r;
                 }
-#pragma unroll
-                for (int t = 0; t < 16; ++t) {
-                    const int b = min(bt * 32 + kap(t, hf), m - 1);   // gn is 0 for b >= m
-                    pv_step<D, NB>(O, Th + (int64_t)b * D, ln, gn[bt][t]);
-                }
-            }
-#pragma unroll
-            for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-                for (int t = 0; t < 16; ++t) pv_step<D, NB>(O, &Vs[jt * 32 + kap(t, hf)][0], ln, cf[jt][t]);
+            far_numerator<D, NB, MT, LDF>(O, gn, cf, Th, Vs, vexp, m, ln, hf);
         }
     }
 
