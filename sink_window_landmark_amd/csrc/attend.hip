@@ -764,29 +764,67 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
         __syncthreads();  // every wave is done with the key tiles
         // landmark keys of the group -> Ks rows 0..m-1 (zero above m);
         // evicted values of the sub-chunk -> Vs rows 0..63 (zero where none)
-        for (int e = tid; e < 2 * KT * (D / 4); e += AT_THREADS) {
-            const int row = e / (D / 4), c4 = (e % (D / 4)) * 4;
-            float4 vx = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (row >= jlo && row < ks)
-                vx = *reinterpret_cast<const float4*>(val_row(p, c, g, c.len0 + r0 + row - c.wg) + c4);
-            *reinterpret_cast<float4*>(&Vs[row][c4]) = vx;
+        // each kind's loads all go out before its stores (a compile-time
+        // count per thread): a few memory round trips, not one per element
+        {
+            constexpr int NE = 2 * KT * (D / 4), NU = (NE + AT_THREADS - 1) / AT_THREADS;
+            float4 vx[NU];
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                const int e = tid + u * AT_THREADS;
+                const int row = min(e / (D / 4), 2 * KT - 1), c4 = (e % (D / 4)) * 4;
+                const int rr = min(max(row, jlo), ks - 1);   // a row that evicts (loads take no lane condition)
+                vx[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (jlo < ks) vx[u] = *reinterpret_cast<const float4*>(val_row(p, c, g, c.len0 + r0 + rr - c.wg) + c4);
+            }
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                const int e = tid + u * AT_THREADS;
+                const int row = e / (D / 4), c4 = (e % (D / 4)) * 4;
+                const bool ev = row >= jlo && row < ks;
+                if (e < NE) *reinterpret_cast<float4*>(&Vs[row][c4]) = ev ? vx[u] : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
         }
         // landmark row a = 32 at + r of K tile at, columns past D zero
-        for (int e = tid; e < 2 * KT * (KD / 4); e += AT_THREADS) {
-            const int row = e / (KD / 4), c4 = (e % (KD / 4)) * 4;
-            const float4 kx = *reinterpret_cast<const float4*>(p.k_tilde + ((int64_t)g * m + min(row, m - 1)) * D + min(c4, D - 4));
-            const bool live = (row < m) & (c4 < D);
-            const Split<true> s0(live ? kx.x : 0.f, live ? kx.y : 0.f), s1(live ? kx.z : 0.f, live ? kx.w : 0.f);
-            const int r = row & 31;
-            unsigned short* t = Kt + (row >> 5) * 2 * L::KH + r * KD + kchunk<D>(r, c4 >> 3) * 8 + (c4 & 4);
-            *reinterpret_cast<u32x2*>(t) = u32x2{s0.hi, s1.hi};
-            *reinterpret_cast<u32x2*>(t + L::KH) = u32x2{s0.lo, s1.lo};
+        {
+            constexpr int NE = 2 * KT * (KD / 4), NU = (NE + AT_THREADS - 1) / AT_THREADS;
+            float4 kx[NU];
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                const int e = tid + u * AT_THREADS;
+                const int row = min(e / (KD / 4), 2 * KT - 1), c4 = (e % (KD / 4)) * 4;
+                kx[u] = *reinterpret_cast<const float4*>(p.k_tilde + ((int64_t)g * m + min(row, m - 1)) * D + min(c4, D - 4));
+            }
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                const int e = tid + u * AT_THREADS;
+                const int row = e / (KD / 4), c4 = (e % (KD / 4)) * 4;
+                const bool live = (row < m) & (c4 < D);
+                const Split<true> s0(live ? kx[u].x : 0.f, live ? kx[u].y : 0.f), s1(live ? kx[u].z : 0.f, live ? kx[u].w : 0.f);
+                const int r = row & 31;
+                unsigned short* t = Kt + (row >> 5) * 2 * L::KH + r * KD + kchunk<D>(r, c4 >> 3) * 8 + (c4 & 4);
+                if (e < NE) {
+                    *reinterpret_cast<u32x2*>(t) = u32x2{s0.hi, s1.hi};
+                    *reinterpret_cast<u32x2*>(t + L::KH) = u32x2{s0.lo, s1.lo};
+                }
+            }
         }
-        for (int e = tid; e < HPB * 4 * 64; e += AT_THREADS) {
-            const int hh = e >> 8, which = (e >> 6) & 3, b = e & 63;
-            const int ghh = g * p.H + min(hgrp * HPB + hh, p.H - 1);
-            const float* src = which == 0 ? p.Ms : which == 1 ? p.Rs : which == 2 ? p.TZ : p.FAC;
-            MR[hh][which][b] = src[((int64_t)s * p.nh + ghh) * m + min(b, m - 1)];
+        {
+            constexpr int NE = HPB * 4 * 64, NU = (NE + AT_THREADS - 1) / AT_THREADS;
+            float x[NU];
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                const int e = min(tid + u * AT_THREADS, NE - 1);
+                const int hh = e >> 8, which = (e >> 6) & 3, b = e & 63;
+                const int ghh = g * p.H + min(hgrp * HPB + hh, p.H - 1);
+                const float* src = which == 0 ? p.Ms : which == 1 ? p.Rs : which == 2 ? p.TZ : p.FAC;
+                x[u] = src[((int64_t)s * p.nh + ghh) * m + min(b, m - 1)];
+            }
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                const int e = tid + u * AT_THREADS;
+                if (e < NE) MR[e >> 8][(e >> 6) & 3][e & 63] = x[u];
+            }
         }
         __syncthreads();
 
@@ -864,7 +902,8 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int b = bt * 32 + kap(v, hf);
-                    mb[bt][v] = b < m ? Ms[b] * LOG2E : -INFINITY;
+                    mb[bt][v] = Ms[b] * LOG2E;   // (rows past m hold row m-1: read, then select)
+                    if (b >= m) mb[bt][v] = -INFINITY;
                     mmax = fmaxf(mmax, mb[bt][v]);
                 }
             mmax = pair_max<5>(mmax);
@@ -880,9 +919,15 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
                     const int b = bt * 32 + kap(v, hf);
                     float u = gn[bt][v];
                     if (p.rect) u = fmaxf(u, 0.f);
-                    const float gain = lane_far & (b < m) ? u * ex2(fmax + mb[bt][v] - cexp) : 0.f;
+                    float gain = u * ex2(fmax + mb[bt][v] - cexp);
+                    float mass = gain * (Rs[b] * Zs[b]);
+                    // computed in every lane, then selected: otherwise the
+                    // compiler moves the work under the lane condition, a
+                    // branch and an LDS wait per element
+                    asm volatile("" : "+v"(gain), "+v"(mass));
+                    if (!lane_far || b >= m) gain = mass = 0.f;
                     gn[bt][v] = gain;
-                    dfar += lane_far & (b < m) ? gain * (Rs[b] * Zs[b]) : 0.f;
+                    dfar += mass;
                 }
             // in-chunk coefficients cf^T = E^T g^T over rows j0 <= j <= i
             // (E against the post-sub-chunk max is the stored one times fac_b)
@@ -935,8 +980,8 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
 #pragma unroll
                 for (int t = 0; t < 16; ++t) {
                     const int b = bt * 32 + kap(t, hf);
-                    const float r = b < m ? Rs[b] : 0.f;
-                    gn[bt][t] *= r;
+                    const float rb = Rs[b];
+                    gn[bt][t] *= b < m ? rb : 0.f;
                 }
             far_numerator<D, NB, MT, LDF>(O, gn, cf, Th, Vs, vexp, m, ln, hf);
         }
