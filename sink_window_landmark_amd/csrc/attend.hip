@@ -447,6 +447,7 @@ __global__ __launch_bounds__(256) void k_theta_kv(KParams p, int nth)
 // The split serves launches with few blocks (a single sub-chunk, short
 // prompts), where one block per sub-chunk would leave most CUs idle.
 constexpr int AT_FULL = 0, AT_PART = 1, AT_MERGE = 2;
+constexpr int AT_MAX_SPLITS = 16;   // splits of one work item's key tiles at most
 
 // Block shape per mode: the merge takes one head per block (two waves, each
 // on a SIMD of its own), so that the few merge blocks of a small call spread
@@ -527,7 +528,7 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
     // thread): the running reference, the mass, then O^T.  AT_PART stores
     // this lane's state after its tiles; AT_MERGE combines the p.nsp states
     // of its lane against their largest reference, before the query halves
-    // take their registers (two records in flight at a time).
+    // take their registers (four records in flight at a time).
     constexpr int PF4 = (NB * 16 + 2 + 3) / 4;
     if constexpr (MODE == AT_MERGE) {
         // this head's records among those of the split blocks' item (their
@@ -536,8 +537,14 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
         const int wp = s + p.S * (g + p.G * (h / PH));
         const int tp = (h % PH) * 128 + tid;
         const float4* pp = reinterpret_cast<const float4*>(p.apart) + ((int64_t)wp * p.nsp * PT + tp) * PF4;
-        for (int k = 0; k < p.nsp; ++k) mrun = fmaxf(mrun, pp[(int64_t)k * PT * PF4].x);
-#pragma unroll 2
+        // the largest reference first, every record's head in flight at once
+        // (splits past nsp read the last record again)
+        float xm[AT_MAX_SPLITS];
+#pragma unroll
+        for (int k = 0; k < AT_MAX_SPLITS; ++k) xm[k] = pp[(int64_t)min(k, p.nsp - 1) * PT * PF4].x;
+#pragma unroll
+        for (int k = 0; k < AT_MAX_SPLITS; ++k) mrun = fmaxf(mrun, xm[k]);
+#pragma unroll 4
         for (int k = 0; k < p.nsp; ++k) {
             const float4* pk = pp + (int64_t)k * PT * PF4;
             float4 r[PF4];
@@ -1021,7 +1028,7 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
 static int attend_splits(const KParams& p, int items)
 {
     const int max_tiles = (p.ns + KT - 1) / KT + (p.W + SUB + KT - 1) / KT + 1;
-    int n = min(16, 256 / max(items, 1));
+    int n = min(AT_MAX_SPLITS, 256 / max(items, 1));
     n = min(n, max_tiles / 4);
     return max(n, 1);
 }
