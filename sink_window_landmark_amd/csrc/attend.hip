@@ -613,8 +613,14 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
         const bool relevant = wave_rows && (sink || (tb <= w_hi && tb + KT - 1 >= w_lo));
         if (!relevant) continue;
 
+        // the score accumulator starts at -bias, the offset of this tile's
+        // weights against the reference as it stands, so the scores come out
+        // biased and the weights need no subtraction of their own (a tile
+        // that raises the reference shifts them once more, below)
+        const float bias = (mrun == -INFINITY ? 0.f : mrun) - P_EXP;
         floatx16 sh, sx;
-        zero16(sh);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sh[v] = -bias;
         zero16(sx);
         const unsigned short* kr = tiles + buf * BUF + ln * KD;
         // a wave in an MFMA stretch gets issue priority over its SIMD partner
@@ -691,8 +697,9 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
         tmax = pair_max<5>(tmax);   // with the lane 32 away (permlane swap, no LDS)
         // raise the reference (and rescale the running sums) only when some
         // query's score exceeds it by more than TAU
-        if (__any(tmax > mrun + TAU)) {
-            const float mnew = fmaxf(mrun, tmax);
+        // (tmax is biased: the score maximum is tmax + bias)
+        if (__any(tmax + bias > mrun + TAU)) {
+            const float mnew = fmaxf(mrun, tmax + bias);
             const float alpha = mnew == -INFINITY ? 1.f : ex2(mrun - mnew);
             lsum *= alpha;
 #pragma unroll
@@ -700,12 +707,15 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
 #pragma unroll
                 for (int v = 0; v < 16; ++v) O[b][v] *= alpha;
             mrun = mnew;
+            // to the raised reference (a lane still without one keeps its bias)
+            const float shift = ((mrun == -INFINITY ? 0.f : mrun) - P_EXP) - bias;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) sacc[v] -= shift;
         }
-        const float msub = (mrun == -INFINITY ? 0.f : mrun) - P_EXP;
         float ts = 0.f;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const float pv = ex2(sacc[v] - msub);
+            const float pv = ex2(sacc[v]);
             sacc[v] = pv;
             ts += pv;
         }
