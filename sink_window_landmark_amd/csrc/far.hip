@@ -158,9 +158,11 @@ __global__ __launch_bounds__(fs_threads<D>()) void k_far_score(KParams p)
             }
         }
     };
-    // landmark query halves of tile ht: q~[hb][16 st + 8 hf + e]
+    // landmark query halves of tile ht: q~[hb][16 st + 8 hf + e] times
+    // scale * log2 e, so that the scores come out in base 2
     fu32x4 qah[NS], qal[NS];
     auto load_q = [&](int ht) {
+        const float qs = p.scale * 1.4426950408889634f;
         const int hb_a = ht * 32 + ln;   // A row of this lane
         const float* qr = p.q_tilde + ((int64_t)g * hm + min(hb_a, hm - 1)) * D;
 #pragma unroll
@@ -172,10 +174,10 @@ __global__ __launch_bounds__(fs_threads<D>()) void k_far_score(KParams p)
                 y = *reinterpret_cast<const float4*>(qr + d0 + 4);
             }
             unsigned h[4], l[4];
-            fsplit<true>(x.x, x.y, h[0], l[0]);
-            fsplit<true>(x.z, x.w, h[1], l[1]);
-            fsplit<true>(y.x, y.y, h[2], l[2]);
-            fsplit<true>(y.z, y.w, h[3], l[3]);
+            fsplit<true>(x.x * qs, x.y * qs, h[0], l[0]);
+            fsplit<true>(x.z * qs, x.w * qs, h[1], l[1]);
+            fsplit<true>(y.x * qs, y.y * qs, h[2], l[2]);
+            fsplit<true>(y.z * qs, y.w * qs, h[3], l[3]);
             qah[st] = fu32x4{h[0], h[1], h[2], h[3]};
             qal[st] = fu32x4{l[0], l[1], l[2], l[3]};
         }
@@ -273,7 +275,9 @@ __global__ __launch_bounds__(fs_threads<D>()) void k_far_score(KParams p)
             for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[jt][v] = fmaf(sx[jt][v], F_LO_DOWN, sh[jt][v]);
-            // lane holds rows hb = ht*32 + kappa(v, hf), columns j = jt*32 + ln
+            // lane holds rows hb = ht*32 + kappa(v, hf), columns j = jt*32 + ln;
+            // scores and their max in base 2 (the max is stored in natural
+            // units, as the state keeps M)
             float mx[16];
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
@@ -281,7 +285,7 @@ __global__ __launch_bounds__(fs_threads<D>()) void k_far_score(KParams p)
 #pragma unroll
                 for (int jt = 0; jt < 2; ++jt) {
                     const int j = jt * 32 + ln;
-                    const float l = (j >= jlo && j < ks) ? acc[jt][v] * p.scale : -INFINITY;
+                    const float l = (j >= jlo && j < ks) ? acc[jt][v] : -INFINITY;
                     acc[jt][v] = l;
                     m2 = fmaxf(m2, l);
                 }
@@ -293,8 +297,9 @@ __global__ __launch_bounds__(fs_threads<D>()) void k_far_score(KParams p)
                 float z = 0.f;
 #pragma unroll
                 for (int jt = 0; jt < 2; ++jt) {
-                    // exp(l - mx): 0 for rows that do not evict (and when none does)
-                    acc[jt][v] = mx[v] == -INFINITY ? 0.f : expf(acc[jt][v] - mx[v]);
+                    // exp(l - mx) as 2^(l2 - mx2): 0 for rows that do not evict (and
+                    // when none does; results below 2^-126 flush to 0)
+                    acc[jt][v] = mx[v] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(acc[jt][v] - mx[v]);
                     z += acc[jt][v];
                 }
                 z = sum32(z);
@@ -302,7 +307,7 @@ __global__ __launch_bounds__(fs_threads<D>()) void k_far_score(KParams p)
 #pragma unroll
                     for (int jt = 0; jt < 2; ++jt) L[(int64_t)hb * SUB + jt * 32 + ln] = acc[jt][v];
                     if (ln == 0) {
-                        MX[hb] = mx[v];
+                        MX[hb] = mx[v] * 0.6931471805599453f;   // ln 2
                         ZL[hb] = z;
                     }
                 }
