@@ -472,7 +472,10 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
     constexpr int NCH = L::BYTES / 1024;      // 1 KB wave copies of a tile
     constexpr int NW = AT_THREADS / 64;
     constexpr int LDF = D + 4;                // fp32 row stride of the epilogue's tiles
-    constexpr int NEAR_BYTES = 2 * L::BYTES;
+    // key-tile buffers: tile t is read while the copies of tiles t+1 ..
+    // t+NBUF-1 are in flight (three where they fit in LDS)
+    constexpr int NBUF = D > 128 ? 2 : 3;
+    constexpr int NEAR_BYTES = MODE == AT_MERGE ? 0 : NBUF * L::BYTES;   // (merge blocks hold no key tiles)
     constexpr int KTB = 2 * 2 * L::KH * 2;     // landmark keys as two fp16 hi/lo K tiles
     constexpr int FAR_BYTES = KTB + 2 * KT * LDF * 4 + HPB * 4 * 64 * 4;
     constexpr int SMEM = NEAR_BYTES > FAR_BYTES ? NEAR_BYTES : FAR_BYTES;
@@ -600,13 +603,27 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
     const int per = (ntiles + nsp - 1) / nsp;
     const int tA = MODE == AT_MERGE ? 0 : min(ntiles, sp * per);
     const int tB = MODE == AT_MERGE ? 0 : min(ntiles, tA + per);
-    if (tA < tB) issue(tA, 0);
+    // a wave's copies per tile, when every wave makes as many (the count it
+    // may leave in flight while waiting for an earlier tile; else it waits
+    // for all)
+    constexpr int KPW = NCH % NW == 0 ? NCH / NW : 0;
+    constexpr int LEFT = (NBUF - 2) * KPW;   // copies of the tiles after the next one
+    for (int t = 0; t < NBUF - 1; ++t)
+        if (tA + t < tB) issue(tA + t, t);
+    int buf = 0;
 #pragma unroll 1
-    for (int tt = tA; tt < tB; ++tt) {
-        const int buf = (tt - tA) & 1;
-        __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of tile tt have landed
-        __syncthreads();                 // ... and every wave's; tile tt-1 is no longer read
-        if (tt + 1 < tB) issue(tt + 1, buf ^ 1);
+    for (int tt = tA; tt < tB; ++tt, buf = buf + 1 == NBUF ? 0 : buf + 1) {
+        // this wave's copies of tile tt have landed (those of later tiles may
+        // still be in flight: vmcnt counts only the tile copies here)
+        if (LEFT > 0 && tt + NBUF - 2 < tB)
+            __builtin_amdgcn_s_waitcnt((LEFT & 15) | (7 << 4) | (15 << 8) | (((LEFT >> 4) & 3) << 14));
+        else
+            __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();   // ... and every wave's; tile tt-1 is no longer read
+        if (tt + NBUF - 1 < tB) {
+            const int nb = buf + NBUF - 1 < NBUF ? buf + NBUF - 1 : buf - 1;   // the buffer of tile tt-1
+            issue(tt + NBUF - 1, nb);
+        }
 
         const bool sink = tt < nst;
         const int tb = sink ? tt * KT : (j0 + tt - nst) * KT;
