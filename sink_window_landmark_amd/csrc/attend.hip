@@ -39,8 +39,8 @@
 // 3 * 2^-22 of |a*b| per product a*b, at a fifth of
 // the fp32 MFMA's time for the three products.  Values split unscaled
 // after a power-of-two scale per (pass, group) that brings their largest
-// magnitude into [2^13, 2^14) (k_vmax; an absolute floor of 2^-24 against
-// that), and the softmax weights are kept in (0, 2^15] with a sum of at
+// magnitude into [2^13, 2^14) (from the value maxima that k_far_score
+// writes; an absolute floor of 2^-24 against that), and the softmax weights are kept in (0, 2^15] with a sum of at
 // least 2^8 so that theirs stays far below that.  Range of the split
 // operands: |k| and |scale * log2(e) * q| at most 65504 (fp16's largest
 // finite value); values of any finite magnitude.
