@@ -278,17 +278,20 @@ __device__ __forceinline__ void split_b(const floatx16& x, int q, int ex, u32x4&
 template <int D, int NB, int MT, int LDF>
 __device__ __forceinline__ void far_numerator(floatx16 (&O)[NB], const floatx16 (&gn)[MT], const floatx16 (&cf)[2],
                                               const FView& Th, const float (*Vs)[LDF], int vexp, int m, int ln,
-                                              int hf)
+                                              int hf, int st_lo, int st_hi)
 {
-    constexpr int ST = 2 * MT;   // k-steps of the Theta chain
+    constexpr int ST = 2 * MT;   // k-steps of the Theta chain; this wave takes st_lo .. st_hi-1 (gn is zero
+                                 // on the others)
     auto krow = [&](int st, int e) { return (st >> 1) * 32 + (st & 1) * 16 + 4 * hf + (e >> 2) * 8 + (e & 3); };
+    auto mine = [&](int st) { return st >= st_lo && st < st_hi; };
     float th[ST][8];
     auto load = [&](int blk) {
         const int col = min(blk * 32 + ln, D - 1);
 #pragma unroll
         for (int st = 0; st < ST; ++st)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) th[st][e] = Th[min(krow(st, e), m - 1) * D + col];   // rows >= m: 0 below
+            for (int e = 0; e < 8; ++e)   // rows >= m: 0 below
+                th[st][e] = mine(st) ? Th[min(krow(st, e), m - 1) * D + col] : 0.f;
     };
 
     float gmax = 0.f, cmax = 0.f;
@@ -332,7 +335,8 @@ __device__ __forceinline__ void far_numerator(floatx16 (&O)[NB], const floatx16 
         load(0);
         u32x4 bh[ST], bl[ST];
 #pragma unroll
-        for (int st = 0; st < ST; ++st) split_b(gn[st >> 1], st & 1, eg, bh[st], bl[st]);
+        for (int st = 0; st < ST; ++st)
+            if (mine(st)) split_b(gn[st >> 1], st & 1, eg, bh[st], bl[st]);
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) {
             float tm = 0.f;
@@ -346,16 +350,18 @@ __device__ __forceinline__ void far_numerator(floatx16 (&O)[NB], const floatx16 
             const int et = __builtin_amdgcn_readfirstlane(value_exp_of(wmax(tm)));
             u32x4 ah[ST], al[ST];
 #pragma unroll
-            for (int st = 0; st < ST; ++st) split8(th[st], et, ah[st], al[st]);
+            for (int st = 0; st < ST; ++st)
+                if (mine(st)) split8(th[st], et, ah[st], al[st]);
             if (blk + 1 < NB) load(blk + 1);
             floatx16 acc;
             zero16(acc);
 #pragma unroll
-            for (int st = 0; st < ST; ++st) {
-                acc = mfma16(ah[st], bh[st], acc);
-                acc = mfma16(ah[st], bl[st], acc);
-                acc = mfma16(al[st], bh[st], acc);
-            }
+            for (int st = 0; st < ST; ++st)
+                if (mine(st)) {
+                    acc = mfma16(ah[st], bh[st], acc);
+                    acc = mfma16(ah[st], bl[st], acc);
+                    acc = mfma16(al[st], bh[st], acc);
+                }
 #pragma unroll
             for (int v = 0; v < 16; ++v) O[blk][v] += ldexpf(acc[v], -(et + eg));
         }
@@ -443,7 +449,8 @@ __global__ __launch_bounds__(256) void k_theta_kv(KParams p, int nth)
 // key tiles; AT_PART, p.nsp blocks per (sub-chunk, group, head group), each
 // over one contiguous range of the tiles, writing its softmax state (running
 // reference, mass, O^T) to p.apart; AT_MERGE, one block per (sub-chunk,
-// group, head group) that merges those states and runs the far readout.
+// group, head), or per half of its query rows, that merges those states and
+// runs the far readout.
 // The split serves launches with few blocks (a single sub-chunk, short
 // prompts), where one block per sub-chunk would leave most CUs idle.
 constexpr int AT_FULL = 0, AT_PART = 1, AT_MERGE = 2;
@@ -451,10 +458,14 @@ constexpr int AT_FULL = 0, AT_PART = 1, AT_MERGE = 2;
 // pays for the longer splits, measured at a single max-window sub-chunk)
 constexpr int AT_MAX_SPLITS = 8;
 
-// Block shape per mode: the merge takes one head per block (two waves, each
-// on a SIMD of its own), so that the few merge blocks of a small call spread
-// their far readouts over more CUs; it reads the split blocks' records by
-// their shape (AtCfg).
+// Block shape per mode: a merge block has two waves, each on a SIMD of its own,
+// so that the few merge blocks of a small call spread their far readouts over
+// more CUs.  It takes one head, a wave per half of the query rows, or, in a
+// split merge (p.msplit), one half of one head's rows: its waves then share
+// the rows and split the landmarks, the first taking the near part and the
+// first landmark tile, the second the other tile (the far numerator and mass
+// are sums over landmarks), and the two meet in LDS for the far-mass guard
+// and the output.  It reads the split blocks' records by their shape (AtCfg).
 template <int D, int MODE>
 struct AtShape {
     static constexpr int HPB = MODE == AT_MERGE ? 1 : AtCfg<D>::HPB;
@@ -480,7 +491,13 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
     constexpr int NEAR_BYTES = MODE == AT_MERGE ? 0 : NBUF * L::BYTES;   // (merge blocks hold no key tiles)
     constexpr int KTB = 2 * 2 * L::KH * 2;     // landmark keys as two fp16 hi/lo K tiles
     constexpr int FAR_BYTES = KTB + 2 * KT * LDF * 4 + HPB * 4 * 64 * 4;
-    constexpr int SMEM = NEAR_BYTES > FAR_BYTES ? NEAR_BYTES : FAR_BYTES;
+    // a split merge block's two waves exchange their far masses (XD, after
+    // the staged tiles) and the second wave's numerator (over the landmark
+    // keys' tiles, no longer read by then)
+    constexpr int XD_BYTES = MODE == AT_MERGE ? 2 * 32 * 4 : 0;
+    static_assert(64 * NB * 16 * 4 <= KTB, "a wave's O^T fits where the landmark keys were staged");
+    constexpr int SMEM0 = NEAR_BYTES > FAR_BYTES ? NEAR_BYTES : FAR_BYTES;
+    constexpr int SMEM = SMEM0 + XD_BYTES;
     constexpr float LOG2E = 1.4426950408889634f;
     __shared__ __align__(16) unsigned char smem[SMEM];
     unsigned short* const tiles = reinterpret_cast<unsigned short*>(smem);
@@ -491,11 +508,15 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
     // and the post-sub-chunk max M', rescale R, incoming mass Z and E's
     // factor of each head's landmarks
     float(*const MR)[4][64] = reinterpret_cast<float(*)[4][64]>(smem + KTB + 2 * KT * LDF * 4);
+    float(*const XD)[32] = reinterpret_cast<float(*)[32]>(smem + SMEM0);
 
     // work item = (sub-chunk, group, head group), dealt to XCDs as ranges of
-    // sub-chunks (range_item)
+    // sub-chunks (range_item); a split block also takes split sp of the
+    // item's key tiles, a merge block of a split merge query half sp of one
+    // head
     const int hgroups = (p.H + HPB - 1) / HPB;
-    const int nsp = MODE == AT_PART ? p.nsp : 1;
+    const bool msplit = MODE == AT_MERGE && MT == 2 && p.msplit;   // (two landmark tiles to split)
+    const int nsp = MODE == AT_PART ? p.nsp : msplit ? 2 : 1;
     int s, gi, sp;
     range_item(xcd_work_item(blockIdx.x, p.S * p.G * hgroups * nsp), p.S, p.G * hgroups, nsp, s, gi, sp);
     const int g = gi % p.G, hgrp = gi / p.G;
@@ -514,7 +535,12 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
     const int base = c.len0 + r0;                   // position of chunk row 0
     const int lo_blk = max(0, base - c.wg + 1);
     const int hi_blk = base + ks - 1;
-    const int ia = (wave & 1) * 32;
+    const int ia = (msplit ? sp : wave & 1) * 32;
+    // the landmark tile this wave takes in the far readout: the waves of a
+    // split merge block share their rows and split the landmarks between
+    // them; other waves take all (-1)
+    const int rt = msplit ? wave & 1 : -1;
+    auto my_tile = [&](int bt) { return rt < 0 || bt == rt; };
     const int i = ia + ln;                          // this lane's query row
     const int hi_q = base + i;
     const int lo_q = max(0, hi_q - c.wg + 1);
@@ -540,7 +566,7 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
         // shape: PH heads, PT threads)
         constexpr int PT = AtCfg<D>::THREADS, PH = AtCfg<D>::HPB;
         const int wp = s + p.S * (g + p.G * (h / PH));
-        const int tp = (h % PH) * 128 + tid;
+        const int tp = (h % PH) * 128 + ia * 2 + lane;   // that block's thread of this lane's query
         const float4* pp = reinterpret_cast<const float4*>(p.apart) + ((int64_t)wp * p.nsp * PT + tp) * PF4;
         // the largest reference first, every record's head in flight at once
         // (splits past nsp read the last record again)
@@ -549,8 +575,9 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
         for (int k = 0; k < AT_MAX_SPLITS; ++k) xm[k] = pp[(int64_t)min(k, p.nsp - 1) * PT * PF4].x;
 #pragma unroll
         for (int k = 0; k < AT_MAX_SPLITS; ++k) mrun = fmaxf(mrun, xm[k]);
+        // the first wave takes the near part; the second needs the reference alone
 #pragma unroll 4
-        for (int k = 0; k < p.nsp; ++k) {
+        for (int k = 0; k < (rt <= 0 ? p.nsp : 0); ++k) {
             const float4* pk = pp + (int64_t)k * PT * PF4;
             float4 r[PF4];
 #pragma unroll
@@ -917,6 +944,7 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
 #pragma unroll
             for (int bt = 0; bt < MT; ++bt) {
                 zero16(gn[bt]);
+                if (!my_tile(bt)) continue;
                 const int b = bt * 32 + ln;
 #pragma unroll
                 for (int at = 0; at < MT; ++at) {
@@ -952,6 +980,7 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
             for (int bt = 0; bt < MT; ++bt)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
+                    if (!my_tile(bt)) continue;
                     const int b = bt * 32 + kap(v, hf);
                     float u = gn[bt][v];
                     if (p.rect) u = fmaxf(u, 0.f);
@@ -974,6 +1003,7 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
                 const int j = jt * 32 + ln;
 #pragma unroll
                 for (int bt = 0; bt < MT; ++bt) {
+                    if (!my_tile(bt)) continue;
                     float av[16];
 #pragma unroll
                     for (int t = 0; t < 16; ++t) {
@@ -994,6 +1024,13 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
                 }
             }
             dfar = pair_sum<5>(dfar);
+            if (msplit) {
+                // the far mass over both waves' landmarks (the waves of a
+                // split merge block share their query rows, so both are here)
+                if (hf == 0) XD[wave][ln] = dfar;
+                __syncthreads();
+                dfar = XD[0][ln] + XD[1][ln];
+            }
             const bool have = lane_far && dfar >= 0.f;
             if (!have) {
                 dfar = 0.f;
@@ -1019,11 +1056,29 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
                     const float rb = Rs[b];
                     gn[bt][t] *= b < m ? rb : 0.f;
                 }
-            far_numerator<D, NB, MT, LDF>(O, gn, cf, Th, Vs, vexp, m, ln, hf);
+            far_numerator<D, NB, MT, LDF>(O, gn, cf, Th, Vs, vexp, m, ln, hf, rt < 0 ? 0 : 2 * rt,
+                                          rt < 0 ? 2 * MT : 2 * rt + 2);
+        }
+        if (msplit) {
+            // the second wave's share of the numerator to the first, through
+            // the landmark keys' place (both waves have passed the far-mass
+            // exchange, so both are done with them)
+            float* oc = reinterpret_cast<float*>(smem) + lane;
+            if (wave_rows && rt == 1)
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) oc[(b * 16 + v) * 64] = O[b][v];
+            __syncthreads();
+            if (wave_rows && rt == 0)
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) O[b][v] += oc[(b * 16 + v) * 64];
         }
     }
 
-    if (active && i < ks) {
+    if (active && i < ks && rt <= 0) {
         // without a far part the value sums still carry 2^vexp (with one,
         // the near part was brought to the far part's scale above)
         const float inv = ldexpf(1.f / fmaxf(den, 1e-30f), blk_far ? 0 : -vexp);
@@ -1076,9 +1131,15 @@ static hipError_t launch_dm(const KParams& p0, hipStream_t st)
     hipLaunchKernelGGL((k_attend<D, MT, AT_PART>), dim3(items * p.nsp), dim3(AtCfg<D>::THREADS), 0, st, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // the merge: one block per (sub-chunk, group, head)
+    // the merge: one block per (sub-chunk, group, head), or per half of its
+    // rows when that still leaves at most one block per CU (a few merge
+    // blocks run their far readouts as latency-bound chains, which the split
+    // halves; many are bound by throughput, which the split's duplicated
+    // staging would cost)
     constexpr int MERGE_THREADS = AtShape<D, AT_MERGE>::THREADS;
-    hipLaunchKernelGGL((k_attend<D, MT, AT_MERGE>), dim3(p.S * p.G * p.H), dim3(MERGE_THREADS), 0, st, p);
+    const int heads = p.S * p.G * p.H;
+    p.msplit = MT == 2 && 2 * heads <= 256;
+    hipLaunchKernelGGL((k_attend<D, MT, AT_MERGE>), dim3(heads * (p.msplit ? 2 : 1)), dim3(MERGE_THREADS), 0, st, p);
     return hipGetLastError();
 }
 

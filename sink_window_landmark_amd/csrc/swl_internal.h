@@ -52,6 +52,7 @@ struct KParams {
     int64_t theta_prev_stride;
     float* apart;             // split-window attention partials (attend_part_floats())
     int nsp;                  // splits of the window per attention work item (set by launch_attend)
+    int msplit;               // merge blocks split a head's query rows and landmarks (set by launch_attend)
     float* vmax;              // [G][VM_SLOTS] largest |value| seen by each far_score block of the group
     int vm_n;                 // far_score blocks per group (slots of vmax in use)
     unsigned short* kvs;      // [G][kv_tiles] fp16 key tiles of the pass (k_kv_split)

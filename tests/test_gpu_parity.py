@@ -325,6 +325,35 @@ def test_split_window_small_heads(d):
     check_state(read_state(st), orc)
 
 
+@pytest.mark.parametrize("rect", [False, True])
+def test_split_merge_landmark_tiles(rect):
+    """Merges of few heads split each head's query rows over two blocks and
+    the landmarks over their two waves: m = 48 (a second landmark tile with 16
+    landmarks), mu of mixed signs (the two tiles' far masses of either sign;
+    head 0 all negative, so its far part is dropped by the guard on the total),
+    a 300-row prompt (5 sub-chunks, 30 merge heads), then 64-, 20- (no rows in
+    the second half) and 33-row attend_chunk + commit calls, against the
+    oracle."""
+    banner(f"split merge m=48 rect={rect}: prefill 300, chunks 64/20/33")
+    cfg = synth.Config("mtiles", G=2, H=3, d=64, dv=64, ns=4, W=128, m=48, rows=300,
+                       windows=(128, 96), rect=rect)
+    host = synth.make_state(cfg)
+    r = np.random.default_rng(11)
+    host.mu = (r.standard_normal(host.mu.shape) / cfg.m).astype(np.float32)
+    host.mu[0] = -np.abs(host.mu[0])
+    sizes = [64, 20, 33]
+    n = cfg.rows + sum(sizes)
+    q, k, v = synth.rows(cfg, 0, n)
+    st = _state(cfg, host)
+    orc = oracle.from_config(cfg, host, threads=oracle_threads())
+    T = cfg.rows
+    got = _prefill(cfg, st, q[:T], k[:T], v[:T], poison=True)
+    check_out(got, orc.step(q[:T], k[:T], v[:T]), "prefill")
+    got = _chunks(cfg, st, q[T:], k[T:], v[T:], sizes, poison=True)
+    check_out(got, orc.step(q[T:], k[T:], v[T:]), f"chunks {sizes}")
+    check_state(read_state(st), orc)
+
+
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["maxwin", "mixed"])
 def test_full_size_every_row(name):
