@@ -1107,8 +1107,8 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
 }
 
 // Splits of the window per (sub-chunk, group, head group) item: enough for
-// about 256 blocks, at most 16, at least 4 key tiles per split, and never
-// more than the partials plane holds (256 pairs).
+// about 256 blocks, at most AT_MAX_SPLITS, at least 4 key tiles per split,
+// and never more than the partials plane holds (256 pairs).
 static int attend_splits(const KParams& p, int items)
 {
     const int max_tiles = (p.ns + KT - 1) / KT + (p.W + SUB + KT - 1) / KT + 1;
