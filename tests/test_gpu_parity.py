@@ -354,6 +354,29 @@ def test_split_merge_landmark_tiles(rect):
     check_state(read_state(st), orc)
 
 
+def test_split_merge_wide_heads():
+    """The split merge at d = 256 with two landmark tiles (m = 64; two heads
+    per attention block, the largest staging of the far readout): a 200-row
+    prompt (4 sub-chunks, 16 merge heads), then 64- and 20-row
+    attend_chunk + commit calls, against the oracle."""
+    import math
+    banner("split merge d=256 m=64: prefill 200, chunks 64/20")
+    cfg = synth.Config("wide", G=2, H=2, d=256, dv=256, ns=4, W=128, m=64, rows=200, windows=(128, 72),
+                       landmark_scale=1.0 / math.sqrt(256))
+    host = synth.make_state(cfg)
+    sizes = [64, 20]
+    n = cfg.rows + sum(sizes)
+    q, k, v = synth.rows(cfg, 0, n)
+    st = _state(cfg, host)
+    orc = oracle.from_config(cfg, host, threads=oracle_threads())
+    T = cfg.rows
+    got = _prefill(cfg, st, q[:T], k[:T], v[:T], poison=True)
+    check_out(got, orc.step(q[:T], k[:T], v[:T]), "prefill")
+    got = _chunks(cfg, st, q[T:], k[T:], v[T:], sizes, poison=True)
+    check_out(got, orc.step(q[T:], k[T:], v[T:]), f"chunks {sizes}")
+    check_state(read_state(st), orc)
+
+
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["maxwin", "mixed"])
 def test_full_size_every_row(name):
