@@ -490,7 +490,15 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
     constexpr int NBUF = D > 128 ? 2 : 3;
     constexpr int NEAR_BYTES = MODE == AT_MERGE ? 0 : NBUF * L::BYTES;   // (merge blocks hold no key tiles)
     constexpr int KTB = 2 * 2 * L::KH * 2;     // landmark keys as two fp16 hi/lo K tiles
-    constexpr int FAR_BYTES = KTB + 2 * KT * LDF * 4 + HPB * 4 * 64 * 4;
+    // and, in full blocks where it fits, E of the block's heads (rows padded
+    // to 72 floats, so that the two row groups a read touches fall in
+    // different banks; merge blocks, whose LDS sets how many share a CU,
+    // read E from memory)
+    constexpr int ELD = SUB + 8;
+    constexpr int FAR_BYTES0 = KTB + 2 * KT * LDF * 4 + HPB * 4 * 64 * 4;
+    constexpr int E_BYTES = HPB * 64 * ELD * 4;
+    constexpr bool E_LDS = MODE == AT_FULL && FAR_BYTES0 + E_BYTES <= 160 * 1024;
+    constexpr int FAR_BYTES = FAR_BYTES0 + (E_LDS ? E_BYTES : 0);
     // a split merge block's two waves exchange their far masses (XD, after
     // the staged tiles) and the second wave's numerator (over the landmark
     // keys' tiles, no longer read by then)
@@ -508,6 +516,7 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
     // and the post-sub-chunk max M', rescale R, incoming mass Z and E's
     // factor of each head's landmarks
     float(*const MR)[4][64] = reinterpret_cast<float(*)[4][64]>(smem + KTB + 2 * KT * LDF * 4);
+    float(*const ES)[64][ELD] = reinterpret_cast<float(*)[64][ELD]>(smem + FAR_BYTES0);   // [head][b][j]
     float(*const XD)[32] = reinterpret_cast<float(*)[32]>(smem + SMEM0);
 
     // work item = (sub-chunk, group, head group), dealt to XCDs as ranges of
@@ -889,6 +898,25 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
                 if (e < NE) MR[e >> 8][(e >> 6) & 3][e & 63] = x[u];
             }
         }
+        if constexpr (E_LDS) {
+            // E of each head of the block: [b][j] against the sub-chunk's own
+            // max, 0 where row j evicts nothing; rows past m zero
+            constexpr int NE = HPB * 64 * (SUB / 4), NU = (NE + AT_THREADS - 1) / AT_THREADS;
+            float4 ex[NU];
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                const int e = min(tid + u * AT_THREADS, NE - 1);
+                const int hh = e / (64 * (SUB / 4)), b = (e / (SUB / 4)) & 63, j4 = e % (SUB / 4);
+                const int ghh = g * p.H + min(hgrp * HPB + hh, p.H - 1);
+                ex[u] = *reinterpret_cast<const float4*>(p.E + (((int64_t)s * p.nh + ghh) * m + min(b, m - 1)) * SUB + j4 * 4);
+            }
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                const int e = tid + u * AT_THREADS;
+                const int hh = e / (64 * (SUB / 4)), b = (e / (SUB / 4)) & 63, j4 = e % (SUB / 4);
+                if (e < NE) *reinterpret_cast<float4*>(&ES[hh][b][j4 * 4]) = b < m ? ex[u] : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
         __syncthreads();
 
         const int farl = sm.nfar0 + (i >= sm.j0 ? i - sm.j0 + 1 : 0);
@@ -1008,7 +1036,8 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
 #pragma unroll
                     for (int t = 0; t < 16; ++t) {
                         const int b = bt * 32 + kap(t, hf);
-                        av[t] = b < m ? Eb[(int64_t)b * SUB + j] : 0.f;
+                        if constexpr (E_LDS) av[t] = ES[wave >> 1][b][j];   // (rows past m hold zeros)
+                        else av[t] = b < m ? Eb[(int64_t)b * SUB + j] : 0.f;
                     }
 #pragma unroll
                     for (int t = 0; t < 16; ++t) {
