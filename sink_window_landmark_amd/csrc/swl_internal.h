@@ -85,11 +85,13 @@ __device__ __forceinline__ float4 rope4(const float* x, const float* tab, int c4
                        b.w * cs.w + a.w * sn.w);
 }
 
-// The output gate 1 / (1 + exp(-z s)) (0 for very negative z s, 1 for
-// very positive: exp overflows to inf or underflows to 0, no NaN).
+// The output gate 1 / (1 + exp(-z s)), as 1 / (1 + 2^(-z s log2 e)) on the
+// hardware exponential and reciprocal (a few ulp in all; 0 for very negative
+// z s, 1 for very positive: the exponential overflows to inf or underflows
+// to 0, no NaN).
 __device__ __forceinline__ float gate_of(float z, float s)
 {
-    return 1.f / (1.f + expf(-z * s));
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z * s * 1.4426950408889634f));
 }
 
 // Ring bookkeeping of group g at the start of a call.
