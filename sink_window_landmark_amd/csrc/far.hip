@@ -427,6 +427,23 @@ __device__ __forceinline__ void dtheta_body(const KParams& p, int64_t bid)
     const int hm = p.H * p.m;
     const int64_t nhm = (int64_t)p.nh * p.m;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, ln = lane & 31;
+    const int64_t row0 = (int64_t)s * nhm + (int64_t)g * hm;   // landmark row (s, g*H*m)
+    const int nht = (hm + 31) / 32;
+    // this lane's E row of landmark-row tile ht (zero past hm)
+    auto load_e = [&](int ht, float (&e)[32]) {
+        const int hb = ht * 32 + ln;
+        const bool rv = hb < hm;
+        const float* Lr = p.E + (row0 + min(hb, hm - 1)) * SUB + hf * 32;
+#pragma unroll
+        for (int k = 0; k < 32; k += 4) {
+            const float4 x = *reinterpret_cast<const float4*>(Lr + k);
+            e[k] = rv ? x.x : 0.f; e[k + 1] = rv ? x.y : 0.f;
+            e[k + 2] = rv ? x.z : 0.f; e[k + 3] = rv ? x.w : 0.f;
+        }
+    };
+    // the wave's first tile's E rows go out before the values' staging
+    float e0[32];
+    if (wave < nht) load_e(wave, e0);
     const int vexp = value_exp(p, g);   // the values enter the split times 2^vexp
     {
         // units of two rows (2 jp, 2 jp + 1) x four columns: clamped
@@ -467,21 +484,7 @@ __device__ __forceinline__ void dtheta_body(const KParams& p, int64_t bid)
         }
     }
     __syncthreads();
-    const int64_t row0 = (int64_t)s * nhm + (int64_t)g * hm;   // landmark row (s, g*H*m)
-    const int nht = (hm + 31) / 32;
-    for (int ht = wave; ht < nht; ht += 4) {
-        const int hb = ht * 32 + ln;              // this lane's E row
-        const bool rv = hb < hm;
-        float e[32];
-        {
-            const float* Lr = p.E + (row0 + min(hb, hm - 1)) * SUB + hf * 32;
-#pragma unroll
-            for (int k = 0; k < 32; k += 4) {
-                const float4 x = *reinterpret_cast<const float4*>(Lr + k);
-                e[k] = rv ? x.x : 0.f; e[k + 1] = rv ? x.y : 0.f;
-                e[k + 2] = rv ? x.z : 0.f; e[k + 3] = rv ? x.w : 0.f;
-            }
-        }
+    auto tile = [&](int ht, const float (&e)[32]) {
         // E * 2^12 as fp16 halves: k-step st takes rows j = 32 hf + 8 st + e
         // of this lane's landmark row (its own e[8 st + e])
         fu32x4 eh[4], el[4];
@@ -537,6 +540,12 @@ __device__ __forceinline__ void dtheta_body(const KParams& p, int64_t bid)
                 }
             }
         }
+    };
+    if (wave < nht) tile(wave, e0);
+    for (int ht = wave + 4; ht < nht; ht += 4) {
+        float e[32];
+        load_e(ht, e);
+        tile(ht, e);
     }
 }
 
