@@ -36,12 +36,12 @@
 // hi*hi + (hi*lo + lo*hi) * 2^-sc on v_mfma_f32_32x32x16_f16 with fp32
 // accumulation (the hi*lo terms of the scores in an accumulator of their
 // own); the dropped lo*lo term and the rounding of lo leave at most
-// 3 * 2^-22 of |a*b| per product a*b, at a fifth of
-// the fp32 MFMA's time for the three products.  Values split unscaled
-// after a power-of-two scale per (pass, group) that brings their largest
-// magnitude into [2^13, 2^14) (from the value maxima that k_far_score
-// writes; an absolute floor of 2^-24 against that), and the softmax weights are kept in (0, 2^15] with a sum of at
-// least 2^8 so that theirs stays far below that.  Range of the split
+// 3 * 2^-22 of |a*b| per product a*b, at a fifth of the fp32 MFMA's time
+// for the three products.  Values split unscaled after a power-of-two scale
+// per (pass, group) that brings their largest magnitude into [2^13, 2^14)
+// (from the value maxima that k_far_score writes; an absolute floor of
+// 2^-24 against that), and the softmax weights are kept in (0, 2^15] with a
+// sum of at least 2^8 so that theirs stays far below that.  Range of the split
 // operands: |k| and |scale * log2(e) * q| at most 65504 (fp16's largest
 // finite value); values of any finite magnitude.
 //
@@ -908,13 +908,15 @@ __global__ __launch_bounds__((AtShape<D, MODE>::THREADS)) void k_attend(KParams 
                 const int e = min(tid + u * AT_THREADS, NE - 1);
                 const int hh = e / (64 * (SUB / 4)), b = (e / (SUB / 4)) & 63, j4 = e % (SUB / 4);
                 const int ghh = g * p.H + min(hgrp * HPB + hh, p.H - 1);
-                ex[u] = *reinterpret_cast<const float4*>(p.E + (((int64_t)s * p.nh + ghh) * m + min(b, m - 1)) * SUB + j4 * 4);
+                const float* src = p.E + (((int64_t)s * p.nh + ghh) * m + min(b, m - 1)) * SUB + j4 * 4;
+                ex[u] = *reinterpret_cast<const float4*>(src);
             }
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
                 const int e = tid + u * AT_THREADS;
                 const int hh = e / (64 * (SUB / 4)), b = (e / (SUB / 4)) & 63, j4 = e % (SUB / 4);
-                if (e < NE) *reinterpret_cast<float4*>(&ES[hh][b][j4 * 4]) = b < m ? ex[u] : make_float4(0.f, 0.f, 0.f, 0.f);
+                if (e < NE)
+                    *reinterpret_cast<float4*>(&ES[hh][b][j4 * 4]) = b < m ? ex[u] : make_float4(0.f, 0.f, 0.f, 0.f);
             }
         }
         __syncthreads();
