@@ -148,9 +148,9 @@ int swl_prefill(const swl_geom* geom, const swl_state* st,
 
 /* Stages of a call, as reported to a swl_stage_fn.  A prefill pass makes
  * five launches, reported in this order: far score (which also takes the
- * values' scale), far scan (which also forms the accumulator increments,
- * dtheta), theta scan (which also splits the key tiles), attend, ring
- * (which also updates meta).  SWL_STAGE_DTHETA, SWL_STAGE_META,
+ * values' scale and forms the accumulator increments, dtheta), far scan,
+ * theta scan (which also splits the key tiles), attend, ring (which also
+ * updates meta).  SWL_STAGE_DTHETA, SWL_STAGE_META,
  * SWL_STAGE_KV_SPLIT and SWL_STAGE_VALUE_SCALE name parts of those
  * launches and are not reported on their own. */
 enum swl_stage {

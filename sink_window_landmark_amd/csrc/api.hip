@@ -137,7 +137,7 @@ static void set_scratch(KParams& p, const swl_geom* g, void* scratch, int S)
     p.TH = reinterpret_cast<float*>(b + c.th);
     p.apart = reinterpret_cast<float*>(b + c.apart);
     p.vmax = reinterpret_cast<float*>(b + c.vm);
-    p.vm_n = fs_blocks_per_group(S, g->G);
+    p.vm_n = fs_blocks_per_group(S, g->G, g->H * g->m);
     p.meta_copy = reinterpret_cast<uint32_t*>(b + c.mc);
     p.kvs = reinterpret_cast<unsigned short*>(b + c.kv);
     p.kv_tiles = kv_tiles(g->ns, g->W, S);
@@ -169,15 +169,16 @@ static KParams after_first(const KParams& p)
     return q;
 }
 
-// far_e (the values' scale, scores, scan, E and the accumulator increment)
-// + attention (near part and far readout) of one call; the state is
-// unchanged.
-static int run_attend(const KParams& p, hipStream_t st)
+// far_e (the values' scale, scores, E and the accumulator increment; then
+// the far scan, beside the key tiles) + attention (near part and far
+// readout) of one call; the state is unchanged.
+static int run_attend(const KParams& p0, hipStream_t st)
 {
+    KParams p = p0;
+    p.vm_far = 1;
     SWL_TRY(launch_far_score(p, st));
     const KParams q = after_first(p);
-    SWL_TRY(launch_scan_dtheta(q, st));
-    SWL_TRY(launch_theta_kv(q, false, true, st));
+    SWL_TRY(launch_theta_kv(q, true, false, true, st));
     SWL_TRY(launch_attend(q, st));
     return SWL_OK;
 }
@@ -302,11 +303,11 @@ static int run_rows(const swl_geom* geom, const swl_state* st, const float* q, c
         set_scratch(p, geom, scratch, S_max);
         p.theta_prev = p.TH;
         p.theta_prev_stride = (int64_t)nh * geom->m * geom->dv;
-        SWL_STAGE(SWL_STAGE_FAR_SCORE, launch_far_score(p, hs));   // with the values' scale
+        SWL_STAGE(SWL_STAGE_FAR_SCORE, launch_far_score(p, hs));   // with the increments
         const KParams q = after_first(p);
-        SWL_STAGE(SWL_STAGE_FAR_SCAN, launch_scan_dtheta(q, hs));   // with the increments
+        SWL_STAGE(SWL_STAGE_FAR_SCAN, launch_far_scan(q, attend, hs));   // with the values' scale
         if (attend) {
-            SWL_STAGE(SWL_STAGE_THETA_SCAN, launch_theta_kv(q, true, true, hs));   // with the key tiles
+            SWL_STAGE(SWL_STAGE_THETA_SCAN, launch_theta_kv(q, false, true, true, hs));   // with the key tiles
             SWL_STAGE(SWL_STAGE_ATTEND, launch_attend(q, hs));
             SWL_STAGE(SWL_STAGE_RING, launch_commit(q, false, hs));   // with the meta
         } else {

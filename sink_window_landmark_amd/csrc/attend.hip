@@ -377,11 +377,14 @@ __device__ __forceinline__ void far_numerator(floatx16 (&O)[NB], const floatx16 
 // attention takes back out of its value sums.
 // ---------------------------------------------------------------------------
 template <int D>
-__device__ __forceinline__ void kv_split_body(const KParams& p, int64_t bid)
+constexpr int kv_lds_floats() { return 2 * KT * (D + 1); }
+
+template <int D>
+__device__ __forceinline__ void kv_split_body(const KParams& p, int64_t bid, float* lds)
 {
     using L = KvTile<D>;
-    __shared__ float kf[KT][D + 1];
-    __shared__ float vf[KT][D + 1];
+    float(*const kf)[D + 1] = reinterpret_cast<float(*)[D + 1]>(lds);   // [KT][D + 1]
+    float(*const vf)[D + 1] = reinterpret_cast<float(*)[D + 1]>(lds + KT * (D + 1));
     const int t = (int)(bid % p.kv_tiles), g = (int)(bid / p.kv_tiles);
     const int nst = (p.ns + KT - 1) / KT;
     const GMeta c = load_gmeta(p.meta, g, p.W);
@@ -435,14 +438,19 @@ __device__ __forceinline__ void kv_split_body(const KParams& p, int64_t bid)
     }
 }
 
-// The accumulator scan (stages.h; with its commit of Theta, M and Z) and
-// the key tiles of a pass in one launch: blocks [0, nth) scan, the rest
-// split tiles.  The two do not depend on each other.
+// The key tiles of a pass in one launch with either the far scan (a call
+// whose accumulator scan runs in its commit) or the accumulator scan (after
+// a far scan launch; with its commit of Theta, M and Z): blocks [0, nmz)
+// run the far scan, the next nth the accumulator scan (stages.h), the rest
+// split tiles.  None waits on another.
 template <int D>
-__global__ __launch_bounds__(256) void k_theta_kv(KParams p, int nth)
+__global__ __launch_bounds__(256) void k_theta_kv(KParams p, int nmz, int nth)
 {
-    if ((int)blockIdx.x < nth) theta_scan_body(p, true, blockIdx.x);
-    else kv_split_body<D>(p, (int64_t)blockIdx.x - nth);
+    __shared__ __align__(16) float lds[kv_lds_floats<D>()];
+    const int b = blockIdx.x;
+    if (b < nmz) mz_scan_body(p, b);
+    else if (b < nmz + nth) theta_scan_body(p, true, b - nmz);
+    else kv_split_body<D>(p, (int64_t)b - nmz - nth, lds);
 }
 
 // MODE: AT_FULL, one block per (sub-chunk, group, head group) over all of its
@@ -1196,24 +1204,25 @@ int kv_tiles(int ns, int W, int S)
 size_t kv_tile_bytes(int d) { return (size_t)128 * ((d < 16 ? 16 : d) + d); }
 
 template <int D>
-static hipError_t launch_theta_kv_d(const KParams& p, bool theta, bool kv, hipStream_t st)
+static hipError_t launch_theta_kv_d(const KParams& p, bool mz, bool theta, bool kv, hipStream_t st)
 {
+    const int64_t nmz = mz ? far_scan_blocks(p) : 0;
     const int64_t nth = theta ? theta_blocks(p) : 0;
     const int64_t nkv = kv ? (int64_t)p.G * p.kv_tiles : 0;
-    if (nth + nkv == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_theta_kv<D>, dim3((unsigned)(nth + nkv)), dim3(256), 0, st, p, (int)nth);
+    hipLaunchKernelGGL(k_theta_kv<D>, dim3((unsigned)(nmz + nth + nkv)), dim3(256), 0, st, p, (int)nmz,
+                       (int)nth);
     return hipGetLastError();
 }
 
-hipError_t launch_theta_kv(const KParams& p, bool theta, bool kv, hipStream_t st)
+hipError_t launch_theta_kv(const KParams& p, bool mz, bool theta, bool kv, hipStream_t st)
 {
     switch (p.d) {
-    case 8: return launch_theta_kv_d<8>(p, theta, kv, st);
-    case 16: return launch_theta_kv_d<16>(p, theta, kv, st);
-    case 32: return launch_theta_kv_d<32>(p, theta, kv, st);
-    case 64: return launch_theta_kv_d<64>(p, theta, kv, st);
-    case 128: return launch_theta_kv_d<128>(p, theta, kv, st);
-    case 256: return launch_theta_kv_d<256>(p, theta, kv, st);
+    case 8: return launch_theta_kv_d<8>(p, mz, theta, kv, st);
+    case 16: return launch_theta_kv_d<16>(p, mz, theta, kv, st);
+    case 32: return launch_theta_kv_d<32>(p, mz, theta, kv, st);
+    case 64: return launch_theta_kv_d<64>(p, mz, theta, kv, st);
+    case 128: return launch_theta_kv_d<128>(p, mz, theta, kv, st);
+    case 256: return launch_theta_kv_d<256>(p, mz, theta, kv, st);
     default: return hipErrorInvalidValue;
     }
 }

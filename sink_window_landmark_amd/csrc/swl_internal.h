@@ -54,7 +54,8 @@ struct KParams {
     int nsp;                  // splits of the window per attention work item (set by launch_attend)
     int msplit;               // merge blocks split a head's query rows and landmarks (set by launch_attend)
     float* vmax;              // [G][VM_SLOTS] largest |value| seen by each far_score block of the group
-    int vm_n;                 // far_score blocks per group (slots of vmax in use)
+    int vm_n;                 // value-maxima shares per group (slots of vmax in use)
+    int vm_far;               // far_score takes the value maxima (no far scan launch follows)
     unsigned short* kvs;      // [G][kv_tiles] fp16 key tiles of the pass (k_kv_split)
     int kv_tiles;             // tiles per group: the sinks, then the aligned window tiles
     // fused ingest and output steps (null: off)
@@ -214,13 +215,26 @@ __host__ __device__ inline int fs_runs(int S, int G)
     const int rl = fs_run(S, G);
     return (S + rl - 1) / rl;
 }
-// blocks per group of the launch: one per run, and at least 32, so that the
-// value maxima of a short call still spread over many blocks (the blocks
-// past the runs take only their share of the values)
-constexpr int FS_MIN_BLOCKS = 32;
-__host__ __device__ inline int fs_blocks_per_group(int S, int G)
+// blocks per run: while the launch would have fewer than 128 working
+// blocks, the hm / 32 landmark-row tiles of a run are split over 2, 4, ...
+// blocks (a power of two, at most the tile count).  Each such block loads
+// the run's keys and values again, so launches that already fill half the
+// machine keep one block per run.
+__host__ __device__ inline int fs_tsplit(int S, int G, int hm)
 {
-    const int n = fs_runs(S, G);
+    const int nht = (hm + 31) / 32;
+    const int n = fs_runs(S, G) * G;
+    int ts = 1;
+    while (2 * ts <= nht && n * ts < 128) ts *= 2;
+    return ts;
+}
+// blocks per group of the launch: one per run and tile split, and at least
+// 32, so that the value maxima of a short call still spread over many
+// blocks (the blocks past the runs take only their share of the values)
+constexpr int FS_MIN_BLOCKS = 32;
+__host__ __device__ inline int fs_blocks_per_group(int S, int G, int hm)
+{
+    const int n = fs_runs(S, G) * fs_tsplit(S, G, hm);
     return n > FS_MIN_BLOCKS ? n : FS_MIN_BLOCKS;
 }
 
@@ -228,9 +242,9 @@ __host__ __device__ inline int fs_blocks_per_group(int S, int G)
 hipError_t launch_init(const KParams& p, const uint32_t* windows, hipStream_t st);
 hipError_t launch_far_score(const KParams& p, hipStream_t st);
 // the far scan and the accumulator increments in one launch
-hipError_t launch_scan_dtheta(const KParams& p, hipStream_t st);
+hipError_t launch_far_scan(const KParams& p, bool vm, hipStream_t st);   // vm: with the value maxima
 // the accumulator scan (commit) and the key tiles in one launch (either may be off)
-hipError_t launch_theta_kv(const KParams& p, bool theta, bool kv, hipStream_t st);
+hipError_t launch_theta_kv(const KParams& p, bool mz, bool theta, bool kv, hipStream_t st);
 hipError_t launch_attend(const KParams& p, hipStream_t st);
 // tiles per group and bytes per tile of the fp16 key tiles
 int kv_tiles(int ns, int W, int S);
