@@ -240,13 +240,17 @@ struct FView {
 
 // Split fp16 halves of 8 values times 2^ex (the scaling is exact): an A
 // operand, or the B operand of k-step q of a C-layout tile x (its values
-// 8q .. 8q+7 in this lane).
+// 8q .. 8q+7 in this lane).  The remainders come from v_fma_mix (the same
+// bits as a conversion and a subtraction, in one instruction), after the
+// scaled values are pinned as rounded fp32 numbers as in Split.
 __device__ __forceinline__ void split8(const float (&a)[8], int ex, u32x4& hi, u32x4& lo)
 {
     unsigned h[4], l[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const Split<false> s(ldexpf(a[2 * k], ex), ldexpf(a[2 * k + 1], ex));
+        float x = ldexpf(a[2 * k], ex), y = ldexpf(a[2 * k + 1], ex);
+        asm("" : "+v"(x), "+v"(y));
+        const SplitMix s(x, y);
         h[k] = s.hi;
         l[k] = s.lo;
     }
