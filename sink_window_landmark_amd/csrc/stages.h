@@ -248,7 +248,7 @@ __host__ __device__ inline int64_t ring_blocks(const KParams& p)
     return (int64_t)(p.T < p.W ? p.T : p.W) * p.G;
 }
 
-// Ring commit, block `bid` of ring_blocks(p) (256 threads): chunk row r of
+// Ring commit, block `bid` of ring_blocks(p) (any block size): chunk row r of
 // the call lands in slot (head0 + len0 + r) mod w_g, the slot its own
 // eviction freed (o1b_ring_commit).  Only the last w_g rows of the call
 // survive in the ring, so only they are written: that keeps the writes of a
@@ -267,10 +267,11 @@ __device__ __forceinline__ void ring_body(const KParams& p, int64_t bid)
     float* kd = p.ring_k + ((int64_t)g * p.W + slot) * p.d;
     float* vd = p.ring_v + ((int64_t)g * p.W + slot) * p.dv;
     const float* kt = p.rope ? p.rope + (int64_t)r * p.d : nullptr;   // the ring holds turned keys
-    for (int t = threadIdx.x; t < p.d / 4; t += blockDim.x)
-        reinterpret_cast<float4*>(kd)[t] = rope4(ks, kt, 4 * t, p.d);
-    for (int t = threadIdx.x; t < p.dv / 4; t += blockDim.x)
-        reinterpret_cast<float4*>(vd)[t] = reinterpret_cast<const float4*>(vs)[t];
+    // the key's float4s, then the value's, over the block's threads
+    for (int t = threadIdx.x; t < p.d / 4 + p.dv / 4; t += blockDim.x) {
+        if (t < p.d / 4) reinterpret_cast<float4*>(kd)[t] = rope4(ks, kt, 4 * t, p.d);
+        else reinterpret_cast<float4*>(vd)[t - p.d / 4] = reinterpret_cast<const float4*>(vs)[t - p.d / 4];
+    }
 }
 
 // len, head and nfar after T pushes (o1b_meta with k = T), from the

@@ -55,7 +55,10 @@ hipError_t launch_init(const KParams& p, const uint32_t* windows, hipStream_t st
 hipError_t launch_commit(const KParams& p, bool theta, hipStream_t st)
 {
     const int64_t nth = theta ? theta_blocks(p) : 0;
-    hipLaunchKernelGGL(k_commit, dim3((unsigned)(nth + ring_blocks(p) + 1)), dim3(256), 0, st, p, (int)nth);
+    // without the scan (256 threads per block) the ring rows take one wave
+    // each, so that every block of a long pass is resident at once
+    hipLaunchKernelGGL(k_commit, dim3((unsigned)(nth + ring_blocks(p) + 1)), dim3(theta ? 256 : 64), 0, st, p,
+                       (int)nth);
     return hipGetLastError();
 }
 
