@@ -646,6 +646,23 @@ def test_many_groups():
     check_state(read_state(st), orc)
 
 
+@pytest.mark.parametrize("d,H", [(64, 16), (256, 4)])
+def test_more_landmark_tiles_than_waves(d, H):
+    """A prompt of 64 sub-chunks in two groups, whose far-score launch keeps
+    one block per sub-chunk (it already has 128), with more landmark-row
+    tiles per group (H * m / 32) than the block has waves: each wave then
+    scores several tiles, loading their query halves in turn."""
+    banner(f"far score, tiles over waves: d={d} H={H} m=64, 4096 rows")
+    cfg = synth.Config("tiles", G=2, H=H, d=d, dv=d, ns=4, W=128, m=64, rows=4096)
+    host = synth.make_state(cfg)
+    q, k, v = synth.rows(cfg, 0, 4096)
+    st = _state(cfg, host)
+    got = _prefill(cfg, st, q, k, v, poison=True)
+    orc = oracle.from_config(cfg, host, threads=oracle_threads())
+    check_out(got, orc.step(q, k, v))
+    check_state(read_state(st), orc)
+
+
 @pytest.mark.parametrize("W,T", [(65536, 3000), (5000, 6000)])
 def test_tokens_over_many_splits(W, T):
     """Decode with the window split into more than 64 partials per head (the
