@@ -147,12 +147,14 @@ int swl_prefill(const swl_geom* geom, const swl_state* st,
                 float* out, void* scratch, size_t scratch_bytes, void* stream);
 
 /* Stages of a call, as reported to a swl_stage_fn.  A prefill pass makes
- * five launches, reported in this order: far score (which also takes the
- * values' scale and forms the accumulator increments, dtheta), far scan,
- * theta scan (which also splits the key tiles), attend, ring (which also
- * updates meta).  SWL_STAGE_DTHETA, SWL_STAGE_META,
- * SWL_STAGE_KV_SPLIT and SWL_STAGE_VALUE_SCALE name parts of those
- * launches and are not reported on their own. */
+ * five launches, reported in this order: far score (which also forms the
+ * accumulator increments, dtheta), far scan (which also takes the values'
+ * scale), theta scan (which also splits the key tiles), attend, ring
+ * (which also updates meta).  A pass without attention (swl_commit_rows)
+ * makes three: far score, far scan, and theta scan with the ring and meta.
+ * SWL_STAGE_DTHETA, SWL_STAGE_META, SWL_STAGE_KV_SPLIT and
+ * SWL_STAGE_VALUE_SCALE name parts of those launches and are not reported
+ * on their own. */
 enum swl_stage {
     SWL_STAGE_FAR_SCORE = 0,  /* evicted key x landmark scores */
     SWL_STAGE_FAR_SCAN = 1,   /* post-sub-chunk max, rescale and incoming mass */
