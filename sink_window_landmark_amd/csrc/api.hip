@@ -176,6 +176,7 @@ static int run_attend(const KParams& p0, hipStream_t st)
 {
     KParams p = p0;
     p.vm_far = 1;
+    p.vm_n = FS_MIN_BLOCKS;   // far_score's value-maxima blocks per group
     SWL_TRY(launch_far_score(p, st));
     const KParams q = after_first(p);
     SWL_TRY(launch_theta_kv(q, true, false, true, st));

@@ -96,8 +96,8 @@ __device__ __forceinline__ int kswz(int r, int c)
 // As the first launch of a call it also copies the call-start meta to
 // p.meta_copy (block 0), which the later launches read, so that the last one
 // can write the new meta, and, in a call without a far scan launch
-// (p.vm_far), takes the value maxima (value_max_share): blocks past the
-// runs do only that.
+// (p.vm_far), takes the value maxima (value_max_share) in FS_MIN_BLOCKS
+// blocks per group of their own, after the working ones.
 // ---------------------------------------------------------------------------
 // eight waves; four at d = 256, where the query halves alone take 128 registers
 template <int D>
@@ -136,8 +136,8 @@ __global__ __launch_bounds__(fs_threads<D>()) void k_far_score(KParams p)
     const int rl = fs_run(p.S, p.G);
     const int nrun = fs_runs(p.S, p.G);
     const int ts = fs_tsplit(p.S, p.G, hm);
-    // nrun * ts, or (taking the value maxima) at least FS_MIN_BLOCKS
-    const int nblk = p.vm_far ? fs_blocks_per_group(p.S, p.G, hm) : fs_runs(p.S, p.G) * fs_tsplit(p.S, p.G, hm);
+    // nrun * ts working blocks, then (taking the value maxima) FS_MIN_BLOCKS more
+    const int nblk = nrun * ts + (p.vm_far ? FS_MIN_BLOCKS : 0);
     const int w = xcd_work_item(blockIdx.x, nblk * p.G);
     const int bi = w % nblk, g = w / nblk;
     const int run = bi / ts, tp = bi % ts;
@@ -291,9 +291,17 @@ __global__ __launch_bounds__(fs_threads<D>()) void k_far_score(KParams p)
     };
 
     if (blockIdx.x == 0 && tid < 4 * p.G) p.meta_copy[tid] = p.meta[tid];
-    // without the value maxima the query halves' loads go out first, beside
-    // the keys' and values', and are split after them
-    const bool qpre = !p.vm_far && resident && wave < (t_hi - t_lo) * dup && bi < nrun * ts;   // (uniform)
+    if (bi >= nrun * ts) {
+        // a block for the value maxima only (uniform over the block): share
+        // bi - nrun * ts of FS_MIN_BLOCKS, so that the working blocks do not
+        // wait on those loads
+        __shared__ float vred[FS_THREADS / 64];
+        value_max_share<D, FS_THREADS>(p, c, g, bi - nrun * ts, FS_MIN_BLOCKS, vred);
+        return;
+    }
+    // the query halves' loads go out first, beside the keys' and values',
+    // and are split after them
+    const bool qpre = resident && wave < (t_hi - t_lo) * dup;   // (uniform)
     float4 qx[NS][2];
     if (qpre) fetch_q(t_lo + wave / dup, qx);
     v4 xk[PT];
@@ -301,13 +309,6 @@ __global__ __launch_bounds__(fs_threads<D>()) void k_far_score(KParams p)
     {
         load_keys(s_lo, xk);
         load_vals(s_lo, xv);
-        // the value maxima, where no far scan launch follows (its loads go
-        // out beside the first sub-chunk's keys and values)
-        if (p.vm_far) {
-            __shared__ float vred[FS_THREADS / 64];
-            value_max_share<D, FS_THREADS>(p, c, g, bi, nblk, vred);
-        }
-        if (bi >= nrun * ts) return;   // a block for the value maxima only (uniform over the block)
         const float mv = wmax(vals_max(s_lo, xv));
         if (lane == 0) vmw[wave] = mv;
     }
@@ -484,7 +485,7 @@ template <int D>
 static void launch_fs(const KParams& p, hipStream_t st)
 {
     const int hm = p.H * p.m;
-    const int nblk = p.vm_far ? fs_blocks_per_group(p.S, p.G, hm) : fs_runs(p.S, p.G) * fs_tsplit(p.S, p.G, hm);
+    const int nblk = fs_runs(p.S, p.G) * fs_tsplit(p.S, p.G, hm) + (p.vm_far ? FS_MIN_BLOCKS : 0);
     hipLaunchKernelGGL(k_far_score<D>, dim3(nblk * p.G), dim3(fs_threads<D>()), 0, st,
                        p);
 }

@@ -228,9 +228,9 @@ __host__ __device__ inline int fs_tsplit(int S, int G, int hm)
     while (2 * ts <= nht && n * ts < 128) ts *= 2;
     return ts;
 }
-// blocks per group of the launch: one per run and tile split, and at least
-// 32, so that the value maxima of a short call still spread over many
-// blocks (the blocks past the runs take only their share of the values)
+// value-maxima shares per group: one per far_score run and tile split, and
+// at least 32 (the far scan launch's maxima blocks; a call without that
+// launch gives far_score FS_MIN_BLOCKS maxima blocks per group of their own)
 constexpr int FS_MIN_BLOCKS = 32;
 __host__ __device__ inline int fs_blocks_per_group(int S, int G, int hm)
 {
