@@ -313,7 +313,6 @@ __global__ __launch_bounds__(fs_threads<D>()) void k_far_score(KParams p)
         if (lane == 0) vmw[wave] = mv;
     }
     if (qpre) split_q(qx);
-    else if (resident && wave < (t_hi - t_lo) * dup) load_q(t_lo + wave / dup);
 #pragma unroll 1
     for (int s = s_lo; s < s_hi; ++s) {
         __syncthreads();   // ek and vt are no longer read; vmw holds sub-chunk s's wave maxima
