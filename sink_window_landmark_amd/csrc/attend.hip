@@ -466,9 +466,10 @@ __global__ __launch_bounds__(256) void k_theta_kv(KParams p, int nmz, int nth)
 // The split serves launches with few blocks (a single sub-chunk, short
 // prompts), where one block per sub-chunk would leave most CUs idle.
 constexpr int AT_FULL = 0, AT_PART = 1, AT_MERGE = 2;
-// splits of one work item's key tiles at most (8: a merge of fewer records
-// pays for the longer splits, measured at a single max-window sub-chunk)
-constexpr int AT_MAX_SPLITS = 8;
+// splits of one work item's key tiles at most (12: at a single max-window
+// sub-chunk, more splits shorten the split blocks by more than the merge of
+// their records lengthens)
+constexpr int AT_MAX_SPLITS = 12;
 
 // Block shape per mode: a merge block has two waves, each on a SIMD of its own,
 // so that the few merge blocks of a small call spread their far readouts over

@@ -283,7 +283,7 @@ def test_split_window_calls():
     """Calls with few attention work items split the window over several
     blocks and merge their partial softmax states: prefills of 1500 and 700
     rows (2 and 5 splits; the far field starts at row 2048), then 64-, 37-
-    and 64-row attend_chunk + commit calls (8 splits; the far score's
+    and 64-row attend_chunk + commit calls (12 splits; the far score's
     landmark-row tiles over 8 blocks per group, four waves per tile), at the
     max-window geometry, every output against the oracle."""
     cfg = synth.CONFIGS["maxwin"]
